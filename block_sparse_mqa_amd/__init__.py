@@ -1,0 +1,239 @@
+"""Python binding of libhysparse.so, the HIP (gfx950) library of the HySparse
+MQA sparse-attention forward path.
+
+The entry points mirror the C ABI of ``include/hs.h`` one to one
+(``hs_block_score_fwd``, ``hs_topk_blocks``, ``hs_sparse_gather_fwd``,
+``hs_swa_fwd``, ``hs_num_blocks``, ``hs_workspace_size``). They only marshal
+arguments: tensors are device buffers owned by the caller (PyTorch provides
+memory and the current stream), and every step of the computation runs in the
+library's kernels. There is no fallback: if the library is missing, or an
+argument is rejected, the call raises.
+
+The convenience functions ``block_score``, ``topk_blocks``, ``sparse_gather``
+and ``swa`` allocate the outputs (and any workspace) with PyTorch and call the
+entry points above.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhysparse.so")
+
+HS_OK, HS_ERR_INVALID_ARG, HS_ERR_UNSUPPORTED, HS_ERR_HIP, HS_ERR_WORKSPACE = 0, -1, -2, -3, -4
+HS_BF16, HS_F32 = 0, 1
+HS_OP_BLOCK_SCORE, HS_OP_SPARSE_GATHER, HS_OP_SWA = 0, 1, 2
+
+EXPORTS = ("hs_num_blocks", "hs_workspace_size", "hs_block_score_fwd", "hs_topk_blocks",
+           "hs_sparse_gather_fwd", "hs_swa_fwd", "hs_status_string", "hs_last_error",
+           "hs_version")
+
+
+class HsProblem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("seqlen_q", ctypes.c_int32), ("seqlen_kv", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32), ("head_dim_qk", ctypes.c_int32),
+        ("head_dim_v", ctypes.c_int32), ("block_size", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+        ("kv_lens", ctypes.POINTER(ctypes.c_int32)), ("n_kv_lens", ctypes.c_int32),
+        ("doc_start", ctypes.POINTER(ctypes.c_int32)),
+        ("doc_end", ctypes.POINTER(ctypes.c_int32)), ("n_docs", ctypes.c_int32),
+    ]
+
+
+class HsError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libhysparse.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m block_sparse_mqa_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(HsProblem)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.hs_num_blocks.argtypes, lib.hs_num_blocks.restype = [P], i32
+    lib.hs_workspace_size.argtypes = [P, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.hs_workspace_size.restype = i32
+    lib.hs_block_score_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hs_block_score_fwd.restype = i32
+    lib.hs_topk_blocks.argtypes, lib.hs_topk_blocks.restype = [P, vp, i32, vp, vp], i32
+    lib.hs_sparse_gather_fwd.argtypes = [P, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+    lib.hs_sparse_gather_fwd.restype = i32
+    lib.hs_swa_fwd.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+    lib.hs_swa_fwd.restype = i32
+    lib.hs_status_string.argtypes, lib.hs_status_string.restype = [i32], ctypes.c_char_p
+    lib.hs_last_error.argtypes, lib.hs_last_error.restype = [], ctypes.c_char_p
+    lib.hs_version.argtypes, lib.hs_version.restype = [], i32
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status == HS_OK:
+        return
+    lib = load_library()
+    msg = f"{lib.hs_status_string(status).decode()}: {lib.hs_last_error().decode()}"
+    if status == HS_ERR_INVALID_ARG:
+        raise ValueError(msg)
+    if status == HS_ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise HsError(msg)
+
+
+class Problem:
+    """Owns an ``hs_problem`` and the host arrays it points to."""
+
+    def __init__(self, B: int, Sq: int, Skv: int, H: int, Dk: int, Dv: int, *,
+                 block_size: int = 64, scale: float = 0.0, dtype: str = "bf16",
+                 kv_lens: Optional[Sequence[int]] = None,
+                 doc_start: Optional[Sequence[int]] = None,
+                 doc_end: Optional[Sequence[int]] = None):
+        self.B, self.Sq, self.Skv, self.H, self.Dk, self.Dv = B, Sq, Skv, H, Dk, Dv
+        self.dtype = dtype
+        self._kv = (ctypes.c_int32 * len(kv_lens))(*kv_lens) if kv_lens is not None else None
+        self._ds = (ctypes.c_int32 * len(doc_start))(*doc_start) if doc_start is not None else None
+        self._de = (ctypes.c_int32 * len(doc_end))(*doc_end) if doc_end is not None else None
+        self.c = HsProblem(
+            batch=B, seqlen_q=Sq, seqlen_kv=Skv, num_heads=H, head_dim_qk=Dk, head_dim_v=Dv,
+            block_size=block_size, scale=float(scale),
+            dtype=HS_BF16 if dtype == "bf16" else HS_F32,
+            kv_lens=ctypes.cast(self._kv, ctypes.POINTER(ctypes.c_int32)) if self._kv else None,
+            n_kv_lens=len(kv_lens) if kv_lens is not None else 0,
+            doc_start=ctypes.cast(self._ds, ctypes.POINTER(ctypes.c_int32)) if self._ds else None,
+            doc_end=ctypes.cast(self._de, ctypes.POINTER(ctypes.c_int32)) if self._de else None,
+            n_docs=len(doc_start) if doc_start is not None else 0)
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+    import torch
+    return int(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(name, t, dtype=None, shape=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+# ---------------------------------------------------------------------------
+# Entry points (same names as the C ABI).
+# ---------------------------------------------------------------------------
+def hs_num_blocks(prob: Problem) -> int:
+    nb = load_library().hs_num_blocks(prob.ref)
+    if nb < 0:
+        _check(nb)
+    return nb
+
+
+def hs_workspace_size(prob: Problem, op: int, top_k: int = 0, window: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().hs_workspace_size(prob.ref, op, top_k, window, ctypes.byref(n)))
+    return n.value
+
+
+def hs_block_score_fwd(prob, q, kv, sink, out, lse, block_logit, ws=None, stream=None):
+    for n, t in (("q", q), ("kv", kv), ("sink", sink), ("out", out), ("lse", lse),
+                 ("block_logit", block_logit), ("ws", ws)):
+        _dev(n, t)
+    _check(load_library().hs_block_score_fwd(
+        prob.ref, _ptr(q), _ptr(kv), _ptr(sink), _ptr(out), _ptr(lse), _ptr(block_logit),
+        _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def hs_topk_blocks(prob, block_logit, top_k, block_idx, stream=None):
+    _dev("block_logit", block_logit)
+    _dev("block_idx", block_idx)
+    _check(load_library().hs_topk_blocks(prob.ref, _ptr(block_logit), int(top_k),
+                                         _ptr(block_idx), _stream(stream)))
+
+
+def hs_sparse_gather_fwd(prob, q, kv, sink, block_idx, top_k, out, lse, ws=None, stream=None):
+    for n, t in (("q", q), ("kv", kv), ("sink", sink), ("block_idx", block_idx), ("out", out),
+                 ("lse", lse), ("ws", ws)):
+        _dev(n, t)
+    _check(load_library().hs_sparse_gather_fwd(
+        prob.ref, _ptr(q), _ptr(kv), _ptr(sink), _ptr(block_idx), int(top_k), _ptr(out),
+        _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
+def hs_swa_fwd(prob, q, kv, sink, window, out, lse, ws=None, stream=None):
+    for n, t in (("q", q), ("kv", kv), ("sink", sink), ("out", out), ("lse", lse), ("ws", ws)):
+        _dev(n, t)
+    _check(load_library().hs_swa_fwd(
+        prob.ref, _ptr(q), _ptr(kv), _ptr(sink), int(window), _ptr(out), _ptr(lse), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Convenience wrappers: allocate outputs with PyTorch, then call the above.
+# ---------------------------------------------------------------------------
+def _torch_dtype(prob):
+    import torch
+    return torch.bfloat16 if prob.dtype == "bf16" else torch.float32
+
+
+def _workspace(prob, op, top_k=0, window=0):
+    import torch
+    n = hs_workspace_size(prob, op, top_k, window)
+    return torch.empty(max(1, (n + 3) // 4), dtype=torch.float32, device="cuda") if n else None
+
+
+def block_score(prob, q, kv, sink=None, stream=None):
+    import torch
+    out = torch.empty((prob.B, prob.Sq, prob.H, prob.Dv), dtype=_torch_dtype(prob), device=q.device)
+    lse = torch.empty((prob.B, prob.Sq, prob.H), dtype=torch.float32, device=q.device)
+    bl = torch.empty((prob.B, prob.Sq, hs_num_blocks(prob)), dtype=torch.float32, device=q.device)
+    hs_block_score_fwd(prob, q, kv, sink, out, lse, bl, _workspace(prob, HS_OP_BLOCK_SCORE), stream)
+    return out, lse, bl
+
+
+def topk_blocks(prob, block_logit, top_k, stream=None):
+    import torch
+    idx = torch.empty((prob.B, prob.Sq, top_k), dtype=torch.int32, device=block_logit.device)
+    hs_topk_blocks(prob, block_logit, top_k, idx, stream)
+    return idx
+
+
+def sparse_gather(prob, q, kv, sink, block_idx, top_k, stream=None):
+    import torch
+    out = torch.empty((prob.B, prob.Sq, prob.H, prob.Dv), dtype=_torch_dtype(prob), device=q.device)
+    lse = torch.empty((prob.B, prob.Sq, prob.H), dtype=torch.float32, device=q.device)
+    hs_sparse_gather_fwd(prob, q, kv, sink, block_idx, top_k, out, lse,
+                         _workspace(prob, HS_OP_SPARSE_GATHER, top_k=top_k), stream)
+    return out, lse
+
+
+def swa(prob, q, kv, sink, window, stream=None):
+    import torch
+    out = torch.empty((prob.B, prob.Sq, prob.H, prob.Dv), dtype=_torch_dtype(prob), device=q.device)
+    lse = torch.empty((prob.B, prob.Sq, prob.H), dtype=torch.float32, device=q.device)
+    hs_swa_fwd(prob, q, kv, sink, window, out, lse, _workspace(prob, HS_OP_SWA, window=window),
+               stream)
+    return out, lse

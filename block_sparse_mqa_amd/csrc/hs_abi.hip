@@ -1,0 +1,307 @@
+// Host side of the C ABI declared in include/hs.h: argument validation, the
+// block table of packed documents, workspace sizing and kernel launches.
+//
+// Validation follows the error conventions of the pages: every check runs on
+// the host before anything is launched and failures are reported, not
+// asserted (review of PaddleFleet PR 1453, the request to replace assert
+// checks with ValueError); an input the path cannot honour is rejected rather
+// than dropped (page "Support attn sink in fa3", the sink discussion; page
+// "TileLang CSA compressed indexer for DSv4", the request to raise instead of
+// silently ignoring a document mask).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/hs.h"
+#include "hs_common.h"
+#include "hs_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hs_status fail(hs_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+// Validates the problem and fills the kernel geometry.
+hs_status prepare(const hs_problem* p, hs::Geom& g) {
+  g_last_error.clear();
+  if (!p) return fail(HS_ERR_INVALID_ARG, "problem is NULL");
+  if (p->batch < 1 || p->seqlen_q < 1 || p->seqlen_kv < 1)
+    return fail(HS_ERR_INVALID_ARG, "batch, seqlen_q and seqlen_kv must be >= 1 (got %d, %d, %d)",
+                p->batch, p->seqlen_q, p->seqlen_kv);
+  if (p->num_heads < 1 || p->head_dim_qk < 1 || p->head_dim_v < 1)
+    return fail(HS_ERR_INVALID_ARG, "num_heads, head_dim_qk and head_dim_v must be >= 1");
+  if (p->head_dim_v > p->head_dim_qk)
+    return fail(HS_ERR_INVALID_ARG,
+                "head_dim_v (%d) > head_dim_qk (%d): the value is the leading region of the key",
+                p->head_dim_v, p->head_dim_qk);
+  if (p->dtype != HS_BF16 && p->dtype != HS_F32)
+    return fail(HS_ERR_INVALID_ARG, "dtype %d is not an hs_dtype", p->dtype);
+  if (p->block_size != 64)
+    return fail(HS_ERR_UNSUPPORTED, "block_size %d: only 64 is built", p->block_size);
+  if (!std::isfinite(p->scale))
+    return fail(HS_ERR_INVALID_ARG, "scale must be finite");
+  if (p->dtype == HS_BF16) {
+    if (p->num_heads != 64 || p->head_dim_qk != 576 || p->head_dim_v != 512)
+      return fail(HS_ERR_UNSUPPORTED,
+                  "bf16 is built for H=64, Dk=576, Dv=512 only (got H=%d, Dk=%d, Dv=%d)",
+                  p->num_heads, p->head_dim_qk, p->head_dim_v);
+  } else {
+    if (p->num_heads > 16 || p->head_dim_qk > 128)
+      return fail(HS_ERR_UNSUPPORTED, "f32 is built for H <= 16 and Dk <= 128 (got H=%d, Dk=%d)",
+                  p->num_heads, p->head_dim_qk);
+  }
+  if (p->batch > hs::kMaxBatch)
+    return fail(HS_ERR_UNSUPPORTED, "batch %d exceeds %d", p->batch, hs::kMaxBatch);
+
+  std::memset(&g, 0, sizeof(g));
+  g.B = p->batch;
+  g.Sq = p->seqlen_q;
+  g.Skv = p->seqlen_kv;
+  g.H = p->num_heads;
+  g.Dk = p->head_dim_qk;
+  g.Dv = p->head_dim_v;
+  g.BS = p->block_size;
+  const double scale = p->scale > 0.f ? (double)p->scale : 1.0 / std::sqrt((double)p->head_dim_qk);
+  g.scale_log2 = (float)(scale * 1.4426950408889634);
+
+  if (p->kv_lens) {
+    if (p->n_kv_lens != p->batch)
+      return fail(HS_ERR_INVALID_ARG, "n_kv_lens (%d) != batch (%d)", p->n_kv_lens, p->batch);
+    for (int b = 0; b < p->batch; ++b) {
+      const int L = p->kv_lens[b];
+      if (L < p->seqlen_q || L > p->seqlen_kv)
+        return fail(HS_ERR_INVALID_ARG, "kv_lens[%d] = %d outside [seqlen_q=%d, seqlen_kv=%d]", b, L,
+                    p->seqlen_q, p->seqlen_kv);
+      g.kv_len[b] = L;
+    }
+  } else {
+    if (p->n_kv_lens != 0) return fail(HS_ERR_INVALID_ARG, "n_kv_lens set without kv_lens");
+    if (p->seqlen_q > p->seqlen_kv)
+      return fail(HS_ERR_INVALID_ARG, "seqlen_q (%d) > seqlen_kv (%d)", p->seqlen_q, p->seqlen_kv);
+    for (int b = 0; b < p->batch; ++b) g.kv_len[b] = p->seqlen_kv;
+  }
+
+  if (p->n_docs != 0 || p->doc_start || p->doc_end) {
+    if (p->n_docs < 1 || !p->doc_start || !p->doc_end)
+      return fail(HS_ERR_INVALID_ARG, "documents need doc_start, doc_end and n_docs >= 1");
+    if (p->n_docs > hs::kMaxDocs)
+      return fail(HS_ERR_UNSUPPORTED, "n_docs %d exceeds %d", p->n_docs, hs::kMaxDocs);
+    if (p->batch != 1 || p->kv_lens)
+      return fail(HS_ERR_INVALID_ARG, "documents require batch == 1 and no kv_lens");
+    if (p->seqlen_q != p->seqlen_kv)
+      return fail(HS_ERR_INVALID_ARG, "documents require seqlen_q == seqlen_kv");
+    int expect = 0, blk = 0;
+    for (int d = 0; d < p->n_docs; ++d) {
+      const int s = p->doc_start[d], e = p->doc_end[d];
+      if (s != expect || e <= s)
+        return fail(HS_ERR_INVALID_ARG,
+                    "documents must tile [0, seqlen) in order: doc %d is [%d, %d), expected start %d",
+                    d, s, e, expect);
+      g.doc_start[d] = s;
+      g.doc_end[d] = e;
+      g.doc_blk0[d] = blk;
+      blk += (e - s + g.BS - 1) / g.BS;
+      expect = e;
+    }
+    if (expect != p->seqlen_q)
+      return fail(HS_ERR_INVALID_ARG, "documents end at %d, seqlen is %d", expect, p->seqlen_q);
+    g.doc_blk0[p->n_docs] = blk;
+    g.n_docs = p->n_docs;
+    g.NB = blk;
+  } else {
+    int nb = 0;
+    for (int b = 0; b < p->batch; ++b) nb = std::max(nb, (g.kv_len[b] + g.BS - 1) / g.BS);
+    g.NB = nb;
+  }
+  return HS_OK;
+}
+
+// Number of key-range splits for single-token rows (decode): enough
+// workgroups to fill the chip, each split owning at least 4 tiles.
+int choose_nsplit(const hs::Geom& g, int op, int top_k, int window) {
+  if (g.Dk != 576) return 1;
+  const int items = g.B * g.Sq;
+  if (items >= 512) return 1;
+  int max_tiles;
+  if (op == HS_OP_SPARSE_GATHER) max_tiles = top_k;
+  else if (op == HS_OP_SWA) max_tiles = std::min(g.NB, (window + g.BS - 1) / g.BS + 1);
+  else max_tiles = g.NB;
+  int ns = (1024 + items - 1) / items;
+  ns = std::min(ns, std::max(1, max_tiles / 4));
+  return std::max(1, std::min(ns, 64));
+}
+
+size_t split_ws_bytes(const hs::Geom& g, int nsplit) {
+  if (nsplit <= 1) return 0;
+  const size_t slots = (size_t)g.B * g.Sq * nsplit * g.H;
+  return slots * (size_t)g.Dv * sizeof(float) + slots * 2 * sizeof(float);
+}
+
+hs_status check_ptr(const void* ptr, const char* name, unsigned align = 16) {
+  if (!ptr) return fail(HS_ERR_INVALID_ARG, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(ptr) % align != 0)
+    return fail(HS_ERR_INVALID_ARG, "%s is not %u-byte aligned", name, align);
+  return HS_OK;
+}
+
+hs_status hip_status(int err, const char* what) {
+  if (err != 0)
+    return fail(HS_ERR_HIP, "%s: %s", what, hipGetErrorString(static_cast<hipError_t>(err)));
+  return HS_OK;
+}
+
+hs_status launch_attn(int op, const hs_problem* p, const void* q, const void* kv, const float* sink,
+                      const int32_t* block_idx, int32_t top_k, int32_t window, void* out,
+                      float* lse, float* block_logit, void* ws, size_t ws_bytes, void* stream) {
+  hs::Geom g;
+  hs_status st = prepare(p, g);
+  if (st != HS_OK) return st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(kv, "kv")) || (st = check_ptr(out, "out")) ||
+      (st = check_ptr(lse, "lse", 4)))
+    return st;
+  if (op == HS_OP_BLOCK_SCORE && (st = check_ptr(block_logit, "block_logit", 4))) return st;
+  if (op == HS_OP_SPARSE_GATHER) {
+    if ((st = check_ptr(block_idx, "block_idx", 4))) return st;
+    if (top_k < 1) return fail(HS_ERR_INVALID_ARG, "top_k must be >= 1 (got %d)", top_k);
+    if (top_k > 64) return fail(HS_ERR_UNSUPPORTED, "top_k %d exceeds 64", top_k);
+  }
+  if (op == HS_OP_SWA && window < 1)
+    return fail(HS_ERR_INVALID_ARG, "window must be >= 1 (got %d)", window);
+  if (sink && reinterpret_cast<uintptr_t>(sink) % 4 != 0)
+    return fail(HS_ERR_INVALID_ARG, "sink is not 4-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (g.Sq * g.B == 0) return HS_OK;
+
+  if (p->dtype == HS_BF16) {
+    const int nsplit = choose_nsplit(g, op, top_k, window);
+    const size_t need = split_ws_bytes(g, nsplit);
+    if (need > 0 && (!ws || ws_bytes < need))
+      return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                  ws ? ws_bytes : (size_t)0);
+    if (need > 0 && reinterpret_cast<uintptr_t>(ws) % 16 != 0)
+      return fail(HS_ERR_WORKSPACE, "workspace is not 16-byte aligned");
+    hs::AttnArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = static_cast<const __bf16*>(q);
+    a.kv = static_cast<const __bf16*>(kv);
+    a.sink = sink;
+    a.out = static_cast<__bf16*>(out);
+    a.lse = lse;
+    a.block_logit = block_logit;
+    a.block_idx = block_idx;
+    a.top_k = top_k;
+    a.window = window;
+    a.nsplit = nsplit;
+    if (nsplit > 1) {
+      const size_t slots = (size_t)g.B * g.Sq * nsplit * g.H;
+      a.ws_o = static_cast<float*>(ws);
+      a.ws_ml = static_cast<float*>(ws) + slots * g.Dv;
+    }
+    a.g = g;
+    return hip_status(hs::attn_bf16_launch(op, a, s), "attention launch");
+  }
+  hs::AttnF32Args a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = static_cast<const float*>(q);
+  a.kv = static_cast<const float*>(kv);
+  a.sink = sink;
+  a.out = static_cast<float*>(out);
+  a.lse = lse;
+  a.block_logit = block_logit;
+  a.block_idx = block_idx;
+  a.top_k = top_k;
+  a.window = window;
+  a.g = g;
+  return hip_status(hs::attn_f32_launch(op, a, s), "attention launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t hs_version(void) { return 100; }
+
+const char* hs_status_string(int32_t status) {
+  switch (status) {
+    case HS_OK: return "HS_OK";
+    case HS_ERR_INVALID_ARG: return "HS_ERR_INVALID_ARG";
+    case HS_ERR_UNSUPPORTED: return "HS_ERR_UNSUPPORTED";
+    case HS_ERR_HIP: return "HS_ERR_HIP";
+    case HS_ERR_WORKSPACE: return "HS_ERR_WORKSPACE";
+    default: return "HS_UNKNOWN_STATUS";
+  }
+}
+
+const char* hs_last_error(void) { return g_last_error.c_str(); }
+
+int32_t hs_num_blocks(const hs_problem* p) {
+  hs::Geom g;
+  const hs_status st = prepare(p, g);
+  return st == HS_OK ? g.NB : (int32_t)st;
+}
+
+hs_status hs_workspace_size(const hs_problem* p, int32_t op, int32_t top_k, int32_t window,
+                            size_t* bytes) {
+  hs::Geom g;
+  hs_status st = prepare(p, g);
+  if (st != HS_OK) return st;
+  if (!bytes) return fail(HS_ERR_INVALID_ARG, "bytes is NULL");
+  if (op < HS_OP_BLOCK_SCORE || op > HS_OP_SWA) return fail(HS_ERR_INVALID_ARG, "unknown op %d", op);
+  *bytes = p->dtype == HS_BF16 ? split_ws_bytes(g, choose_nsplit(g, op, top_k, window)) : 0;
+  return HS_OK;
+}
+
+hs_status hs_block_score_fwd(const hs_problem* p, const void* q, const void* kv, const float* sink,
+                             void* out, float* lse, float* block_logit, void* ws, size_t ws_bytes,
+                             void* stream) {
+  return launch_attn(HS_OP_BLOCK_SCORE, p, q, kv, sink, nullptr, 0, 0, out, lse, block_logit, ws,
+                     ws_bytes, stream);
+}
+
+hs_status hs_sparse_gather_fwd(const hs_problem* p, const void* q, const void* kv,
+                               const float* sink, const int32_t* block_idx, int32_t top_k,
+                               void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return launch_attn(HS_OP_SPARSE_GATHER, p, q, kv, sink, block_idx, top_k, 0, out, lse, nullptr,
+                     ws, ws_bytes, stream);
+}
+
+hs_status hs_swa_fwd(const hs_problem* p, const void* q, const void* kv, const float* sink,
+                     int32_t window, void* out, float* lse, void* ws, size_t ws_bytes,
+                     void* stream) {
+  return launch_attn(HS_OP_SWA, p, q, kv, sink, nullptr, 0, window, out, lse, nullptr, ws, ws_bytes,
+                     stream);
+}
+
+hs_status hs_topk_blocks(const hs_problem* p, const float* block_logit, int32_t top_k,
+                         int32_t* block_idx, void* stream) {
+  hs::Geom g;
+  hs_status st = prepare(p, g);
+  if (st != HS_OK) return st;
+  if ((st = check_ptr(block_logit, "block_logit", 4)) || (st = check_ptr(block_idx, "block_idx", 4)))
+    return st;
+  if (top_k < 1) return fail(HS_ERR_INVALID_ARG, "top_k must be >= 1 (got %d)", top_k);
+  if (top_k > 64) return fail(HS_ERR_UNSUPPORTED, "top_k %d exceeds 64", top_k);
+  if (g.NB > 4096) return fail(HS_ERR_UNSUPPORTED, "%d blocks exceed 4096", g.NB);
+  hs::TopkArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.block_logit = block_logit;
+  a.block_idx = block_idx;
+  a.top_k = top_k;
+  a.g = g;
+  return hip_status(hs::topk_launch(a, static_cast<hipStream_t>(stream)), "top-k launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,399 @@
+// bf16 MFMA attention engine for the HySparse MQA forward path on gfx950.
+//
+// One kernel template serves the three attention operations of the method
+// (page "HySparse MQA sparse attention (FA4 block scoring + SWA MQA +
+// block-sparse DSA gather)", section "Core"): causal attention fused with
+// per-block scores, block-sparse gather attention, and sliding-window
+// attention, all with the optional learnable per-head sink. The shapes are the
+// absorbed-MLA MQA layout of the same page, section "FlashMLA sparse kernel
+// constraints": 64 query heads share one latent KV head with Dk = 576 columns,
+// and the value is its leading Dv = 512 columns.
+//
+// Work decomposition
+//   A workgroup owns one query token: its 64 heads are 64 rows. It walks a
+//   sequence of 64-key tiles; every tile is exactly one key block, so a row's
+//   reduction over a tile is that block's log-sum-exp. Four waves split the
+//   heads (wave w owns heads 16w .. 16w+15) and share each KV tile, which is
+//   staged once in LDS (the one KV head serves every query head). One
+//   workgroup per CU, one wave per SIMD: Q stays in 72 VGPRs, the O
+//   accumulator takes 128, the scores 16. Tiles are double-buffered so the
+//   copy of tile t+1 overlaps the MFMAs of tile t.
+//
+// Contractions (v_mfma_f32_16x16x32_bf16)
+//   S^T[key, row] = K_tile[key, :] . Q[row, :]     A = K (LDS), B = Q (VGPRs)
+//   Lane l then holds 16 scores of ONE row (head l%16): the softmax row
+//   statistics are in-register reductions plus two exchanges across the four
+//   16-lane groups.
+//   O^T[dim, row] += V^T[dim, key] . P^T[key, row]
+//   A = V^T comes from the LDS transpose read ds_read_b64_tr_b16; B = P^T is
+//   taken straight from the S^T registers: inside each 32-key k-step the key
+//   order is permuted the same way on both operands, so P never moves.
+//
+// LDS tile layout: 72 column chunks of 8 bf16 (16 B); chunk c holds the 16 B
+//   of every key of the tile at [c * 1088 + key * 16]. The 64 B pad per chunk
+//   keeps the two chunks touched by one transpose-read lane group on
+//   different banks. Tiles are filled with global_load_lds_dwordx4 (lane l of
+//   a wave instruction writes 16 B at base + 16 l): one wave instruction per
+//   chunk, no VGPR staging.
+//
+// Softmax: scores live in the log2 domain (scale * log2 e folded in). Per
+//   tile, p = exp2(x - m_tile): the tile max is the stabiliser of the block
+//   log-sum-exp, so a block far below the running max cannot underflow to
+//   -inf. The running reference max is raised only when a tile max exceeds it
+//   by more than 8 (factor 256), so O is rescaled rarely; the result is the
+//   same up to rounding. The sink enters as the initial reference max
+//   sigma * log2 e with weight 1, counted once per row.
+#include <hip/hip_runtime.h>
+
+#include "hs_common.h"
+#include "hs_kernels.h"
+
+namespace hs {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define HS_LDS __attribute__((address_space(3)))
+#define HS_GLB __attribute__((address_space(1)))
+
+namespace mla {
+constexpr int H = 64, DK = 576, DV = 512, BS = 64;
+constexpr int NW = 4;                        // waves per workgroup
+constexpr int RW = 16;                       // rows (heads) per wave
+constexpr int NTHREADS = 64 * NW;
+constexpr int NCH = DK / 8;                  // 72 chunks of 8 columns
+constexpr int CH_STRIDE = BS * 16 + 64;      // bytes per chunk region
+constexpr int TILE_BYTES = NCH * CH_STRIDE;  // 78336
+constexpr int KSTEPS = DK / 32;              // 18 k-steps of the score MFMA
+constexpr int DBLK = DV / 16;                // 32 column blocks of O
+constexpr float TAU = 8.0f;                  // lazy-rescale threshold (log2 units)
+}  // namespace mla
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Copy one 64-key tile (rows [start, start+len), clamped) into an LDS buffer.
+__device__ __forceinline__ void stage_tile(char* buf, const bf16* kv_entry, const Blk& blk,
+                                           int wave, int lane) {
+  using namespace mla;
+  const int key = blk.start + min(lane, blk.len - 1);
+  const bf16* src = kv_entry + (size_t)key * DK;
+#pragma unroll
+  for (int i = 0; i < NCH / NW; ++i) {
+    const int c = wave + NW * i;
+    __builtin_amdgcn_global_load_lds((const HS_GLB void*)(src + 8 * c),
+                                     (HS_LDS void*)(buf + c * CH_STRIDE), 16, 0, 0);
+  }
+}
+
+template <int OP, bool SPLIT>
+__global__ __launch_bounds__(mla::NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_bf16_kernel(AttnArgs a) {
+  using namespace mla;
+  __shared__ __attribute__((aligned(16))) char lds[2 * TILE_BYTES];
+  __shared__ float bl_slot[2][NW];
+  __shared__ int tile_list[64];
+  __shared__ int tile_count;
+
+  const Geom& g = a.g;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int grp = lane >> 4;     // 16-lane group: k-offset 8*grp inside a k-step
+  const int l16 = lane & 15;
+  const int head = wave * RW + l16;
+
+  // Work item: heaviest query rows first (causal cost grows with position).
+  int w = blockIdx.x;
+  const int split = SPLIT ? (w % a.nsplit) : 0;
+  if (SPLIT) w /= a.nsplit;
+  const int b = w / g.Sq;
+  const int r = g.Sq - 1 - (w % g.Sq);
+  const size_t row = (size_t)b * g.Sq + r;
+
+  const RowRange rr = row_range(g, OP, b, r, a.window);
+  const int nb_b = nb_of_entry(g, b);
+
+  // Tile sequence: a block range, or the listed blocks that intersect the
+  // allowed key range (compacted in order of the list).
+  int ntiles;
+  if (OP == kGather) {
+    if (wave == 0) {
+      int j = -1;
+      bool ok = false;
+      if (lane < a.top_k) {
+        j = a.block_idx[row * a.top_k + lane];
+        if (j >= 0 && j < nb_b) {
+          const Blk bk = block_rows(g, b, j);
+          ok = !(bk.start > rr.hi || bk.start + bk.len - 1 < rr.lo);
+        }
+      }
+      const unsigned long long m = __ballot(ok);
+      const int pos = __popcll(m & ((1ull << lane) - 1ull));
+      if (ok) tile_list[pos] = j;
+      if (lane == 0) tile_count = __popcll(m);
+    }
+    __syncthreads();
+    ntiles = tile_count;
+  } else {
+    ntiles = rr.j_last - rr.j_first + 1;
+  }
+  int t_begin = 0, t_end = ntiles;
+  if (SPLIT) {
+    const int per = (ntiles + a.nsplit - 1) / a.nsplit;
+    t_begin = min(ntiles, split * per);
+    t_end = min(ntiles, t_begin + per);
+  }
+  auto tile_block = [&](int t) -> int { return OP == kGather ? tile_list[t] : rr.j_first + t; };
+
+  // Block-score columns this row never visits are -inf.
+  if (OP == kScore && split == 0) {
+    float* blr = a.block_logit + row * g.NB;
+    for (int j = threadIdx.x; j < g.NB; j += NTHREADS)
+      if (j < rr.j_first || j > rr.j_last) blr[j] = -INFINITY;
+  }
+
+  const bf16* kv_entry = a.kv + (size_t)b * g.Skv * DK;
+  if (t_begin < t_end)
+    stage_tile(lds + (t_begin & 1) * TILE_BYTES, kv_entry, block_rows(g, b, tile_block(t_begin)),
+               wave, lane);
+
+  // Q rows of this wave as MFMA B operands: lane holds q[row, head, 32ks + 8grp .. +8].
+  bf16x8 qreg[KSTEPS];
+  {
+    const bf16* qp = a.q + (row * H + head) * DK + 8 * grp;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) qreg[ks] = *(const bf16x8*)(qp + 32 * ks);
+  }
+
+  const float sk = (a.sink != nullptr && split == 0) ? a.sink[head] * kLog2e : -INFINITY;
+  float m_run = sk;
+  float l_run = (sk > -INFINITY && grp == 0) ? 1.0f : 0.0f;  // lane-partial denominator
+  f32x4 oacc[DBLK];
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const float sl2 = g.scale_log2;
+  int j_prev = -1;  // block whose score partials wait in bl_slot
+  int par = 0;
+
+  for (int t = t_begin; t < t_end; ++t) {
+    const int j = tile_block(t);
+    const Blk blk = block_rows(g, b, j);
+    char* buf = lds + (t & 1) * TILE_BYTES;
+
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // tile t resident; tile t-1 fully consumed; partials visible
+    if (OP == kScore && j_prev >= 0 && threadIdx.x == 0) {
+      float v = bl_slot[par ^ 1][0];
+#pragma unroll
+      for (int k = 1; k < NW; ++k) v = fmaxf(v, bl_slot[par ^ 1][k]);
+      a.block_logit[row * g.NB + j_prev] = v * kLn2;
+    }
+    if (t + 1 < t_end)
+      stage_tile(lds + ((t + 1) & 1) * TILE_BYTES, kv_entry, block_rows(g, b, tile_block(t + 1)),
+                 wave, lane);
+
+    // S^T = K . Q^T over four 16-key blocks.
+    f32x4 s[4] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f},
+                  f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const HS_LDS char* base = (const HS_LDS char*)(buf + (4 * ks + grp) * CH_STRIDE + l16 * 16);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8 kf = *(const HS_LDS bf16x8*)(base + kb * 256);
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qreg[ks], s[kb], 0, 0, 0);
+      }
+    }
+
+    // Mask, log2 domain. s[kb][i] is key 16kb + 4grp + i of row l16.
+    float x[16];
+    {
+      const int klo = rr.lo - blk.start, khi = min(rr.hi - blk.start, blk.len - 1);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = 16 * kb + 4 * grp + i;
+          x[4 * kb + i] = (m >= klo && m <= khi) ? s[kb][i] * sl2 : -INFINITY;
+        }
+    }
+    float mx = x[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+
+    float p[16];
+    float psum = 0.f;
+    if (mx == -INFINITY) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) p[i] = 0.f;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        p[i] = fast_exp2(x[i] - mx);
+        psum += p[i];
+      }
+    }
+
+    if (OP == kScore) {
+      float tot = psum + __shfl_xor(psum, 16);
+      tot += __shfl_xor(tot, 32);
+      float bl = (mx == -INFINITY) ? -INFINITY : mx + fast_log2(tot);
+      // max over the 16 heads of this wave (lanes differing in bits 0..3)
+      bl = fmaxf(bl, __shfl_xor(bl, 1));
+      bl = fmaxf(bl, __shfl_xor(bl, 2));
+      bl = fmaxf(bl, __shfl_xor(bl, 4));
+      bl = fmaxf(bl, __shfl_xor(bl, 8));
+      if (lane == 0) bl_slot[par][wave] = bl;
+      j_prev = j;
+      par ^= 1;
+    }
+
+    // Online softmax with a lazily raised reference max.
+    if (mx > m_run + TAU) {
+      const float alpha = fast_exp2(m_run - mx);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) oacc[db] *= alpha;
+      m_run = mx;
+    }
+    const float f = (mx == -INFINITY) ? 0.f : fast_exp2(mx - m_run);
+    l_run += psum * f;
+
+    // P^T B operands for the two 32-key k-steps: k-step kk takes key blocks
+    // 2kk (registers e=0..3) and 2kk+1 (e=4..7).
+    bf16x8 pb[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[kk][e] = (bf16)(p[8 * kk + e] * f);
+
+    // O^T += V^T . P^T. The transpose read of lane group grp covers dims
+    // 16db + 0..15; lane i of the group addresses key kbase + i/4, dims
+    // 16db + 4(i%4) .. +3, and receives dim 16db + l16 for keys kbase .. +3.
+    const int dsub = 4 * (l16 & 3);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int k0 = 32 * kk + 4 * grp + (l16 >> 2);
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        const int d0 = 16 * db + dsub;
+        const HS_LDS char* vb = (const HS_LDS char*)(buf + (d0 >> 3) * CH_STRIDE + (d0 & 7) * 2);
+        const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((HS_LDS bf16x4*)(vb + k0 * 16));
+        const bf16x4 hi4 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((HS_LDS bf16x4*)(vb + (k0 + 16) * 16));
+        bf16x8 va;
+        va[0] = lo4[0]; va[1] = lo4[1]; va[2] = lo4[2]; va[3] = lo4[3];
+        va[4] = hi4[0]; va[5] = hi4[1]; va[6] = hi4[2]; va[7] = hi4[3];
+        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[kk], oacc[db], 0, 0, 0);
+      }
+    }
+  }
+
+  if (OP == kScore) {
+    __syncthreads();
+    if (j_prev >= 0 && threadIdx.x == 0) {
+      float v = bl_slot[par ^ 1][0];
+#pragma unroll
+      for (int k = 1; k < NW; ++k) v = fmaxf(v, bl_slot[par ^ 1][k]);
+      a.block_logit[row * g.NB + j_prev] = v * kLn2;
+    }
+  }
+
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  // oacc[db][i] is O[row l16][dim 16db + 4grp + i].
+  if (!SPLIT) {
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    bf16* op = a.out + (row * H + head) * DV + 4 * grp;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+      bf16x4 v;
+      v[0] = (bf16)(oacc[db][0] * inv);
+      v[1] = (bf16)(oacc[db][1] * inv);
+      v[2] = (bf16)(oacc[db][2] * inv);
+      v[3] = (bf16)(oacc[db][3] * inv);
+      *(bf16x4*)(op + 16 * db) = v;
+    }
+    if (grp == 0)
+      a.lse[row * H + head] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
+  } else {
+    // Unnormalised partial: O (fp32), reference max (log2) and denominator.
+    const size_t slot = (size_t)w * a.nsplit + split;
+    float* op = a.ws_o + (slot * H + head) * DV + 4 * grp;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) *(f32x4*)(op + 16 * db) = oacc[db];
+    if (grp == 0) {
+      a.ws_ml[(slot * H + head) * 2 + 0] = m_run;
+      a.ws_ml[(slot * H + head) * 2 + 1] = l_tot;
+    }
+  }
+}
+
+// Merge split partials: one wave per (item, head); lane owns 8 columns.
+__global__ __launch_bounds__(64) void merge_bf16_kernel(AttnArgs a) {
+  using namespace mla;
+  const int item = blockIdx.x / H;
+  const int head = blockIdx.x % H;
+  const int lane = threadIdx.x;
+  float M = -INFINITY;
+  for (int s = 0; s < a.nsplit; ++s) {
+    const size_t slot = (size_t)item * a.nsplit + s;
+    const float m = a.ws_ml[(slot * H + head) * 2 + 0];
+    const float l = a.ws_ml[(slot * H + head) * 2 + 1];
+    if (l > 0.f) M = fmaxf(M, m);
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+  if (M > -INFINITY) {
+    for (int s = 0; s < a.nsplit; ++s) {
+      const size_t slot = (size_t)item * a.nsplit + s;
+      const float m = a.ws_ml[(slot * H + head) * 2 + 0];
+      const float l = a.ws_ml[(slot * H + head) * 2 + 1];
+      if (!(l > 0.f)) continue;
+      const float wgt = fast_exp2(m - M);
+      L += l * wgt;
+      const float* op = a.ws_o + (slot * H + head) * DV + 8 * lane;
+      const f32x4 v0 = *(const f32x4*)op;
+      const f32x4 v1 = *(const f32x4*)(op + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] += v0[e] * wgt;
+        acc[4 + e] += v1[e] * wgt;
+      }
+    }
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  bf16x8 o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = (bf16)(acc[e] * inv);
+  // Items follow the launch order of the attention kernel: item = b*Sq + (Sq-1-r).
+  const int b = item / a.g.Sq;
+  const int r = a.g.Sq - 1 - (item % a.g.Sq);
+  const size_t row = (size_t)b * a.g.Sq + r;
+  *(bf16x8*)(a.out + (row * H + head) * DV + 8 * lane) = o;
+  if (lane == 0) a.lse[row * H + head] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
+}
+
+int attn_bf16_launch(int op, const AttnArgs& a, hipStream_t stream) {
+  const int items = a.g.B * a.g.Sq;
+  const dim3 block(mla::NTHREADS);
+  const dim3 grid((unsigned)(items * a.nsplit));
+  if (a.nsplit == 1) {
+    if (op == kScore) hipLaunchKernelGGL((attn_bf16_kernel<kScore, false>), grid, block, 0, stream, a);
+    else if (op == kGather) hipLaunchKernelGGL((attn_bf16_kernel<kGather, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<kSwa, false>), grid, block, 0, stream, a);
+  } else {
+    if (op == kScore) hipLaunchKernelGGL((attn_bf16_kernel<kScore, true>), grid, block, 0, stream, a);
+    else if (op == kGather) hipLaunchKernelGGL((attn_bf16_kernel<kGather, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<kSwa, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL(merge_bf16_kernel, dim3((unsigned)(items * mla::H)), dim3(64), 0, stream, a);
+  }
+  return (int)hipGetLastError();
+}
+
+}  // namespace hs

@@ -1,0 +1,98 @@
+// Device-side problem geometry shared by the HIP kernels of the HySparse MQA
+// forward path: positions, packed documents and key blocks.
+//
+// Blocks restart at each document's first row and never cross a document
+// (review of PaddleFleet PR 1453, block-score PyLayer comments: the per-block
+// start row block_bos). Block ids are global, numbered in document order.
+// A query row r of batch entry b sits at position L_b - Sq + r (blog page on
+// the unified sparse-attention dispatcher, decode paragraph: a decode token's
+// key length is the cache plus the current token).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hs {
+
+constexpr int kMaxBatch = 256;
+constexpr int kMaxDocs = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Copied by value into kernel arguments.
+struct Geom {
+  int B, Sq, Skv, H, Dk, Dv, BS, NB;
+  int n_docs;
+  float scale_log2;              // softmax scale * log2(e)
+  int kv_len[kMaxBatch];         // valid KV rows per entry (Skv when not given)
+  int doc_start[kMaxDocs];
+  int doc_end[kMaxDocs];
+  int doc_blk0[kMaxDocs + 1];    // first global block id of each document
+};
+
+struct Doc {
+  int start, end, blk0;
+};
+
+struct Blk {
+  int start, len;
+};
+
+// Document holding position p of entry b.
+__device__ __forceinline__ Doc doc_of_pos(const Geom& g, int b, int p) {
+  if (g.n_docs == 0) return Doc{0, g.kv_len[b], 0};
+  int lo = 0, hi = g.n_docs - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (g.doc_start[mid] <= p) lo = mid; else hi = mid - 1;
+  }
+  return Doc{g.doc_start[lo], g.doc_end[lo], g.doc_blk0[lo]};
+}
+
+// Number of key blocks of entry b.
+__device__ __forceinline__ int nb_of_entry(const Geom& g, int b) {
+  if (g.n_docs == 0) return (g.kv_len[b] + g.BS - 1) / g.BS;
+  return g.doc_blk0[g.n_docs];
+}
+
+// Rows [start, start + len) of block j of entry b (j must be valid).
+__device__ __forceinline__ Blk block_rows(const Geom& g, int b, int j) {
+  if (g.n_docs == 0) {
+    int s = j * g.BS;
+    return Blk{s, min(g.BS, g.kv_len[b] - s)};
+  }
+  int lo = 0, hi = g.n_docs - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (g.doc_blk0[mid] <= j) lo = mid; else hi = mid - 1;
+  }
+  int s = g.doc_start[lo] + (j - g.doc_blk0[lo]) * g.BS;
+  return Blk{s, min(g.BS, g.doc_end[lo] - s)};
+}
+
+// Global block id of position p inside document d.
+__device__ __forceinline__ int block_of_pos(const Geom& g, const Doc& d, int p) {
+  return d.blk0 + (p - d.start) / g.BS;
+}
+
+// Key range [lo, hi] a row may attend to for each operation, and the block
+// range that covers it.
+enum Op { kScore = 0, kGather = 1, kSwa = 2 };
+
+struct RowRange {
+  int pos, lo, hi, j_first, j_last;
+};
+
+__device__ __forceinline__ RowRange row_range(const Geom& g, int op, int b, int r, int window) {
+  RowRange rr;
+  rr.pos = g.kv_len[b] - g.Sq + r;
+  Doc d = doc_of_pos(g, b, rr.pos);
+  rr.lo = d.start;
+  rr.hi = rr.pos;
+  if (op == kSwa) rr.lo = max(rr.lo, rr.pos - window + 1);
+  rr.j_first = block_of_pos(g, d, rr.lo);
+  rr.j_last = block_of_pos(g, d, rr.hi);
+  return rr;
+}
+
+}  // namespace hs

@@ -1,0 +1,52 @@
+// Kernel argument blocks and launchers used by the C ABI (hs_abi.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "hs_common.h"
+
+namespace hs {
+
+// Arguments of the attention kernels (both dtypes; q/kv/out are typed by the
+// launcher). Passed by value.
+struct AttnArgs {
+  const __bf16* q;
+  const __bf16* kv;
+  const float* sink;         // [H] or nullptr
+  __bf16* out;
+  float* lse;
+  float* block_logit;        // score operation only
+  const int* block_idx;      // gather operation only
+  int top_k;
+  int window;
+  int nsplit;                // > 1: split key range, partials merged after
+  float* ws_o;               // [items * nsplit, H, Dv] fp32 partial O
+  float* ws_ml;              // [items * nsplit, H, 2] fp32 (max, denominator)
+  Geom g;
+};
+
+struct AttnF32Args {
+  const float* q;
+  const float* kv;
+  const float* sink;
+  float* out;
+  float* lse;
+  float* block_logit;
+  const int* block_idx;
+  int top_k;
+  int window;
+  Geom g;
+};
+
+struct TopkArgs {
+  const float* block_logit;  // [B, Sq, NB]
+  int* block_idx;            // [B, Sq, top_k]
+  int top_k;
+  Geom g;
+};
+
+int attn_bf16_launch(int op, const AttnArgs& a, hipStream_t stream);
+int attn_f32_launch(int op, const AttnF32Args& a, hipStream_t stream);
+int topk_launch(const TopkArgs& a, hipStream_t stream);
+
+}  // namespace hs

@@ -1,0 +1,163 @@
+/*
+ * hs.h -- C ABI of the HySparse MQA sparse-attention forward path on MI355X
+ * (gfx950).
+ *
+ * The method (page "HySparse MQA sparse attention (FA4 block scoring + SWA MQA
+ * + block-sparse DSA gather)", sections "What" and "Core") is three
+ * cooperating structures over one shared latent KV head: a causal full
+ * attention that also emits a scaled score per key block, a per-token top-k
+ * selection of key blocks, and an attention that gathers only the selected
+ * blocks; a sliding-window MQA branch runs beside them. Every attention call
+ * takes an optional learnable per-head sink (same page, "Core", the learnable
+ * per-head attn_sink bullet).
+ *
+ * Shapes follow the absorbed-MLA layout of the same page, section "FlashMLA
+ * sparse kernel constraints": one KV head whose rows hold Dk = kv_lora_rank +
+ * rope columns; the value of key i is the leading Dv columns of that row.
+ *
+ * Supported instantiations (anything else returns HS_ERR_UNSUPPORTED):
+ *   HS_BF16: H = 64, Dk = 576, Dv = 512, block_size = 64
+ *   HS_F32 : 1 <= H <= 16, 1 <= Dk <= 128, 1 <= Dv <= Dk, block_size = 64
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layouts (row-major, innermost stride 1, all device pointers 16-byte
+ * aligned):
+ *   q           [B, Sq, H, Dk]   dtype
+ *   kv          [B, Skv, Dk]     dtype   (value = kv[..., :Dv])
+ *   sink        [H]              float32, or NULL (= no sink, i.e. -inf)
+ *   out         [B, Sq, H, Dv]   dtype
+ *   lse         [B, Sq, H]       float32, natural log, sink included
+ *   block_logit [B, Sq, NB]      float32, NB = hs_num_blocks()
+ *   block_idx   [B, Sq, top_k]   int32
+ * Positions: query row r of batch b sits at absolute position
+ *   p = L_b - Sq + r, where L_b = kv_lens[b] (or Skv when kv_lens is NULL);
+ * a decode token is the last row of its cache (blog page on the unified
+ * sparse-attention dispatcher, decode paragraph: key length = cache +
+ * current token). The allowed keys of p are doc_start(p) <= i <= p.
+ * Documents: optional packed-document bounds (B == 1, Sq == Skv, doc_start /
+ * doc_end tile [0, Sq) in ascending contiguous order). Blocks restart at each
+ * document's first row and never cross a document (review of PaddleFleet PR
+ * 1453, block-score PyLayer comments: the block_bos input). Block ids are
+ * global, numbered in document order.
+ * Ownership: every tensor pointer is caller-owned device memory; the library
+ * allocates nothing, keeps no pointer after return, and copies the small host
+ * arrays of hs_problem (kv_lens, doc_start, doc_end) by value into kernel
+ * arguments before returning.
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = default stream).
+ * Calls enqueue work and return without synchronising; a fault inside a
+ * kernel surfaces at the caller's next synchronisation.
+ * Errors: every check runs on the host before any launch; on failure nothing
+ * is launched, the status is returned and hs_last_error() holds a message
+ * (thread-local). Unsupported inputs are rejected, never silently ignored or
+ * routed to another implementation (page "Support attn sink in fa3": a path
+ * that cannot honour the sink must reject rather than drop it).
+ * Reentrancy: stateless apart from the thread-local error string.
+ */
+#ifndef HS_H_
+#define HS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HS_OK = 0,
+  HS_ERR_INVALID_ARG = -1,   /* NULL pointer, bad size, inconsistent documents */
+  HS_ERR_UNSUPPORTED = -2,   /* valid but not an instantiation built here      */
+  HS_ERR_HIP = -3,           /* the HIP runtime reported an error at launch    */
+  HS_ERR_WORKSPACE = -4      /* workspace missing or smaller than required     */
+} hs_status;
+
+typedef enum { HS_BF16 = 0, HS_F32 = 1 } hs_dtype;
+
+typedef enum { HS_OP_BLOCK_SCORE = 0, HS_OP_SPARSE_GATHER = 1, HS_OP_SWA = 2 } hs_op;
+
+typedef struct {
+  int32_t batch;          /* B                                                   */
+  int32_t seqlen_q;       /* Sq: query rows per batch entry                     */
+  int32_t seqlen_kv;      /* Skv: KV row stride per batch entry                 */
+  int32_t num_heads;      /* H: query heads sharing the one KV head             */
+  int32_t head_dim_qk;    /* Dk                                                 */
+  int32_t head_dim_v;     /* Dv <= Dk: value = leading Dv columns of kv         */
+  int32_t block_size;     /* key-block size (64)                                */
+  float scale;            /* softmax scale; <= 0 selects 1/sqrt(Dk)             */
+  int32_t dtype;          /* hs_dtype of q, kv and out                          */
+  const int32_t* kv_lens; /* HOST [B] valid KV length per entry, or NULL (=Skv) */
+  int32_t n_kv_lens;      /* must equal B when kv_lens is set (B <= 256)        */
+  const int32_t* doc_start; /* HOST [n_docs] packed documents, or NULL          */
+  const int32_t* doc_end;   /* HOST [n_docs]                                     */
+  int32_t n_docs;         /* 0, or 1..64 with B == 1 and kv_lens == NULL        */
+} hs_problem;
+
+/* Number of key blocks NB = columns of block_logit: the largest, over the
+ * batch, of sum over documents of ceil(L_d / block_size). Returns NB >= 1, or
+ * a negative hs_status if the problem is invalid. */
+int32_t hs_num_blocks(const hs_problem* p);
+
+/* Workspace bytes the given operation needs for this problem (0 when it
+ * needs none; single-token decode splits the key range across workgroups and
+ * merges partial results through the workspace). top_k and window are the
+ * values the operation will be called with (ignored where irrelevant). */
+hs_status hs_workspace_size(const hs_problem* p, int32_t op, int32_t top_k, int32_t window,
+                            size_t* bytes);
+
+/* Fused causal attention and block scores (page "HySparse MQA sparse
+ * attention ...", section "Core", first bullet; per-file table row for
+ * block_score_fa4.py: causal attention fused with a scaled block_logit).
+ *   out[b,r,h,:] = attention of q[b,r,h] over the allowed keys, with sink;
+ *   lse[b,r,h]   = natural-log normaliser, sink included;
+ *   block_logit[b,r,j] = max over heads h of ln sum over the allowed keys i
+ *                  of block j of exp(scale * q[b,r,h] . kv[b,i]); the sink is
+ *                  never part of it; -inf where block j has no allowed key
+ *                  (blocks of other documents, past the causal limit, or
+ *                  beyond this entry's block count). Every column is written.
+ * q, kv, out: dtype; sink may be NULL; ws/ws_bytes per hs_workspace_size. */
+hs_status hs_block_score_fwd(const hs_problem* p, const void* q, const void* kv,
+                             const float* sink, void* out, float* lse, float* block_logit,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* Per-token top-k block selection (same page, per-file table row for
+ * pipeline.py: top-k block selection on the block scores before the gather).
+ * For each row, C = {j : block_logit[j] > -inf}. If |C| <= top_k all of C is
+ * kept; otherwise the row's own block (the block holding its position) plus
+ * the top_k-1 best other blocks of C ordered by (score descending, index
+ * ascending). Indices are written ascending, padded with -1 to top_k entries.
+ * Comparisons are exact on the float32 inputs. 1 <= top_k <= 64. */
+hs_status hs_topk_blocks(const hs_problem* p, const float* block_logit, int32_t top_k,
+                         int32_t* block_idx, void* stream);
+
+/* Block-sparse gather attention (same page, "Core", block-sparse DSA gather
+ * bullet; per-file table row for block_sparse_mqa_dsa.py): attention with
+ * sink over the union of the listed blocks intersected with the allowed keys.
+ * Entries < 0 or >= the entry's block count are skipped; the entries of a row
+ * must be distinct (not checked: device data). */
+hs_status hs_sparse_gather_fwd(const hs_problem* p, const void* q, const void* kv,
+                               const float* sink, const int32_t* block_idx, int32_t top_k,
+                               void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Sliding-window MQA attention (same page, "Core", SWA bullet; per-file table
+ * rows for swa_attn.py and windowed_mqa_attn*.py): attention with sink over
+ * the allowed keys i with i >= p - window + 1 (window keys including the
+ * token itself). window >= 1. */
+hs_status hs_swa_fwd(const hs_problem* p, const void* q, const void* kv, const float* sink,
+                     int32_t window, void* out, float* lse, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Static description of a status code. */
+const char* hs_status_string(int32_t status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* hs_last_error(void);
+
+/* ABI version of this library (major * 100 + minor). */
+int32_t hs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HS_H_ */

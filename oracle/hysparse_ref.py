@@ -194,8 +194,8 @@ def merge_partials(outs: List[np.ndarray], lses: List[np.ndarray]):
 # The four operations.
 # ---------------------------------------------------------------------------
 def _prepare(q, kv, sink, Dv):
-    q = _to64(q)
-    kv = _to64(kv)
+    """Inputs stay as given (numpy or torch); rows are converted to float64
+    only when used, so sampled rows of a large problem stay cheap."""
     sk = None if sink is None else _to64(sink)
     B, Sq, H, Dk = q.shape
     assert kv.shape[0] == B and kv.shape[2] == Dk and Dv <= Dk
@@ -224,7 +224,7 @@ def _op(kind, q, kv, sink, Dv, scale, block_size, kv_lens=None, doc_start=None,
         L = _valid_len(b, Skv, kv_lens)
         bt = block_table(L, block_size, doc_start, doc_end)
         blk_of_key = bt.block_of_key(L)
-        k = kv[b, :L]
+        k = _to64(kv[b, :L])
         v = k[:, :Dv]
         # Bound the [rows, H, keys] float64 score array to about 2e7 entries.
         ch = chunk or max(1, int(2e7 // (H * max(1, L))))
@@ -246,7 +246,7 @@ def _op(kind, q, kv, sink, Dv, scale, block_size, kv_lens=None, doc_start=None,
                     ok = (j >= 0) & (j < bt.nb)
                     member |= ok[:, None] & (kb[None, :] == j[:, None])
                 allowed &= member
-            s = _scores(q[b, rows_sel[rr]], k[kmin:kmax], scale)
+            s = _scores(_to64(q[b, rows_sel[rr]]), k[kmin:kmax], scale)
             o, ls = _attend_masked(s, allowed, v[kmin:kmax], sk)
             out[b, rr] = o
             lse[b, rr] = ls

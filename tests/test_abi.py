@@ -1,0 +1,112 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects invalid arguments before any launch. No call
+here reaches the GPU (each one fails validation or is host-only), so these
+run on a machine without one."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_mqa_amd as hs
+from oracle import hysparse_ref as ref
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    with open(os.path.join(ROOT, "include", "hs.h")) as f:
+        src = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(hs_[a-z_0-9]+)\s*\(",
+                                 src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = hs.load_library()
+    names = _header_functions()
+    assert set(names) == set(hs.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.hs_version() == 100
+
+
+def _mla(**kw):
+    base = dict(B=1, Sq=128, Skv=128, H=64, Dk=576, Dv=512)
+    base.update(kw)
+    return hs.Problem(base.pop("B"), base.pop("Sq"), base.pop("Skv"), base.pop("H"),
+                      base.pop("Dk"), base.pop("Dv"), **base)
+
+
+@pytest.mark.parametrize("kw,exc", [
+    (dict(B=0), ValueError),
+    (dict(Sq=0), ValueError),
+    (dict(Sq=200), ValueError),                                # Sq > Skv
+    (dict(Dv=600, Dk=576), ValueError),                        # value wider than key
+    (dict(H=32), NotImplementedError),                         # not a built instantiation
+    (dict(block_size=32), NotImplementedError),
+    (dict(dtype="f32", H=32, Dk=96, Dv=64), NotImplementedError),
+    (dict(kv_lens=[100, 100]), ValueError),                    # n_kv_lens != B
+    (dict(kv_lens=[127], Sq=128), ValueError),                 # Sq > L_b
+    (dict(kv_lens=[129]), ValueError),                         # L_b > Skv
+    (dict(doc_start=[0, 60], doc_end=[60, 100]), ValueError),  # docs do not reach Sq
+    (dict(doc_start=[0, 61], doc_end=[60, 128]), ValueError),  # gap
+    (dict(doc_start=[0], doc_end=[128], B=2), ValueError),     # docs need B == 1
+    (dict(doc_start=list(range(0, 65 * 2, 2)), doc_end=list(range(2, 65 * 2 + 2, 2)),
+          Sq=130, Skv=130), NotImplementedError),              # more than 64 docs
+])
+def test_problem_validation(kw, exc):
+    with pytest.raises(exc):
+        hs.hs_num_blocks(_mla(**kw))
+
+
+def test_entry_points_reject_before_launch():
+    lib = hs.load_library()
+    p = _mla()
+    fake = ctypes.c_void_p(4096)
+    # NULL q
+    st = lib.hs_block_score_fwd(p.ref, None, fake, None, fake, fake, fake, None, 0, None)
+    assert st == hs.HS_ERR_INVALID_ARG and b"q is NULL" in lib.hs_last_error()
+    # misaligned kv
+    st = lib.hs_block_score_fwd(p.ref, fake, ctypes.c_void_p(4098), None, fake, fake, fake, None, 0, None)
+    assert st == hs.HS_ERR_INVALID_ARG and b"kv" in lib.hs_last_error()
+    # top_k out of range
+    st = lib.hs_topk_blocks(p.ref, fake, 0, fake, None)
+    assert st == hs.HS_ERR_INVALID_ARG
+    st = lib.hs_topk_blocks(p.ref, fake, 65, fake, None)
+    assert st == hs.HS_ERR_UNSUPPORTED
+    st = lib.hs_sparse_gather_fwd(p.ref, fake, fake, None, fake, 0, fake, fake, None, 0, None)
+    assert st == hs.HS_ERR_INVALID_ARG
+    # window < 1
+    st = lib.hs_swa_fwd(p.ref, fake, fake, None, 0, fake, fake, None, 0, None)
+    assert st == hs.HS_ERR_INVALID_ARG and b"window" in lib.hs_last_error()
+    # decode that needs a workspace but gets none
+    d = _mla(B=2, Sq=1, Skv=4096, kv_lens=[4096, 2000])
+    assert hs.hs_workspace_size(d, hs.HS_OP_BLOCK_SCORE) > 0
+    st = lib.hs_block_score_fwd(d.ref, fake, fake, None, fake, fake, fake, None, 0, None)
+    assert st == hs.HS_ERR_WORKSPACE
+    assert lib.hs_status_string(-2) == b"HS_ERR_UNSUPPORTED"
+
+
+@pytest.mark.parametrize("case", [
+    dict(L=512, docs=None, kv_lens=None, B=1),
+    dict(L=130, docs=None, kv_lens=None, B=1),
+    dict(L=200, docs=[(0, 70), (70, 71), (71, 134), (134, 200)], kv_lens=None, B=1),
+    dict(L=65536, docs=None, kv_lens=[16384, 65536, 17, 40000], B=4),
+])
+def test_block_count_matches_oracle(case):
+    docs = case["docs"]
+    ds = [a for a, _ in docs] if docs else None
+    de = [b for _, b in docs] if docs else None
+    Sq = 1 if case["kv_lens"] else case["L"]
+    p = _mla(B=case["B"], Sq=Sq, Skv=case["L"], kv_lens=case["kv_lens"], doc_start=ds, doc_end=de)
+    assert hs.hs_num_blocks(p) == ref.num_blocks(case["B"], case["L"], 64, case["kv_lens"], ds, de)
+
+
+def test_workspace_only_for_split_decode():
+    assert hs.hs_workspace_size(_mla(Sq=4096, Skv=4096), hs.HS_OP_BLOCK_SCORE) == 0
+    d = _mla(B=32, Sq=1, Skv=65536, kv_lens=[65536] * 32)
+    for op in (hs.HS_OP_BLOCK_SCORE, hs.HS_OP_SPARSE_GATHER, hs.HS_OP_SWA):
+        n = hs.hs_workspace_size(d, op, top_k=32, window=1024)
+        assert n > 0 and n % (32 * 64 * 4) == 0
+    assert hs.hs_workspace_size(_mla(dtype="f32", H=8, Dk=96, Dv=64, B=2, Sq=1, Skv=512,
+                                     kv_lens=[512, 3]), hs.HS_OP_BLOCK_SCORE) == 0
