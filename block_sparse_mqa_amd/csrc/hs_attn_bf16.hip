@@ -69,10 +69,48 @@ constexpr int TILE_BYTES = NCH * CH_STRIDE;  // 78336
 constexpr int KSTEPS = DK / 32;              // 18 k-steps of the score MFMA
 constexpr int DBLK = DV / 16;                // 32 column blocks of O
 constexpr float TAU = 8.0f;                  // lazy-rescale threshold (log2 units)
+constexpr int SG = 2;                        // k-steps per score prefetch group
+constexpr int PG = 8;                        // column blocks per PV prefetch group
 }  // namespace mla
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Cross-lane reductions without LDS round trips. A row (head) of the score
+// tile lives in lanes {l, l^16, l^32, l^48}; the heads of one wave are the
+// 16 lanes of a DPP row.
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Max over the 16 lanes of a DPP row: xor 1, xor 2, half-row mirror, row mirror.
+__device__ __forceinline__ float max_row16(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  v = fmaxf(v, dpp<0x140>(v));
+  return v;
+}
+
+// Wait for outstanding LDS reads only (lgkmcnt(0); vmcnt and expcnt left at
+// their maxima so in-flight tile copies keep running).
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Copy one 64-key tile (rows [start, start+len), clamped) into an LDS buffer.
 __device__ __forceinline__ void stage_tile(char* buf, const bf16* kv_entry, const Blk& blk,
@@ -92,7 +130,10 @@ template <int OP, bool SPLIT>
 __global__ __launch_bounds__(mla::NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_bf16_kernel(AttnArgs a) {
   using namespace mla;
-  __shared__ __attribute__((aligned(16))) char lds[2 * TILE_BYTES];
+  // Two separate buffers (not one array with a computed offset) so that the
+  // compiler can prove a tile copy in flight never aliases the tile being read.
+  __shared__ __attribute__((aligned(16))) char buf_a[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char buf_b[TILE_BYTES];
   __shared__ float bl_slot[2][NW];
   __shared__ int tile_list[64];
   __shared__ int tile_count;
@@ -155,9 +196,7 @@ void attn_bf16_kernel(AttnArgs a) {
   }
 
   const bf16* kv_entry = a.kv + (size_t)b * g.Skv * DK;
-  if (t_begin < t_end)
-    stage_tile(lds + (t_begin & 1) * TILE_BYTES, kv_entry, block_rows(g, b, tile_block(t_begin)),
-               wave, lane);
+  if (t_begin < t_end) stage_tile(buf_a, kv_entry, block_rows(g, b, tile_block(t_begin)), wave, lane);
 
   // Q rows of this wave as MFMA B operands: lane holds q[row, head, 32ks + 8grp .. +8].
   bf16x8 qreg[KSTEPS];
@@ -178,10 +217,11 @@ void attn_bf16_kernel(AttnArgs a) {
   int j_prev = -1;  // block whose score partials wait in bl_slot
   int par = 0;
 
-  for (int t = t_begin; t < t_end; ++t) {
+  // One tile: scores, block score, online softmax and PV on `cur`, while the
+  // next tile streams into `nxt`.
+  auto step = [&](char* cur, char* nxt, int t) __attribute__((always_inline)) {
     const int j = tile_block(t);
     const Blk blk = block_rows(g, b, j);
-    char* buf = lds + (t & 1) * TILE_BYTES;
 
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // tile t resident; tile t-1 fully consumed; partials visible
@@ -191,63 +231,84 @@ void attn_bf16_kernel(AttnArgs a) {
       for (int k = 1; k < NW; ++k) v = fmaxf(v, bl_slot[par ^ 1][k]);
       a.block_logit[row * g.NB + j_prev] = v * kLn2;
     }
-    if (t + 1 < t_end)
-      stage_tile(lds + ((t + 1) & 1) * TILE_BYTES, kv_entry, block_rows(g, b, tile_block(t + 1)),
-                 wave, lane);
+    if (t + 1 < t_end) stage_tile(nxt, kv_entry, block_rows(g, b, tile_block(t + 1)), wave, lane);
 
-    // S^T = K . Q^T over four 16-key blocks.
+    // S^T = K . Q^T over four 16-key blocks. K fragments are read from LDS
+    // one group of SG k-steps ahead; each group boundary first waits for the
+    // reads of the group about to be consumed (issued one group earlier).
     f32x4 s[4] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f},
                   f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    {
+      const HS_LDS char* kbase = (const HS_LDS char*)(cur + grp * CH_STRIDE + l16 * 16);
+      bf16x8 fa[4 * SG], fb[4 * SG];
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const HS_LDS char* base = (const HS_LDS char*)(buf + (4 * ks + grp) * CH_STRIDE + l16 * 16);
+      for (int u = 0; u < SG; ++u)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const bf16x8 kf = *(const HS_LDS bf16x8*)(base + kb * 256);
-        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qreg[ks], s[kb], 0, 0, 0);
+        for (int kb = 0; kb < 4; ++kb)
+          fa[4 * u + kb] = *(const HS_LDS bf16x8*)(kbase + (4 * u) * CH_STRIDE + kb * 256);
+#pragma unroll
+      for (int gi = 0; gi < KSTEPS / SG; ++gi) {
+        bf16x8* fc = (gi & 1) ? fb : fa;
+        bf16x8* fn = (gi & 1) ? fa : fb;
+        wait_lds();
+        if (gi + 1 < KSTEPS / SG) {
+#pragma unroll
+          for (int u = 0; u < SG; ++u)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+              fn[4 * u + kb] = *(const HS_LDS bf16x8*)(
+                  kbase + (4 * ((gi + 1) * SG + u)) * CH_STRIDE + kb * 256);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < SG; ++u)
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+            s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fc[4 * u + kb], qreg[gi * SG + u],
+                                                            s[kb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 
-    // Mask, log2 domain. s[kb][i] is key 16kb + 4grp + i of row l16.
+    // Log2 domain; s[kb][i] is key 16kb + 4grp + i of row l16. Keys outside
+    // [lo, hi] (or past the block end) are masked; interior tiles skip it.
     float x[16];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[4 * kb + i] = s[kb][i] * sl2;
     {
       const int klo = rr.lo - blk.start, khi = min(rr.hi - blk.start, blk.len - 1);
+      if (klo > 0 || khi < BS - 1) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = 16 * kb + 4 * grp + i;
-          x[4 * kb + i] = (m >= klo && m <= khi) ? s[kb][i] * sl2 : -INFINITY;
-        }
+          for (int i = 0; i < 4; ++i) {
+            const int m = 16 * kb + 4 * grp + i;
+            if (m < klo || m > khi) x[4 * kb + i] = -INFINITY;
+          }
+      }
     }
     float mx = x[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor32(max_xor16(mx));
 
     float p[16];
     float psum = 0.f;
-    if (mx == -INFINITY) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) p[i] = 0.f;
-    } else {
+    {
+      const float msafe = (mx == -INFINITY) ? 0.f : mx;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        p[i] = fast_exp2(x[i] - mx);
+        p[i] = fast_exp2(x[i] - msafe);
         psum += p[i];
       }
     }
 
     if (OP == kScore) {
-      float tot = psum + __shfl_xor(psum, 16);
-      tot += __shfl_xor(tot, 32);
+      const float tot = sum_xor32(sum_xor16(psum));
       float bl = (mx == -INFINITY) ? -INFINITY : mx + fast_log2(tot);
-      // max over the 16 heads of this wave (lanes differing in bits 0..3)
-      bl = fmaxf(bl, __shfl_xor(bl, 1));
-      bl = fmaxf(bl, __shfl_xor(bl, 2));
-      bl = fmaxf(bl, __shfl_xor(bl, 4));
-      bl = fmaxf(bl, __shfl_xor(bl, 8));
+      bl = max_row16(bl);  // max over the 16 heads of this wave
       if (lane == 0) bl_slot[par][wave] = bl;
       j_prev = j;
       par ^= 1;
@@ -275,23 +336,50 @@ void attn_bf16_kernel(AttnArgs a) {
     // O^T += V^T . P^T. The transpose read of lane group grp covers dims
     // 16db + 0..15; lane i of the group addresses key kbase + i/4, dims
     // 16db + 4(i%4) .. +3, and receives dim 16db + l16 for keys kbase .. +3.
-    const int dsub = 4 * (l16 & 3);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int k0 = 32 * kk + 4 * grp + (l16 >> 2);
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db) {
-        const int d0 = 16 * db + dsub;
-        const HS_LDS char* vb = (const HS_LDS char*)(buf + (d0 >> 3) * CH_STRIDE + (d0 & 7) * 2);
-        const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((HS_LDS bf16x4*)(vb + k0 * 16));
-        const bf16x4 hi4 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((HS_LDS bf16x4*)(vb + (k0 + 16) * 16));
+    // V^T fragments are read one group of PG column blocks ahead.
+    {
+      const int dsub = 4 * (l16 & 3);
+      const HS_LDS char* vbase = (const HS_LDS char*)(cur + (dsub >> 3) * CH_STRIDE +
+                                                       (dsub & 7) * 2 +
+                                                       (4 * grp + (l16 >> 2)) * 16);
+      auto vfrag = [&](int kk, int db) -> bf16x8 {
+        const HS_LDS char* vb = vbase + (2 * db) * CH_STRIDE + (32 * kk) * 16;
+        const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((HS_LDS bf16x4*)(vb));
+        const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((HS_LDS bf16x4*)(vb + 256));
         bf16x8 va;
         va[0] = lo4[0]; va[1] = lo4[1]; va[2] = lo4[2]; va[3] = lo4[3];
         va[4] = hi4[0]; va[5] = hi4[1]; va[6] = hi4[2]; va[7] = hi4[3];
-        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[kk], oacc[db], 0, 0, 0);
+        return va;
+      };
+      constexpr int NGRP = 2 * DBLK / PG;
+      bf16x8 va[PG], vb2[PG];
+#pragma unroll
+      for (int u = 0; u < PG; ++u) va[u] = vfrag(0, u);
+#pragma unroll
+      for (int gi = 0; gi < NGRP; ++gi) {
+        bf16x8* vc = (gi & 1) ? vb2 : va;
+        bf16x8* vn = (gi & 1) ? va : vb2;
+        wait_lds();
+        if (gi + 1 < NGRP) {
+          const int g1 = gi + 1;
+#pragma unroll
+          for (int u = 0; u < PG; ++u) vn[u] = vfrag((g1 * PG) / DBLK, (g1 * PG) % DBLK + u);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const int kk = (gi * PG) / DBLK;
+#pragma unroll
+        for (int u = 0; u < PG; ++u) {
+          const int db = (gi * PG) % DBLK + u;
+          oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vc[u], pb[kk], oacc[db], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+  };
+
+  for (int t = t_begin; t < t_end; t += 2) {
+    step(buf_a, buf_b, t);
+    if (t + 1 < t_end) step(buf_b, buf_a, t + 1);
   }
 
   if (OP == kScore) {
@@ -304,8 +392,7 @@ void attn_bf16_kernel(AttnArgs a) {
     }
   }
 
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  const float l_tot = sum_xor32(sum_xor16(l_run));
   // oacc[db][i] is O[row l16][dim 16db + 4grp + i].
   if (!SPLIT) {
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
