@@ -29,12 +29,14 @@
 //   taken straight from the S^T registers: inside each 32-key k-step the key
 //   order is permuted the same way on both operands, so P never moves.
 //
-// LDS tile layout: 72 column chunks of 8 bf16 (16 B); chunk c holds the 16 B
-//   of every key of the tile at [c * 1088 + key * 16]. The 64 B pad per chunk
-//   keeps the two chunks touched by one transpose-read lane group on
-//   different banks. Tiles are filled with global_load_lds_dwordx4 (lane l of
-//   a wave instruction writes 16 B at base + 16 l): one wave instruction per
-//   chunk, no VGPR staging.
+// LDS tile layout: 9 groups of 64 columns; group G holds, for each key k, the
+//   128 B of columns 64G .. 64G+63 at [G * 8192 + k * 128]. Inside those
+//   128 B, 16-byte chunk c8 (8 columns) sits in slot c8 ^ sw(k), with
+//   sw(k) = 2 * ((k >> 1) & 3) + ((k >> 3) & 1). The swizzle makes the 16
+//   keys of a score-fragment read, and the 8 keys x 2 chunks of a
+//   transpose-read half-wave, land on distinct banks. Tiles are filled with
+//   global_load_lds_dwordx4 (lane l of a wave instruction writes 16 B at base
+//   + 16 l): one instruction covers 8 keys x one full 128 B line each.
 //
 // Softmax: scores live in the log2 domain (scale * log2 e folded in). Per
 //   tile, p = exp2(x - m_tile): the tile max is the stabiliser of the block
@@ -63,9 +65,10 @@ constexpr int H = 64, DK = 576, DV = 512, BS = 64;
 constexpr int NW = 4;                        // waves per workgroup
 constexpr int RW = 16;                       // rows (heads) per wave
 constexpr int NTHREADS = 64 * NW;
-constexpr int NCH = DK / 8;                  // 72 chunks of 8 columns
-constexpr int CH_STRIDE = BS * 16 + 64;      // bytes per chunk region
-constexpr int TILE_BYTES = NCH * CH_STRIDE;  // 78336
+constexpr int NCH = DK / 8;                  // 72 chunks of 8 columns (16 B)
+constexpr int NGR = NCH / 8;                 // 9 groups of 8 chunks (64 columns)
+constexpr int GR_BYTES = BS * 128;           // one group: 64 keys x 128 B
+constexpr int TILE_BYTES = NGR * GR_BYTES;   // 73728
 constexpr int KSTEPS = DK / 32;              // 18 k-steps of the score MFMA
 constexpr int DBLK = DV / 16;                // 32 column blocks of O
 constexpr float TAU = 8.0f;                  // lazy-rescale threshold (log2 units)
@@ -113,16 +116,26 @@ __device__ __forceinline__ float max_row16(float v) {
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Copy one 64-key tile (rows [start, start+len), clamped) into an LDS buffer.
+// Instruction n = (G, kq) = (n / 8, n % 8) fills keys 8kq .. 8kq+7 of column
+// group G; lane l takes key 8kq + l/8 and stores slot l%8, i.e. chunk
+// (l%8) ^ sw(key). Wave w issues n = w + 4i, so kq alternates between w and
+// w + 4 and G = i / 2: two source rows per lane, immediate offsets otherwise.
 __device__ __forceinline__ void stage_tile(char* buf, const bf16* kv_entry, const Blk& blk,
-                                           int wave, int lane) {
+                                           int wave_u, int lane) {
   using namespace mla;
-  const int key = blk.start + min(lane, blk.len - 1);
-  const bf16* src = kv_entry + (size_t)key * DK;
+  const int kl = lane >> 3;                                    // key inside the octet
+  const int c8 = (lane & 7) ^ (2 * ((lane >> 4) & 3) + (wave_u & 1));
+  const int ka = min(8 * wave_u + kl, blk.len - 1);           // kq = w
+  const int kb = min(8 * (wave_u + 4) + kl, blk.len - 1);     // kq = w + 4
+  const char* src_a = (const char*)(kv_entry + (size_t)(blk.start + ka) * DK) + 16 * c8;
+  const char* src_b = (const char*)(kv_entry + (size_t)(blk.start + kb) * DK) + 16 * c8;
+  char* dst = buf + wave_u * 1024;
 #pragma unroll
-  for (int i = 0; i < NCH / NW; ++i) {
-    const int c = wave + NW * i;
-    __builtin_amdgcn_global_load_lds((const HS_GLB void*)(src + 8 * c),
-                                     (HS_LDS void*)(buf + c * CH_STRIDE), 16, 0, 0);
+  for (int G = 0; G < NGR; ++G) {
+    __builtin_amdgcn_global_load_lds((const HS_GLB void*)(src_a + 128 * G),
+                                     (HS_LDS void*)(dst + G * GR_BYTES), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const HS_GLB void*)(src_b + 128 * G),
+                                     (HS_LDS void*)(dst + G * GR_BYTES + 4096), 16, 0, 0);
   }
 }
 
@@ -140,7 +153,7 @@ void attn_bf16_kernel(AttnArgs a) {
 
   const Geom& g = a.g;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int grp = lane >> 4;     // 16-lane group: k-offset 8*grp inside a k-step
   const int l16 = lane & 15;
   const int head = wave * RW + l16;
@@ -239,13 +252,22 @@ void attn_bf16_kernel(AttnArgs a) {
     f32x4 s[4] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f},
                   f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     {
-      const HS_LDS char* kbase = (const HS_LDS char*)(cur + grp * CH_STRIDE + l16 * 16);
+      // Key 16kb + l16, chunk 4ks + grp = group ks/2, chunk-in-group
+      // c8 = 4 (ks & 1) + grp, stored in slot c8 ^ sw with sw depending only
+      // on l16 (bits 1..3 of the key). Even and odd k-steps use two bases.
+      const int swk = 2 * ((l16 >> 1) & 3) + ((l16 >> 3) & 1);
+      const HS_LDS char* kbe = (const HS_LDS char*)(cur + l16 * 128 + 16 * (grp ^ swk));
+      const HS_LDS char* kbo = (const HS_LDS char*)(cur + l16 * 128 + 16 * ((4 + grp) ^ swk));
+      auto kfrag = [&](int ks, int kb) -> bf16x8 {
+        const HS_LDS char* base = (ks & 1) ? kbo : kbe;
+        return *(const HS_LDS bf16x8*)(base + (ks >> 1) * GR_BYTES + kb * 2048);
+      };
       bf16x8 fa[4 * SG], fb[4 * SG];
 #pragma unroll
       for (int u = 0; u < SG; ++u)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
-          fa[4 * u + kb] = *(const HS_LDS bf16x8*)(kbase + (4 * u) * CH_STRIDE + kb * 256);
+          fa[4 * u + kb] = kfrag(u, kb);
 #pragma unroll
       for (int gi = 0; gi < KSTEPS / SG; ++gi) {
         bf16x8* fc = (gi & 1) ? fb : fa;
@@ -256,8 +278,7 @@ void attn_bf16_kernel(AttnArgs a) {
           for (int u = 0; u < SG; ++u)
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
-              fn[4 * u + kb] = *(const HS_LDS bf16x8*)(
-                  kbase + (4 * ((gi + 1) * SG + u)) * CH_STRIDE + kb * 256);
+              fn[4 * u + kb] = kfrag((gi + 1) * SG + u, kb);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -338,14 +359,20 @@ void attn_bf16_kernel(AttnArgs a) {
     // 16db + 4(i%4) .. +3, and receives dim 16db + l16 for keys kbase .. +3.
     // V^T fragments are read one group of PG column blocks ahead.
     {
-      const int dsub = 4 * (l16 & 3);
-      const HS_LDS char* vbase = (const HS_LDS char*)(cur + (dsub >> 3) * CH_STRIDE +
-                                                       (dsub & 7) * 2 +
-                                                       (4 * grp + (l16 >> 2)) * 16);
+      // Lane i of group grp reads key 32kk (+16) + 4grp + i/4, chunk
+      // 2db + ((i >> 1) & 1) (group db/4, chunk-in-group 2 (db & 3) + bit),
+      // byte 8 (i & 1) of it. sw(key) depends only on grp and i here, so four
+      // per-lane bases (one per db & 3) leave only immediate offsets.
+      const int kloc = 4 * grp + (l16 >> 2);
+      const int swv = 2 * ((kloc >> 1) & 3) + ((kloc >> 3) & 1);
+      const int tv = ((l16 >> 1) & 1) ^ swv;
+      const HS_LDS char* vb0 = (const HS_LDS char*)(cur + kloc * 128 + 8 * (l16 & 1));
+      const HS_LDS char* vbase[4] = {vb0 + 16 * (0 ^ tv), vb0 + 16 * (2 ^ tv), vb0 + 16 * (4 ^ tv),
+                                     vb0 + 16 * (6 ^ tv)};
       auto vfrag = [&](int kk, int db) -> bf16x8 {
-        const HS_LDS char* vb = vbase + (2 * db) * CH_STRIDE + (32 * kk) * 16;
+        const HS_LDS char* vb = vbase[db & 3] + (db >> 2) * GR_BYTES + (32 * kk) * 128;
         const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((HS_LDS bf16x4*)(vb));
-        const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((HS_LDS bf16x4*)(vb + 256));
+        const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((HS_LDS bf16x4*)(vb + 16 * 128));
         bf16x8 va;
         va[0] = lo4[0]; va[1] = lo4[1]; va[2] = lo4[2]; va[3] = lo4[3];
         va[4] = hi4[0]; va[5] = hi4[1]; va[6] = hi4[2]; va[7] = hi4[3];
