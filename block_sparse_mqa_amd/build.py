@@ -16,6 +16,10 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libhysparse.so")
 OBJDIR = os.path.join(HERE, "_build")
 SOURCES = ["hs_abi.hip", "hs_attn_bf16.hip", "hs_attn_f32.hip", "hs_topk.hip"]
+# Per-source extra flags. The bf16 engine keeps its MFMA accumulators in
+# VGPRs so that the O rescale and epilogue need no AGPR<->VGPR copies; Q and
+# other long-lived operands then go to AGPRs, which MFMA reads directly.
+EXTRA = {"hs_attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed-FP32 instructions are kept out of every kernel (plain fp32 code only).
@@ -26,7 +30,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
