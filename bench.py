@@ -110,6 +110,22 @@ def cpu_baseline(p, budget_s: float, seed: int = 0):
                       f"(block scores + top-k + gather per row, float64), {spent:.1f} s"}
 
 
+def counter_traffic(path: str, workload: str, kernel: str):
+    """HBM bytes per launch measured by rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+    (each scaled by the reading of a 1 GiB copy), or None when no record
+    exists or the kernel source changed since the counters were taken."""
+    import hashlib
+    try:
+        with open(path) as f:
+            rec = json.load(f)[workload][kernel]
+        with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest()[:16] != rec["source_sha256_16"]:
+                return None
+        return int(rec["bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 class Timer:
     """HIP events recorded on the stream the kernels run on."""
 
@@ -140,8 +156,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the path is built and measured on a single "
-              "MI355X (multi-GPU sharding is described in DESIGN.md but not part of this build).",
-              file=sys.stderr)
+              "MI355X; multi-GPU runs are not supported.", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -233,16 +248,7 @@ def main():
     tflops = ((f_score + (f_gather or 0)) / (ms_per_step * 1e-3) / 1e12)
     achieved = f_score / (k_ms[0] * 1e-3) / 1e12
 
-    traffic = None
-    if os.path.exists(args.traffic_json):
-        try:
-            with open(args.traffic_json) as f:
-                tj = json.load(f)
-            rec = tj.get(p.name, {}).get("block_score")
-            if rec:
-                traffic = rec.get("bytes_per_launch")
-        except Exception:
-            traffic = None
+    traffic = counter_traffic(args.traffic_json, p.name, "block_score")
 
     res = {
         "metric": METRIC,
