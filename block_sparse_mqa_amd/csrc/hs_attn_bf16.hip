@@ -63,6 +63,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 namespace mla {
 constexpr int H = 64, DK = 576, DV = 512, BS = 64;
 constexpr int NW = 4;                        // waves per workgroup
+constexpr int RW = 16;                       // rows (heads) per wave
 constexpr int NTHREADS = 64 * NW;
 constexpr int NCH = DK / 8;                  // 72 chunks of 8 columns (16 B)
 constexpr int NGR = NCH / 8;                 // 9 groups of 8 chunks (64 columns)
@@ -71,8 +72,14 @@ constexpr int TILE_BYTES = NGR * GR_BYTES;   // 73728
 constexpr int KSTEPS = DK / 32;              // 18 k-steps of the score MFMA
 constexpr int DBLK = DV / 16;                // 32 column blocks of O
 constexpr float TAU = 8.0f;                  // lazy-rescale threshold (log2 units)
-constexpr int SG = 2;                        // k-steps per score prefetch group
-constexpr int PG = 8;                        // column blocks per PV prefetch group
+#ifndef HS_SG
+#define HS_SG 2
+#endif
+#ifndef HS_PG
+#define HS_PG 8
+#endif
+constexpr int SG = HS_SG;                    // k-steps per score prefetch group
+constexpr int PG = HS_PG;                    // column blocks per PV prefetch group
 }  // namespace mla
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -146,20 +153,16 @@ void attn_bf16_kernel(AttnArgs a) {
   // compiler can prove a tile copy in flight never aliases the tile being read.
   __shared__ __attribute__((aligned(16))) char buf_a[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char buf_b[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) bf16x8 px[NW][2][64];  // P^T operands per wave
-  __shared__ float mx_x[NW][2][16];                               // half-tile row max / l
-  __shared__ float ps_x[NW][2][16];                               // half-tile row sums
-  __shared__ float bl_slot[2][2];
+  __shared__ float bl_slot[2][NW];
   __shared__ int tile_list[64];
   __shared__ int tile_count;
 
   const Geom& g = a.g;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int rh = wave >> 1;      // head half: heads 32rh .. 32rh+31 (two 16-row blocks)
-  const int dh = wave & 1;       // key half of the scores / column half of O
   const int grp = lane >> 4;     // 16-lane group: k-offset 8*grp inside a k-step
   const int l16 = lane & 15;
+  const int head = wave * RW + l16;
 
   // Work item: heaviest query rows first (causal cost grows with position).
   int w = blockIdx.x;
@@ -214,247 +217,251 @@ void attn_bf16_kernel(AttnArgs a) {
   const bf16* kv_entry = a.kv + (size_t)b * g.Skv * DK;
   if (t_begin < t_end) stage_tile(buf_a, kv_entry, block_rows(g, b, tile_block(t_begin)), wave, lane);
 
-  // Q of the two head blocks as MFMA B operands: lane holds
-  // q[row, 32rh + 16hb + l16, 32ks + 8grp .. +8].
-  bf16x8 qreg[2][KSTEPS];
+  // Q rows of this wave as MFMA B operands: lane holds q[row, head, 32ks + 8grp .. +8].
+  bf16x8 qreg[KSTEPS];
+  {
+    const bf16* qp = a.q + (row * H + head) * DK + 8 * grp;
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const bf16* qp = a.q + (row * H + 32 * rh + 16 * hb + l16) * DK + 8 * grp;
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) qreg[hb][ks] = *(const bf16x8*)(qp + 32 * ks);
+    for (int ks = 0; ks < KSTEPS; ++ks) qreg[ks] = *(const bf16x8*)(qp + 32 * ks);
   }
 
-  // Running state per head block. The sink enters once per row: on the
-  // column-half-0 wave, as the initial reference with weight 1.
-  float m_run[2], l_run[2];
+  const float sk = (a.sink != nullptr && split == 0) ? a.sink[head] * kLog2e : -INFINITY;
+  float m_run = sk;
+  float l_run = (sk > -INFINITY && grp == 0) ? 1.0f : 0.0f;  // lane-partial denominator
+  f32x4 oacc[DBLK];
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const float sk = (a.sink != nullptr && split == 0) ? a.sink[32 * rh + 16 * hb + l16] * kLog2e
-                                                       : -INFINITY;
-    m_run[hb] = sk;
-    l_run[hb] = (sk > -INFINITY && dh == 0 && grp == 0) ? 1.0f : 0.0f;
-  }
-  f32x4 oacc[2][DBLK / 2];  // O^T[dims 256dh + 16dbl + 4grp + i][head 32rh + 16hb + l16]
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-    for (int d = 0; d < DBLK / 2; ++d) oacc[hb][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < DBLK; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const float sl2 = g.scale_log2;
   int j_prev = -1;  // block whose score partials wait in bl_slot
   int par = 0;
 
-  // Per-lane LDS bases. Score fragments: key 16kb + l16, chunk 4ks + grp
-  // (group ks/2, chunk-in-group 4 (ks & 1) + grp) in slot c8 ^ sw(key).
+  // Per-lane LDS bases of the score fragments: key 16kb + l16, chunk 4ks +
+  // grp (group ks/2, chunk-in-group 4 (ks & 1) + grp) in slot c8 ^ sw(key),
+  // where sw depends only on l16 here.
   const int swk = 2 * ((l16 >> 1) & 3) + ((l16 >> 3) & 1);
   const int koff_e = l16 * 128 + 16 * (grp ^ swk);
   const int koff_o = l16 * 128 + 16 * ((4 + grp) ^ swk);
   // Transpose reads: lane i of group grp reads key 32kk (+16) + 4grp + i/4,
-  // chunk 2db + ((i >> 1) & 1), byte 8 (i & 1); four bases for db & 3.
+  // chunk 2db + ((i >> 1) & 1), byte 8 (i & 1); one base per db & 3.
   const int kloc = 4 * grp + (l16 >> 2);
   const int swv = 2 * ((kloc >> 1) & 3) + ((kloc >> 3) & 1);
   const int tv = ((l16 >> 1) & 1) ^ swv;
   const int voff = kloc * 128 + 8 * (l16 & 1);
+  // Tile copy: lane l of instruction (G, kq) takes key 8kq + l/8 and stores
+  // chunk (l%8) ^ sw(key) in slot l%8; wave w issues kq = w and w + 4.
+  const int cp_c8 = (lane & 7) ^ (2 * ((lane >> 4) & 3) + (wave & 1));
 
-  // One tile: half-tile scores, max exchange, P exchange, PV on own columns,
-  // while the next tile streams into `nxt`.
+  // One tile, processed as two 32-key halves so that in-order issue can
+  // overlap VALU with MFMA: the softmax of half 0 runs between the score
+  // MFMAs of half 1, the softmax of half 1 between the PV MFMAs of half 0,
+  // and the block score between those of half 1. The copy of the next tile
+  // is spread over the score MFMAs of half 0.
   auto step = [&](char* cur, char* nxt, int t) __attribute__((always_inline)) {
     const int j = tile_block(t);
     const Blk blk = block_rows(g, b, j);
+    const int klo = rr.lo - blk.start, khi = min(rr.hi - blk.start, blk.len - 1);
 
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // tile t resident; tile t-1 fully consumed; partials visible
     if (OP == kScore && j_prev >= 0 && threadIdx.x == 0) {
-      const float v = fmaxf(bl_slot[par ^ 1][0], bl_slot[par ^ 1][1]);
+      float v = bl_slot[par ^ 1][0];
+#pragma unroll
+      for (int k = 1; k < NW; ++k) v = fmaxf(v, bl_slot[par ^ 1][k]);
       a.block_logit[row * g.NB + j_prev] = v * kLn2;
     }
-    if (t + 1 < t_end) stage_tile(nxt, kv_entry, block_rows(g, b, tile_block(t + 1)), wave, lane);
+    const bool has_next = t + 1 < t_end;
+    const char* cp_a = nullptr;
+    const char* cp_b = nullptr;
+    char* cp_dst = nxt + wave * 1024;
+    if (has_next) {
+      const Blk nb = block_rows(g, b, tile_block(t + 1));
+      const int ka = min(8 * wave + (lane >> 3), nb.len - 1);
+      const int kb2 = min(8 * (wave + 4) + (lane >> 3), nb.len - 1);
+      cp_a = (const char*)(kv_entry + (size_t)(nb.start + ka) * DK) + 16 * cp_c8;
+      cp_b = (const char*)(kv_entry + (size_t)(nb.start + kb2) * DK) + 16 * cp_c8;
+    }
 
-    // S^T for keys 32dh .. 32dh+31 (local key blocks kbl = 0, 1) of both head
-    // blocks; each K fragment feeds two MFMAs.
-    f32x4 s[2][2];
+    const HS_LDS char* kbe = (const HS_LDS char*)(cur + koff_e);
+    const HS_LDS char* kbo = (const HS_LDS char*)(cur + koff_o);
+    auto kfrag = [&](int ks, int kb) -> bf16x8 {
+      const HS_LDS char* base = (ks & 1) ? kbo : kbe;
+      return *(const HS_LDS bf16x8*)(base + (ks >> 1) * GR_BYTES + kb * 2048);
+    };
+    const HS_LDS char* vb0 = (const HS_LDS char*)(cur + voff);
+    auto vfrag = [&](int kk, int db) -> bf16x8 {
+      const HS_LDS char* vb =
+          vb0 + 16 * ((2 * (db & 3)) ^ tv) + (db >> 2) * GR_BYTES + (32 * kk) * 128;
+      const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((HS_LDS bf16x4*)(vb));
+      const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((HS_LDS bf16x4*)(vb + 16 * 128));
+      bf16x8 va;
+      va[0] = lo4[0]; va[1] = lo4[1]; va[2] = lo4[2]; va[3] = lo4[3];
+      va[4] = hi4[0]; va[5] = hi4[1]; va[6] = hi4[2]; va[7] = hi4[3];
+      return va;
+    };
+
+    // Softmax of one half in nine small pieces, issued between MFMAs.
+    // x: the 8 scores of this lane (key blocks 2h, 2h+1), then p.
+    float xh[2][8];
+    float mh[2], sh[2], ph_lane[2];
+    auto soft_piece = [&](int h, int piece, const f32x4* sp) __attribute__((always_inline)) {
+      float* x = xh[h];
+      switch (piece) {
+        case 0:
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
+          for (int i = 0; i < 4; ++i) x[i] = sp[2 * h][i] * sl2;
+          break;
+        case 1:
 #pragma unroll
-      for (int kbl = 0; kbl < 2; ++kbl) s[hb][kbl] = f32x4{0.f, 0.f, 0.f, 0.f};
-    {
-      const HS_LDS char* kbe = (const HS_LDS char*)(cur + koff_e + dh * 4096);
-      const HS_LDS char* kbo = (const HS_LDS char*)(cur + koff_o + dh * 4096);
-      auto kfrag = [&](int ks, int kbl) -> bf16x8 {
-        const HS_LDS char* base = (ks & 1) ? kbo : kbe;
-        return *(const HS_LDS bf16x8*)(base + (ks >> 1) * GR_BYTES + kbl * 2048);
-      };
-      bf16x8 fa[2 * SG], fb[2 * SG];
+          for (int i = 0; i < 4; ++i) x[4 + i] = sp[2 * h + 1][i] * sl2;
+          if (klo > 32 * h || khi < 32 * h + 31) {
 #pragma unroll
-      for (int u = 0; u < SG; ++u)
+            for (int e = 0; e < 8; ++e) {
+              const int m = 32 * h + 16 * (e >> 2) + 4 * grp + (e & 3);
+              if (m < klo || m > khi) x[e] = -INFINITY;
+            }
+          }
+          break;
+        case 2: {
+          float m = x[0];
 #pragma unroll
-        for (int kbl = 0; kbl < 2; ++kbl) fa[2 * u + kbl] = kfrag(u, kbl);
-#pragma unroll
-      for (int gi = 0; gi < KSTEPS / SG; ++gi) {
-        bf16x8* fc = (gi & 1) ? fb : fa;
-        bf16x8* fn = (gi & 1) ? fa : fb;
-        wait_lds();
-        if (gi + 1 < KSTEPS / SG) {
-#pragma unroll
-          for (int u = 0; u < SG; ++u)
-#pragma unroll
-            for (int kbl = 0; kbl < 2; ++kbl) fn[2 * u + kbl] = kfrag((gi + 1) * SG + u, kbl);
+          for (int e = 1; e < 8; ++e) m = fmaxf(m, x[e]);
+          mh[h] = max_xor16(m);
+          break;
         }
-        __builtin_amdgcn_sched_barrier(0);
+        case 3:
+          mh[h] = max_xor32(mh[h]);
+          break;
+        case 4: {
+          const float ms = (mh[h] == -INFINITY) ? 0.f : mh[h];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = fast_exp2(x[e] - ms);
+          break;
+        }
+        case 5: {
+          const float ms = (mh[h] == -INFINITY) ? 0.f : mh[h];
+#pragma unroll
+          for (int e = 4; e < 8; ++e) x[e] = fast_exp2(x[e] - ms);
+          break;
+        }
+        case 6: {
+          float ps = x[0];
+#pragma unroll
+          for (int e = 1; e < 8; ++e) ps += x[e];
+          ph_lane[h] = ps;
+          break;
+        }
+        case 7:
+          sh[h] = sum_xor16(ph_lane[h]);
+          break;
+        default:
+          sh[h] = sum_xor32(sh[h]);
+          break;
+      }
+    };
+    // Online-softmax update for half h (rare rescale) and its bf16 P^T operand.
+    auto finish_half = [&](int h) __attribute__((always_inline)) -> bf16x8 {
+      if (mh[h] > m_run + TAU) {
+        const float alpha = fast_exp2(m_run - mh[h]);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) oacc[db] *= alpha;
+        m_run = mh[h];
+      }
+      const float f = (mh[h] == -INFINITY) ? 0.f : fast_exp2(mh[h] - m_run);
+      l_run += ph_lane[h] * f;
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[e] = (bf16)(xh[h][e] * f);
+      return pb;
+    };
+
+    f32x4 s[4] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f},
+                  f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    constexpr int NG = KSTEPS / SG;  // 9 groups per half
+    bf16x8 fa[2 * SG], fb[2 * SG];
+#pragma unroll
+    for (int u = 0; u < SG; ++u)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) fa[2 * u + k] = kfrag(u, k);
+    // Scores, both halves: group gi of half h uses key blocks 2h, 2h+1.
+#pragma unroll
+    for (int n = 0; n < 2 * NG; ++n) {
+      const int h = n / NG, gi = n % NG;
+      bf16x8* fc = (n & 1) ? fb : fa;
+      bf16x8* fn = (n & 1) ? fa : fb;
+      wait_lds();
+      if (n + 1 < 2 * NG) {
+        const int h1 = (n + 1) / NG, g1 = (n + 1) % NG;
 #pragma unroll
         for (int u = 0; u < SG; ++u)
 #pragma unroll
-          for (int kbl = 0; kbl < 2; ++kbl)
-#pragma unroll
-            for (int hb = 0; hb < 2; ++hb)
-              s[hb][kbl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  fc[2 * u + kbl], qreg[hb][gi * SG + u], s[hb][kbl], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+          for (int k = 0; k < 2; ++k) fn[2 * u + k] = kfrag(g1 * SG + u, 2 * h1 + k);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < SG; ++u)
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+          s[2 * h + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fc[2 * u + k], qreg[gi * SG + u],
+                                                                 s[2 * h + k], 0, 0, 0);
+      if (h == 0) {
+        if (has_next) {
+          __builtin_amdgcn_global_load_lds((const HS_GLB void*)(cp_a + 128 * gi),
+                                           (HS_LDS void*)(cp_dst + gi * GR_BYTES), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((const HS_GLB void*)(cp_b + 128 * gi),
+                                           (HS_LDS void*)(cp_dst + gi * GR_BYTES + 4096), 16, 0,
+                                           0);
+        }
+      } else {
+        soft_piece(0, gi, s);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
 
-    // Log2 domain; s[hb][kbl][i] is key 32dh + 16kbl + 4grp + i of head block
-    // hb, row l16. Keys outside [lo, hi] or past the block end are masked.
-    float x[2][8];
+    // PV over the two 32-key k-steps; V^T fragments one group ahead.
+    constexpr int NGRP = DBLK / PG;  // groups per k-step
+    bf16x8 va[PG], vb2[PG];
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
+    for (int u = 0; u < PG; ++u) va[u] = vfrag(0, u);
+    bf16x8 pb0 = finish_half(0);
+    bf16x8 pb1;
 #pragma unroll
-      for (int kbl = 0; kbl < 2; ++kbl)
+    for (int n = 0; n < 2 * NGRP; ++n) {
+      const int kk = n / NGRP, gi = n % NGRP;
+      bf16x8* vc = (n & 1) ? vb2 : va;
+      bf16x8* vn = (n & 1) ? va : vb2;
+      if (n == NGRP) pb1 = finish_half(1);
+      wait_lds();
+      if (n + 1 < 2 * NGRP) {
+        const int kk1 = (n + 1) / NGRP, g1 = (n + 1) % NGRP;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[hb][4 * kbl + i] = s[hb][kbl][i] * sl2;
-    {
-      const int klo = rr.lo - blk.start, khi = min(rr.hi - blk.start, blk.len - 1);
-      if (klo > 32 * dh || khi < 32 * dh + 31) {
-#pragma unroll
-        for (int kbl = 0; kbl < 2; ++kbl)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int m = 32 * dh + 16 * kbl + 4 * grp + i;
-            if (m < klo || m > khi) {
-              x[0][4 * kbl + i] = -INFINITY;
-              x[1][4 * kbl + i] = -INFINITY;
-            }
-          }
+        for (int u = 0; u < PG; ++u) vn[u] = vfrag(kk1, g1 * PG + u);
       }
-    }
-    float mh[2];
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      float m = x[hb][0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) m = fmaxf(m, x[hb][i]);
-      mh[hb] = max_xor32(max_xor16(m));
-    }
-    if (grp == 0) {
-      mx_x[wave][0][l16] = mh[0];
-      mx_x[wave][1][l16] = mh[1];
-    }
-    __syncthreads();  // half-tile maxima visible
-    float mt[2], f[2], psum[2];
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      mt[hb] = fmaxf(mh[hb], mx_x[wave ^ 1][hb][l16]);
-      const float msafe = (mt[hb] == -INFINITY) ? 0.f : mt[hb];
-      float ps = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        x[hb][i] = fast_exp2(x[hb][i] - msafe);  // now p
-        ps += x[hb][i];
+      for (int u = 0; u < PG; ++u) {
+        const int db = gi * PG + u;
+        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vc[u], kk ? pb1 : pb0, oacc[db], 0, 0, 0);
       }
-      psum[hb] = sum_xor32(sum_xor16(ps));
-      // Online softmax with a lazily raised reference max; both waves of the
-      // pair see the same tile max, so they take the same decisions.
-      if (mt[hb] > m_run[hb] + TAU) {
-        const float alpha = fast_exp2(m_run[hb] - mt[hb]);
-        l_run[hb] *= alpha;
-#pragma unroll
-        for (int d = 0; d < DBLK / 2; ++d) oacc[hb][d] *= alpha;
-        m_run[hb] = mt[hb];
+      if (kk == 0) {
+        // softmax of half 1 in the shadow of the half-0 PV MFMAs
+        for (int piece = (9 * gi) / NGRP; piece < (9 * (gi + 1)) / NGRP; ++piece)
+          soft_piece(1, piece, s);
+      } else if (OP == kScore && gi == 0) {
+        // block log-sum-exp over both halves, then max over the wave's heads
+        const float M = fmaxf(mh[0], mh[1]);
+        float bl = -INFINITY;
+        if (M > -INFINITY)
+          bl = M + fast_log2(sh[0] * fast_exp2(mh[0] - M) + sh[1] * fast_exp2(mh[1] - M));
+        bl = max_row16(bl);
+        if (lane == 0) bl_slot[par][wave] = bl;
       }
-      f[hb] = (mt[hb] == -INFINITY) ? 0.f : fast_exp2(mt[hb] - m_run[hb]);
-      if (grp == 0) l_run[hb] += psum[hb] * f[hb];
+      __builtin_amdgcn_sched_barrier(0);
     }
-
-    // P^T B operands of the own 32-key half, shared with the partner wave,
-    // which owns the other half.
-    bf16x8 p_own[2], p_oth[2];
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) p_own[hb][e] = (bf16)(x[hb][e] * f[hb]);
-      px[wave][hb][lane] = p_own[hb];
-    }
-    if (grp == 0) {
-      ps_x[wave][0][l16] = psum[0];
-      ps_x[wave][1][l16] = psum[1];
-    }
-    __syncthreads();  // P halves and half sums visible
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) p_oth[hb] = px[wave ^ 1][hb][lane];
-
     if (OP == kScore) {
-      // Block log-sum-exp of each head over all 64 keys; max over the heads.
-      float bl = -INFINITY;
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const float tot = psum[hb] + ps_x[wave ^ 1][hb][l16];
-        const float v = (mt[hb] == -INFINITY) ? -INFINITY : mt[hb] + fast_log2(tot);
-        bl = fmaxf(bl, v);
-      }
-      bl = max_row16(bl);
-      if (dh == 0 && lane == 0) bl_slot[par][rh] = bl;
       j_prev = j;
       par ^= 1;
-    }
-
-    // O^T[own 256 columns] += V^T . P^T over both 32-key k-steps (k-step 0 =
-    // the own key half, 1 = the partner's). Each V^T fragment feeds both head
-    // blocks.
-    {
-      const HS_LDS char* vb_own =
-          (const HS_LDS char*)(cur + voff + (4 * dh) * GR_BYTES + (32 * dh) * 128);
-      const HS_LDS char* vb_oth =
-          (const HS_LDS char*)(cur + voff + (4 * dh) * GR_BYTES + (32 * (dh ^ 1)) * 128);
-      auto vfrag = [&](int kk, int dbl) -> bf16x8 {
-        // global column block 16dh + dbl: group 4dh + dbl/4, chunk pair dbl & 3
-        const HS_LDS char* vb = (kk ? vb_oth : vb_own) + 16 * ((2 * (dbl & 3)) ^ tv) +
-                                (dbl >> 2) * GR_BYTES;
-        const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((HS_LDS bf16x4*)(vb));
-        const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((HS_LDS bf16x4*)(vb + 16 * 128));
-        bf16x8 va;
-        va[0] = lo4[0]; va[1] = lo4[1]; va[2] = lo4[2]; va[3] = lo4[3];
-        va[4] = hi4[0]; va[5] = hi4[1]; va[6] = hi4[2]; va[7] = hi4[3];
-        return va;
-      };
-      constexpr int NV = 2 * (DBLK / 2);  // (kk, dbl) fragments
-      constexpr int NGRP = NV / PG;
-      bf16x8 va[PG], vb2[PG];
-#pragma unroll
-      for (int u = 0; u < PG; ++u) va[u] = vfrag(u / (DBLK / 2), u % (DBLK / 2));
-#pragma unroll
-      for (int gi = 0; gi < NGRP; ++gi) {
-        bf16x8* vc = (gi & 1) ? vb2 : va;
-        bf16x8* vn = (gi & 1) ? va : vb2;
-        wait_lds();
-        if (gi + 1 < NGRP) {
-#pragma unroll
-          for (int u = 0; u < PG; ++u) {
-            const int n = (gi + 1) * PG + u;
-            vn[u] = vfrag(n / (DBLK / 2), n % (DBLK / 2));
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < PG; ++u) {
-          const int n = gi * PG + u;
-          const int kk = n / (DBLK / 2), dbl = n % (DBLK / 2);
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb)
-            oacc[hb][dbl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                vc[u], kk ? p_oth[hb] : p_own[hb], oacc[hb][dbl], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
     }
   };
 
@@ -463,53 +470,41 @@ void attn_bf16_kernel(AttnArgs a) {
     if (t + 1 < t_end) step(buf_b, buf_a, t + 1);
   }
 
-  // Row denominators: each wave holds the partial of its own key halves.
-  float l_part[2];
+  if (OP == kScore) {
+    __syncthreads();
+    if (j_prev >= 0 && threadIdx.x == 0) {
+      float v = bl_slot[par ^ 1][0];
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb) l_part[hb] = sum_xor32(sum_xor16(l_run[hb]));
-  __syncthreads();
-  if (OP == kScore && j_prev >= 0 && threadIdx.x == 0) {
-    const float v = fmaxf(bl_slot[par ^ 1][0], bl_slot[par ^ 1][1]);
-    a.block_logit[row * g.NB + j_prev] = v * kLn2;
+      for (int k = 1; k < NW; ++k) v = fmaxf(v, bl_slot[par ^ 1][k]);
+      a.block_logit[row * g.NB + j_prev] = v * kLn2;
+    }
   }
-  if (grp == 0) {
-    mx_x[wave][0][l16] = l_part[0];
-    mx_x[wave][1][l16] = l_part[1];
-  }
-  __syncthreads();
-  float l_tot[2];
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb) l_tot[hb] = l_part[hb] + mx_x[wave ^ 1][hb][l16];
 
-  // oacc[hb][dbl][i] is O[head 32rh + 16hb + l16][column 256dh + 16dbl + 4grp + i].
+  const float l_tot = sum_xor32(sum_xor16(l_run));
+  // oacc[db][i] is O[row l16][dim 16db + 4grp + i].
+  if (!SPLIT) {
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    bf16* op = a.out + (row * H + head) * DV + 4 * grp;
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const int head = 32 * rh + 16 * hb + l16;
-    if (!SPLIT) {
-      const float inv = l_tot[hb] > 0.f ? 1.0f / l_tot[hb] : 0.f;
-      bf16* op = a.out + (row * H + head) * DV + 256 * dh + 4 * grp;
+    for (int db = 0; db < DBLK; ++db) {
+      bf16x4 v;
+      v[0] = (bf16)(oacc[db][0] * inv);
+      v[1] = (bf16)(oacc[db][1] * inv);
+      v[2] = (bf16)(oacc[db][2] * inv);
+      v[3] = (bf16)(oacc[db][3] * inv);
+      *(bf16x4*)(op + 16 * db) = v;
+    }
+    if (grp == 0)
+      a.lse[row * H + head] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
+  } else {
+    // Unnormalised partial: O (fp32), reference max (log2) and denominator.
+    const size_t slot = (size_t)w * a.nsplit + split;
+    float* op = a.ws_o + (slot * H + head) * DV + 4 * grp;
 #pragma unroll
-      for (int d = 0; d < DBLK / 2; ++d) {
-        bf16x4 v;
-        v[0] = (bf16)(oacc[hb][d][0] * inv);
-        v[1] = (bf16)(oacc[hb][d][1] * inv);
-        v[2] = (bf16)(oacc[hb][d][2] * inv);
-        v[3] = (bf16)(oacc[hb][d][3] * inv);
-        *(bf16x4*)(op + 16 * d) = v;
-      }
-      if (dh == 0 && grp == 0)
-        a.lse[row * H + head] =
-            l_tot[hb] > 0.f ? (m_run[hb] + fast_log2(l_tot[hb])) * kLn2 : -INFINITY;
-    } else {
-      // Unnormalised partial: O (fp32), reference max (log2) and denominator.
-      const size_t slot = (size_t)w * a.nsplit + split;
-      float* op = a.ws_o + (slot * H + head) * DV + 256 * dh + 4 * grp;
-#pragma unroll
-      for (int d = 0; d < DBLK / 2; ++d) *(f32x4*)(op + 16 * d) = oacc[hb][d];
-      if (dh == 0 && grp == 0) {
-        a.ws_ml[(slot * H + head) * 2 + 0] = m_run[hb];
-        a.ws_ml[(slot * H + head) * 2 + 1] = l_tot[hb];
-      }
+    for (int db = 0; db < DBLK; ++db) *(f32x4*)(op + 16 * db) = oacc[db];
+    if (grp == 0) {
+      a.ws_ml[(slot * H + head) * 2 + 0] = m_run;
+      a.ws_ml[(slot * H + head) * 2 + 1] = l_tot;
     }
   }
 }
