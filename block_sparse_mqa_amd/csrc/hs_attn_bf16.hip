@@ -359,21 +359,28 @@ void attn_bf16_kernel(AttnArgs a) {
           break;
       }
     };
-    // Online-softmax update for half h (rare rescale) and its bf16 P^T operand.
-    auto finish_half = [&](int h) __attribute__((always_inline)) -> bf16x8 {
+    // Online-softmax update for half h and its bf16 P^T operand, in two
+    // parts: prepare() assumes the reference max stays (the common case) and
+    // can run in an MFMA shadow; commit() raises the reference when the half's
+    // max exceeds it by more than TAU (rare), which rescales O and redoes P.
+    bf16x8 pbh[2];
+    float lph[2];
+    auto prepare_half = [&](int h) __attribute__((always_inline)) {
+      const float f = (mh[h] == -INFINITY) ? 0.f : fast_exp2(mh[h] - m_run);
+      lph[h] = ph_lane[h] * f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pbh[h][e] = (bf16)(xh[h][e] * f);
+    };
+    auto commit_half = [&](int h) __attribute__((always_inline)) {
       if (mh[h] > m_run + TAU) {
         const float alpha = fast_exp2(m_run - mh[h]);
         l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < DBLK; ++db) oacc[db] *= alpha;
         m_run = mh[h];
+        prepare_half(h);
       }
-      const float f = (mh[h] == -INFINITY) ? 0.f : fast_exp2(mh[h] - m_run);
-      l_run += ph_lane[h] * f;
-      bf16x8 pb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = (bf16)(xh[h][e] * f);
-      return pb;
+      l_run += lph[h];
     };
 
     f32x4 s[4] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f},
@@ -415,6 +422,10 @@ void attn_bf16_kernel(AttnArgs a) {
         }
       } else {
         soft_piece(0, gi, s);
+        if (gi == NG - 1) {
+          prepare_half(0);
+          commit_half(0);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -424,14 +435,13 @@ void attn_bf16_kernel(AttnArgs a) {
     bf16x8 va[PG], vb2[PG];
 #pragma unroll
     for (int u = 0; u < PG; ++u) va[u] = vfrag(0, u);
-    bf16x8 pb0 = finish_half(0);
-    bf16x8 pb1;
+
 #pragma unroll
     for (int n = 0; n < 2 * NGRP; ++n) {
       const int kk = n / NGRP, gi = n % NGRP;
       bf16x8* vc = (n & 1) ? vb2 : va;
       bf16x8* vn = (n & 1) ? va : vb2;
-      if (n == NGRP) pb1 = finish_half(1);
+      if (n == NGRP) commit_half(1);
       wait_lds();
       if (n + 1 < 2 * NGRP) {
         const int kk1 = (n + 1) / NGRP, g1 = (n + 1) % NGRP;
@@ -442,12 +452,13 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int u = 0; u < PG; ++u) {
         const int db = gi * PG + u;
-        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vc[u], kk ? pb1 : pb0, oacc[db], 0, 0, 0);
+        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vc[u], pbh[kk], oacc[db], 0, 0, 0);
       }
       if (kk == 0) {
         // softmax of half 1 in the shadow of the half-0 PV MFMAs
         for (int piece = (9 * gi) / NGRP; piece < (9 * (gi + 1)) / NGRP; ++piece)
           soft_piece(1, piece, s);
+        if (gi == NGRP - 1) prepare_half(1);
       } else if (OP == kScore && gi == 0) {
         // block log-sum-exp over both halves, then max over the wave's heads
         const float M = fmaxf(mh[0], mh[1]);
