@@ -32,9 +32,16 @@
 // LDS tile layout: 9 groups of 64 columns; group G holds, for each key k, the
 //   128 B of columns 64G .. 64G+63 at [G * 8192 + k * 128]. Inside those
 //   128 B, 16-byte chunk c8 (8 columns) sits in slot c8 ^ sw(k), with
-//   sw(k) = 2 * ((k >> 1) & 3) + ((k >> 3) & 1). The swizzle makes the 16
-//   keys of a score-fragment read, and the 8 keys x 2 chunks of a
-//   transpose-read half-wave, land on distinct banks. Tiles are filled with
+//   sw(k) = 2 * ((k >> 1) & 3) + ((k >> 3) & 1). Transpose reads are
+//   bank-conflict free under it; the score-fragment ds_read_b128 reads
+//   conflict 2-way (lanes {0-7, 32-39}, {8-15, 40-47}, ... share a cycle), so
+//   they run at about half the LDS rate. Swizzles free of conflicts for both
+//   reads exist (e.g. 3 * bit2 + 4 * bit1) and are faster when no tile copy
+//   runs, but with the copy in flight they are slower end to end: the LDS DMA
+//   returns then find fewer free LDS cycles and hold up the next tile. Moving
+//   the copy elsewhere in the tile, or staging it through registers, costs
+//   more than the conflicts do.
+//   Tiles are filled with
 //   global_load_lds_dwordx4 (lane l of a wave instruction writes 16 B at base
 //   + 16 l): one instruction covers 8 keys x one full 128 B line each.
 //
@@ -117,6 +124,9 @@ __device__ __forceinline__ float max_row16(float v) {
   return v;
 }
 
+// Chunk swizzle of key k inside a tile row (depends on bits 1 to 3 only).
+__device__ __forceinline__ int swz(int k) { return 2 * ((k >> 1) & 3) + ((k >> 3) & 1); }
+
 // Wait for outstanding LDS reads only (lgkmcnt(0); vmcnt and expcnt left at
 // their maxima so in-flight tile copies keep running).
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
@@ -125,12 +135,13 @@ __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F);
 // Instruction n = (G, kq) = (n / 8, n % 8) fills keys 8kq .. 8kq+7 of column
 // group G; lane l takes key 8kq + l/8 and stores slot l%8, i.e. chunk
 // (l%8) ^ sw(key). Wave w issues n = w + 4i, so kq alternates between w and
-// w + 4 and G = i / 2: two source rows per lane, immediate offsets otherwise.
+// w + 4 (same key bit 3) and G = i / 2: two source rows per lane, immediate
+// offsets otherwise.
 __device__ __forceinline__ void stage_tile(char* buf, const bf16* kv_entry, const Blk& blk,
                                            int wave_u, int lane) {
   using namespace mla;
   const int kl = lane >> 3;                                    // key inside the octet
-  const int c8 = (lane & 7) ^ (2 * ((lane >> 4) & 3) + (wave_u & 1));
+  const int c8 = (lane & 7) ^ swz(8 * wave_u + kl);
   const int ka = min(8 * wave_u + kl, blk.len - 1);           // kq = w
   const int kb = min(8 * (wave_u + 4) + kl, blk.len - 1);     // kq = w + 4
   const char* src_a = (const char*)(kv_entry + (size_t)(blk.start + ka) * DK) + 16 * c8;
@@ -239,18 +250,18 @@ void attn_bf16_kernel(AttnArgs a) {
   // Per-lane LDS bases of the score fragments: key 16kb + l16, chunk 4ks +
   // grp (group ks/2, chunk-in-group 4 (ks & 1) + grp) in slot c8 ^ sw(key),
   // where sw depends only on l16 here.
-  const int swk = 2 * ((l16 >> 1) & 3) + ((l16 >> 3) & 1);
+  const int swk = swz(l16);
   const int koff_e = l16 * 128 + 16 * (grp ^ swk);
   const int koff_o = l16 * 128 + 16 * ((4 + grp) ^ swk);
   // Transpose reads: lane i of group grp reads key 32kk (+16) + 4grp + i/4,
   // chunk 2db + ((i >> 1) & 1), byte 8 (i & 1); one base per db & 3.
   const int kloc = 4 * grp + (l16 >> 2);
-  const int swv = 2 * ((kloc >> 1) & 3) + ((kloc >> 3) & 1);
+  const int swv = swz(kloc);
   const int tv = ((l16 >> 1) & 1) ^ swv;
   const int voff = kloc * 128 + 8 * (l16 & 1);
   // Tile copy: lane l of instruction (G, kq) takes key 8kq + l/8 and stores
   // chunk (l%8) ^ sw(key) in slot l%8; wave w issues kq = w and w + 4.
-  const int cp_c8 = (lane & 7) ^ (2 * ((lane >> 4) & 3) + (wave & 1));
+  const int cp_c8 = (lane & 7) ^ swz(8 * wave + (lane >> 3));
 
   // One tile, processed as two 32-key halves so that in-order issue can
   // overlap VALU with MFMA: the softmax of half 0 runs between the score
@@ -413,15 +424,21 @@ void attn_bf16_kernel(AttnArgs a) {
           s[2 * h + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fc[2 * u + k], qreg[gi * SG + u],
                                                                  s[2 * h + k], 0, 0, 0);
       if (h == 0) {
+        // copy column groups G of the next tile in the shadow of these MFMAs
         if (has_next) {
-          __builtin_amdgcn_global_load_lds((const HS_GLB void*)(cp_a + 128 * gi),
-                                           (HS_LDS void*)(cp_dst + gi * GR_BYTES), 16, 0, 0);
-          __builtin_amdgcn_global_load_lds((const HS_GLB void*)(cp_b + 128 * gi),
-                                           (HS_LDS void*)(cp_dst + gi * GR_BYTES + 4096), 16, 0,
-                                           0);
+#pragma unroll
+          for (int G = (NGR * gi) / NG; G < (NGR * (gi + 1)) / NG; ++G) {
+            __builtin_amdgcn_global_load_lds((const HS_GLB void*)(cp_a + 128 * G),
+                                             (HS_LDS void*)(cp_dst + G * GR_BYTES), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const HS_GLB void*)(cp_b + 128 * G),
+                                             (HS_LDS void*)(cp_dst + G * GR_BYTES + 4096), 16,
+                                             0, 0);
+          }
         }
       } else {
-        soft_piece(0, gi, s);
+#pragma unroll
+        for (int piece = (9 * gi) / NG; piece < (9 * (gi + 1)) / NG; ++piece)
+          soft_piece(0, piece, s);
         if (gi == NG - 1) {
           prepare_half(0);
           commit_half(0);
