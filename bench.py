@@ -140,6 +140,276 @@ class Timer:
         return a, b
 
 
+# ---------------------------------------------------------------------------
+# --suite: every named workload, every kernel, warm and cold, against the
+# vendor peaks and the attainable peaks measured by the probe kernels.
+# ---------------------------------------------------------------------------
+
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector (the fp32 shapes use FMAs, no MFMA)
+
+
+def host_blocks(p):
+    """Per batch entry: valid length L_b, document bounds and block table
+    (start, end) in the numbering of block_logit (blocks restart at every
+    document start). Host arithmetic for work counting only."""
+    out = []
+    for b in range(p.B):
+        L = p.kv_lens[b] if p.kv_lens else p.Skv
+        docs = list(zip(p.doc_start, p.doc_end)) if p.doc_start else [(0, L)]
+        blocks = []
+        for s0, e0 in docs:
+            for st in range(s0, e0, p.block_size):
+                blocks.append((st, min(st + p.block_size, e0)))
+        out.append((L, docs, blocks))
+    return out
+
+
+def row_key_counts(p, idx_cpu=None):
+    """Per (batch, row): allowed keys of causal attention, of the window, of
+    the gather over the selected blocks (when indices are given), and the
+    distinct KV rows each operation touches per batch entry."""
+    causal, window, gather = [], [], []
+    kv_rows = {"score": 0, "swa": 0}
+    for b, (L, docs, blocks) in enumerate(host_blocks(p)):
+        pos = np.arange(L - p.Sq, L)
+        lo = np.zeros_like(pos)
+        for s0, e0 in docs:
+            m = (pos >= s0) & (pos < e0)
+            lo[m] = s0
+        causal.append(pos - lo + 1)
+        wlo = np.maximum(lo, pos - p.window + 1)
+        window.append(pos - wlo + 1)
+        kv_rows["score"] += int(pos.max() + 1 - lo.min())
+        kv_rows["swa"] += int(pos.max() + 1 - wlo.min())
+        if idx_cpu is not None:
+            st = np.array([x[0] for x in blocks]); en = np.array([x[1] for x in blocks])
+            g = np.zeros(p.Sq, dtype=np.int64)
+            for k in range(idx_cpu.shape[-1]):
+                j = idx_cpu[b, :, k].astype(np.int64)
+                ok = (j >= 0) & (j < len(blocks))
+                jj = np.where(ok, j, 0)
+                a = np.maximum(st[jj], lo); e = np.minimum(en[jj] - 1, pos)
+                g += np.where(ok, np.clip(e - a + 1, 0, None), 0)
+            gather.append(g)
+    cat = lambda x: np.concatenate(x) if x else None
+    return cat(causal), cat(window), cat(gather), kv_rows
+
+
+def median_time(fn, stream, n=20, warm=3, before=None):
+    """Median launch time (ms) of fn() over n launches after `warm` warm-ups,
+    each bracketed by HIP events on `stream`; before() runs untimed first."""
+    for _ in range(warm):
+        fn()
+    ts = []
+    for _ in range(n):
+        if before is not None:
+            before()
+        a = torch.cuda.Event(enable_timing=True); b = torch.cuda.Event(enable_timing=True)
+        a.record(stream); fn(); b.record(stream)
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
+    return float(np.median(ts))
+
+
+def measure_peaks(dev, stream):
+    from block_sparse_mqa_amd import probe
+    wg, iters = 2048, 10000
+    out = torch.empty(wg * 256, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(2, dtype=torch.int64, device=dev)
+    t = median_time(lambda: probe.hs_probe_mfma_bf16(wg, iters, out, clocks, stream), stream,
+                    n=10, warm=2)
+    mfma = probe.hs_probe_mfma_flops(wg, iters) / (t * 1e-3) / 1e12
+    cyc, ticks = (int(x) for x in clocks.cpu())
+    sclk_ghz = cyc / (ticks / 1e8) / 1e9 if ticks > 0 else None
+    nbytes = 2 << 30
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    t = median_time(lambda: probe.hs_probe_copy(src, dst, nbytes, stream), stream, n=10, warm=2)
+    copy = 2 * nbytes / (t * 1e-3) / 1e9
+    del src, dst
+    return {"mfma_bf16_tflop_s": round(mfma, 1), "copy_gb_s": round(copy, 1),
+            "shader_clock_ghz_under_mfma": None if sclk_ghz is None else round(sclk_ghz, 3),
+            "mfma_probe": f"{wg} workgroups x 4 waves x {iters} x 4 chains of v_mfma_f32_32x32x16_bf16",
+            "copy_probe": f"{nbytes >> 30} GiB read + {nbytes >> 30} GiB written, 16 B per lane, nontemporal"}
+
+
+def oracle_time(p, budget_s, seed=0, threads=None):
+    """Oracle (block scores, top-k, gather; float64) on the workload's rows:
+    all of them when they fit in `budget_s`, else a uniform sample, with the
+    full-run time extrapolated by causal pairs (labelled)."""
+    import contextlib
+    from oracle import hysparse_ref as ref
+    kw = dict(block_size=p.block_size, kv_lens=p.kv_lens, doc_start=p.doc_start, doc_end=p.doc_end)
+    limit = contextlib.nullcontext()
+    if threads is not None:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(threads)
+    causal, _, _, _ = row_key_counts(p)
+    per_row = causal.reshape(p.B, p.Sq).sum(axis=0)       # pairs per row index, all batch entries
+    rng = np.random.default_rng(seed)
+    order = rng.permutation(p.Sq)
+    kv64 = p.kv.to(torch.float64).numpy()
+    done, spent, pairs = 0, 0.0, 0
+    with limit:
+        for r in order:
+            if spent >= budget_s:
+                break
+            t0 = time.perf_counter()
+            rows = [int(r)]
+            _, _, bl = ref.block_score(p.q, kv64, p.sink, p.Dv, p.scale, rows=rows, **kw)
+            own = ref.own_blocks(p.B, p.Sq, p.Skv, p.block_size, p.kv_lens, p.doc_start, p.doc_end,
+                                 rows=rows)
+            sel = ref.topk_blocks(bl, own, p.top_k)
+            idx = np.full((p.B, p.Sq, p.top_k), -1, dtype=np.int64)
+            idx[:, r] = sel[:, 0]
+            ref.sparse_gather(p.q, kv64, p.sink, p.Dv, p.scale, idx, rows=rows, **kw)
+            spent += time.perf_counter() - t0
+            done += 1
+            pairs += int(per_row[r])
+    full = done == p.Sq
+    est_full_s = spent if full else spent * float(per_row.sum()) / max(pairs, 1)
+    return {"tokens_s": round(done * p.B / spent, 3), "rows": done * p.B, "seconds": round(spent, 2),
+            "full": full, "full_run_s": round(est_full_s, 1),
+            "full_run_s_is": "measured" if full else "extrapolated by causal pairs from the sample",
+            "threads": threads if threads is not None else blas_threads()}
+
+
+def suite_config(c, dev, stream, peaks, oracle_budget):
+    p = inputs.config(c)
+    q, kv, sink = p.q.to(dev), p.kv.to(dev), p.sink.to(dev)
+    prob = hs.Problem(p.B, p.Sq, p.Skv, p.H, p.Dk, p.Dv, block_size=p.block_size, scale=p.scale,
+                      dtype=p.dtype, kv_lens=p.kv_lens, doc_start=p.doc_start, doc_end=p.doc_end)
+    NB = hs.hs_num_blocks(prob)
+    tdt = p.torch_dtype
+    out = torch.empty((p.B, p.Sq, p.H, p.Dv), dtype=tdt, device=dev)
+    lse = torch.empty((p.B, p.Sq, p.H), dtype=torch.float32, device=dev)
+    bl = torch.empty((p.B, p.Sq, NB), dtype=torch.float32, device=dev)
+    idx = torch.empty((p.B, p.Sq, p.top_k), dtype=torch.int32, device=dev)
+
+    def ws(op, **k):
+        n = hs.hs_workspace_size(prob, op, **k)
+        return torch.empty((n + 3) // 4, dtype=torch.float32, device=dev) if n else None
+
+    w1, w3, w4 = ws(hs.HS_OP_BLOCK_SCORE), ws(hs.HS_OP_SPARSE_GATHER, top_k=p.top_k), \
+        ws(hs.HS_OP_SWA, window=p.window)
+    calls = {
+        "block_score": lambda: hs.hs_block_score_fwd(prob, q, kv, sink, out, lse, bl, w1, stream),
+        "topk": lambda: hs.hs_topk_blocks(prob, bl, p.top_k, idx, stream),
+        "sparse_gather": lambda: hs.hs_sparse_gather_fwd(prob, q, kv, sink, idx, p.top_k, out, lse,
+                                                         w3, stream),
+        "swa": lambda: hs.hs_swa_fwd(prob, q, kv, sink, p.window, out, lse, w4, stream),
+    }
+    calls["block_score"](); calls["topk"](); torch.cuda.synchronize()
+    idx_cpu = idx.cpu().numpy()
+    causal, window, gather, kv_rows = row_key_counts(p, idx_cpu)
+    fpp, H, es = 2 * p.Dk + 2 * p.Dv, p.H, (2 if p.dtype == "bf16" else 4)
+    qb, ob, lb = p.B * p.Sq * H * p.Dk * es, p.B * p.Sq * H * p.Dv * es, p.B * p.Sq * H * 4
+    work = {
+        "block_score": (int(causal.sum()) * H * fpp,
+                        qb + kv_rows["score"] * p.Dk * es + ob + lb + p.B * p.Sq * NB * 4),
+        "topk": (0, p.B * p.Sq * (NB + p.top_k) * 4),
+        "sparse_gather": (int(gather.sum()) * H * fpp,
+                          qb + ob + lb + p.B * p.Sq * p.top_k * 4 + int(gather.sum()) * p.Dk * es),
+        "swa": (int(window.sum()) * H * fpp, qb + kv_rows["swa"] * p.Dk * es + ob + lb),
+    }
+    peak_f = PEAK_BF16_TFLOPS if p.dtype == "bf16" else PEAK_F32_TFLOPS
+    meas_f = peaks["mfma_bf16_tflop_s"] if p.dtype == "bf16" else None
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    rows = {}
+    for k, fn in calls.items():
+        if k == "sparse_gather":   # indices of this workload's own top-k
+            calls["topk"](); torch.cuda.synchronize()
+        warm = median_time(fn, stream)
+        cold = median_time(fn, stream, n=10, warm=1, before=lambda: scratch.fill_(0.5))
+        F, Bts = work[k]
+        t_roof = max(F / (peak_f * 1e12), Bts / (PEAK_HBM_GBS * 1e9)) * 1e3
+        t_roof_m = max(F / (meas_f * 1e12) if meas_f else 0.0,
+                       Bts / (peaks["copy_gb_s"] * 1e9)) * 1e3
+        bound = "hbm" if Bts / (PEAK_HBM_GBS * 1e9) >= F / (peak_f * 1e12) else \
+            ("mfma" if p.dtype == "bf16" else "alu")
+        rows[k] = {"ms_warm": round(warm, 4), "ms_cold": round(cold, 4),
+                   "tflop": round(F / 1e12, 4), "gb_alg": round(Bts / 1e9, 4), "bound": bound,
+                   "tflop_s": round(F / (warm * 1e-3) / 1e12, 2) if F else None,
+                   "gb_s_alg": round(Bts / (warm * 1e-3) / 1e9, 1),
+                   "frac_vendor": round(t_roof / warm, 4),
+                   "frac_measured_peak": round(t_roof_m / warm, 4) if (meas_f or bound == "hbm") else None}
+        print(f"[suite] workload {c} {k}: {rows[k]}", file=sys.stderr, flush=True)
+    del scratch
+    path_ms = rows["block_score"]["ms_warm"] + rows["topk"]["ms_warm"] + rows["sparse_gather"]["ms_warm"]
+    res = {"workload": p.name, "dtype": p.dtype, "kernels": rows,
+           "metric_path_ms": round(path_ms, 4),
+           "tokens_s": round(p.B * p.Sq / (path_ms * 1e-3), 1),
+           "metric_tflop_s": round((work["block_score"][0] + work["sparse_gather"][0]) /
+                                   (path_ms * 1e-3) / 1e12, 2)}
+    if oracle_budget > 0:
+        res["oracle"] = oracle_time(p, oracle_budget)
+        print(f"[suite] workload {c} oracle: {res['oracle']}", file=sys.stderr, flush=True)
+        if c in (1, 2):
+            res["oracle_1_thread"] = oracle_time(p, min(oracle_budget, 20.0), threads=1)
+    return res
+
+
+def run_suite(args):
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    peaks = measure_peaks(dev, stream)
+    print(json.dumps({"suite": "peaks", **peaks}), flush=True)
+    results = []
+    for c in args.suite_workloads:
+        r = suite_config(c, dev, stream, peaks, args.oracle_budget)
+        results.append(r)
+        print(json.dumps({"suite": "workload", **r}), flush=True)
+        torch.cuda.empty_cache()
+    if args.suite_md:
+        write_suite_md(args.suite_md, peaks, results, args)
+
+
+def write_suite_md(path, peaks, results, args):
+    L = ["# Per-workload measurements (all kernels, warm and cold)\n",
+         "Command (from the repository root, on one MI355X):\n",
+         "```\npython3 bench.py --suite --suite-md " + os.path.relpath(path, ROOT) +
+         f" --oracle-budget {args.oracle_budget:g}\n```\n",
+         f"Attainable peaks measured by the probe kernels (`include/hs_probe.h`): dense bf16 MFMA "
+         f"{peaks['mfma_bf16_tflop_s']:.0f} TFLOP/s ({peaks['mfma_probe']}; shader clock while it ran: "
+         f"{peaks['shader_clock_ghz_under_mfma']} GHz by s_memtime against the 100 MHz reference); copy "
+         f"{peaks['copy_gb_s']:.0f} GB/s ({peaks['copy_probe']}). Vendor peaks: 2500 TFLOP/s bf16 "
+         "MFMA, 157.3 TFLOP/s fp32 vector, 8000 GB/s HBM.\n",
+         "Times are medians of 20 launches after 3 warm-ups (warm) and of 10 launches each after "
+         "writing a 1 GiB buffer, which evicts the 256 MB MALL and the L2 (cold). f = t_roof / t_warm "
+         "with t_roof = max(flops / peak, algorithmic bytes / bandwidth); gather bytes count each "
+         "token's selected KV rows once (shared by its 64 heads), so f can exceed 1 when KV is "
+         "served from cache.\n",
+         "| Workload | Kernel | Warm ms | Cold ms | TFLOP | Alg. GB | Bound | TFLOP/s | GB/s (alg.) | f vendor | f measured peak |",
+         "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in results:
+        for k, v in r["kernels"].items():
+            fm = "—" if v["frac_measured_peak"] is None else f"{v['frac_measured_peak']:.3f}"
+            ts = "—" if v["tflop_s"] is None else f"{v['tflop_s']:.1f}"
+            L.append(f"| {r['workload']} | {k} | {v['ms_warm']:.4f} | {v['ms_cold']:.4f} | "
+                     f"{v['tflop']:.3f} | {v['gb_alg']:.3f} | {v['bound']} | {ts} | {v['gb_s_alg']:.0f} | "
+                     f"{v['frac_vendor']:.3f} | {fm} |")
+    L.append("")
+    L.append("Metric path (block score + top-k + gather) and the float64 oracle on the host:\n")
+    L.append("| Workload | Path ms | tokens/s | TFLOP/s | Oracle tokens/s | Oracle rows | Oracle full-run s |")
+    L.append("|---|---|---|---|---|---|---|")
+    for r in results:
+        o = r.get("oracle")
+        if o:
+            ot = f"{o['tokens_s']} ({o['threads']} threads)"
+            extra = r.get("oracle_1_thread")
+            if extra:
+                ot += f"; {extra['tokens_s']} (1 thread)"
+            orow = f"{o['rows']}{'' if o['full'] else ' (sample)'}"
+            ofull = f"{o['full_run_s']} ({o['full_run_s_is']})"
+        else:
+            ot = orow = ofull = "—"
+        L.append(f"| {r['workload']} | {r['metric_path_ms']:.3f} | {r['tokens_s']:.0f} | "
+                 f"{r['metric_tflop_s']:.1f} | {ot} | {orow} | {ofull} |")
+    L.append("")
+    with open(path, "w") as f:
+        f.write("\n".join(L))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,6 +422,13 @@ def main():
                     help="after timing, run one 1 GiB device copy (counter calibration)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM traffic per launch measured by counters, if recorded")
+    ap.add_argument("--suite", action="store_true",
+                    help="measure every named workload and kernel (warm, cold, rooflines) instead "
+                         "of the metric line")
+    ap.add_argument("--suite-workloads", type=int, nargs="+", default=[1, 2, 3, 4, 5])
+    ap.add_argument("--suite-md", default=None, help="also write the suite as a markdown table")
+    ap.add_argument("--oracle-budget", type=float, default=20.0,
+                    help="seconds of oracle time per workload in the suite (0 = skip)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -161,6 +438,10 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+
+    if args.suite:
+        run_suite(args)
+        return
 
     p = inputs.config(args.workload)
     dev = torch.device("cuda:0")

@@ -14,12 +14,16 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libhysparse.so")
+# Roofline probes (dense MFMA loop, copy): a separate library, not the method's ABI.
+PROBE_LIB = os.path.join(HERE, "libhsprobe.so")
+PROBE_SOURCES = ["hs_probe.hip"]
 OBJDIR = os.path.join(HERE, "_build")
 SOURCES = ["hs_abi.hip", "hs_attn_bf16.hip", "hs_attn_f32.hip", "hs_topk.hip"]
 # Per-source extra flags. The bf16 engine keeps its MFMA accumulators in
 # VGPRs so that the O rescale and epilogue need no AGPR<->VGPR copies; Q and
 # other long-lived operands then go to AGPRs, which MFMA reads directly.
-EXTRA = {"hs_attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"hs_attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "hs_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed-FP32 instructions are kept out of every kernel (plain fp32 code only).
@@ -38,18 +42,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"link of {os.path.basename(lib)} failed:\n{r.stderr}")
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJDIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=min(5, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

@@ -110,3 +110,20 @@ def test_workspace_only_for_split_decode():
         assert n > 0 and n % (32 * 64 * 4) == 0
     assert hs.hs_workspace_size(_mla(dtype="f32", H=8, Dk=96, Dv=64, B=2, Sq=1, Skv=512,
                                      kv_lens=[512, 3]), hs.HS_OP_BLOCK_SCORE) == 0
+
+
+def test_probe_library_exports_every_declared_symbol():
+    from block_sparse_mqa_amd import probe
+    with open(os.path.join(ROOT, "include", "hs_probe.h")) as f:
+        src = f.read()
+    names = set(re.findall(r"^\s*[a-z_0-9]+\s+(hs_probe_[a-z_0-9]+)\s*\(", src, flags=re.M))
+    assert names == set(probe.EXPORTS), names
+    lib = probe.load_probe_library()
+    for n in names:
+        assert hasattr(lib, n), n
+    # host-only arithmetic and host-side argument checks (no launch happens)
+    assert lib.hs_probe_mfma_flops(2, 3) == 2 * 4 * 3 * 4 * 32 * 32 * 16 * 2
+    assert lib.hs_probe_mfma_bf16(0, 1, ctypes.c_void_p(256), None, None) == -1
+    assert lib.hs_probe_mfma_bf16(1, 1, ctypes.c_void_p(256), ctypes.c_void_p(260), None) == -1
+    assert lib.hs_probe_copy(ctypes.c_void_p(256), ctypes.c_void_p(4096), 15, None) == -1
+    assert lib.hs_probe_copy(ctypes.c_void_p(256), ctypes.c_void_p(272), 64, None) == -1  # overlap
