@@ -10,6 +10,7 @@
 // silently ignoring a document mask).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -129,19 +130,41 @@ hs_status prepare(const hs_problem* p, hs::Geom& g) {
   return HS_OK;
 }
 
-// Number of key-range splits for single-token rows (decode): enough
-// workgroups to fill the chip, each split owning at least 4 tiles.
-int choose_nsplit(const hs::Geom& g, int op, int top_k, int window) {
-  if (g.Dk != 576) return 1;
+// Key-range split for few rows (decode): rows are cut into chunks of the same
+// number of tiles, sized so that about 512 workgroups have work (two per CU),
+// with at least 4 tiles per chunk and at most 64 chunks per row. Long rows get
+// more chunks than short ones; chunks past the end of a row are empty and
+// their workgroups exit at once. The gather's tile count is data dependent,
+// so top_k stands in for it.
+struct SplitPlan {
+  int nsplit, tiles;
+};
+
+SplitPlan plan_split(const hs::Geom& g, int op, int top_k, int window) {
+  SplitPlan sp{1, 0};
+  if (g.Dk != 576) return sp;
   const int items = g.B * g.Sq;
-  if (items >= 512) return 1;
-  int max_tiles;
-  if (op == HS_OP_SPARSE_GATHER) max_tiles = top_k;
-  else if (op == HS_OP_SWA) max_tiles = std::min(g.NB, (window + g.BS - 1) / g.BS + 1);
-  else max_tiles = g.NB;
-  int ns = (1024 + items - 1) / items;
-  ns = std::min(ns, std::max(1, max_tiles / 4));
-  return std::max(1, std::min(ns, 64));
+  if (items >= 512) return sp;
+  long total = 0;
+  int longest = 1;
+  for (int b = 0; b < g.B; ++b)
+    for (int r = 0; r < g.Sq; ++r) {
+      int n;
+      if (op == HS_OP_SPARSE_GATHER) {
+        n = top_k;
+      } else {
+        const hs::RowRange rr = hs::row_range(g, op == HS_OP_SWA ? hs::kSwa : hs::kScore, b, r,
+                                              window);
+        n = rr.j_last - rr.j_first + 1;
+      }
+      total += n;
+      longest = std::max(longest, n);
+    }
+  int tiles = (int)std::max<long>(4, (total + 511) / 512);
+  tiles = std::max(tiles, (longest + 63) / 64);
+  const int ns = (longest + tiles - 1) / tiles;
+  if (ns > 1) sp = SplitPlan{ns, tiles};
+  return sp;
 }
 
 size_t split_ws_bytes(const hs::Geom& g, int nsplit) {
@@ -186,7 +209,8 @@ hs_status launch_attn(int op, const hs_problem* p, const void* q, const void* kv
   if (g.Sq * g.B == 0) return HS_OK;
 
   if (p->dtype == HS_BF16) {
-    const int nsplit = choose_nsplit(g, op, top_k, window);
+    const SplitPlan sp = plan_split(g, op, top_k, window);
+    const int nsplit = sp.nsplit;
     const size_t need = split_ws_bytes(g, nsplit);
     if (need > 0 && (!ws || ws_bytes < need))
       return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
@@ -205,6 +229,7 @@ hs_status launch_attn(int op, const hs_problem* p, const void* q, const void* kv
     a.top_k = top_k;
     a.window = window;
     a.nsplit = nsplit;
+    a.split_tiles = sp.tiles;
     if (nsplit > 1) {
       const size_t slots = (size_t)g.B * g.Sq * nsplit * g.H;
       a.ws_o = static_cast<float*>(ws);
@@ -260,7 +285,7 @@ hs_status hs_workspace_size(const hs_problem* p, int32_t op, int32_t top_k, int3
   if (st != HS_OK) return st;
   if (!bytes) return fail(HS_ERR_INVALID_ARG, "bytes is NULL");
   if (op < HS_OP_BLOCK_SCORE || op > HS_OP_SWA) return fail(HS_ERR_INVALID_ARG, "unknown op %d", op);
-  *bytes = p->dtype == HS_BF16 ? split_ws_bytes(g, choose_nsplit(g, op, top_k, window)) : 0;
+  *bytes = p->dtype == HS_BF16 ? split_ws_bytes(g, plan_split(g, op, top_k, window).nsplit) : 0;
   return HS_OK;
 }
 

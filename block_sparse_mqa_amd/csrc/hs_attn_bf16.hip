@@ -212,9 +212,17 @@ void attn_bf16_kernel(AttnArgs a) {
   }
   int t_begin = 0, t_end = ntiles;
   if (SPLIT) {
-    const int per = (ntiles + a.nsplit - 1) / a.nsplit;
-    t_begin = min(ntiles, split * per);
-    t_end = min(ntiles, t_begin + per);
+    t_begin = min(ntiles, split * a.split_tiles);
+    t_end = min(ntiles, t_begin + a.split_tiles);
+    if (split > 0 && t_begin == t_end) {
+      // chunk past the end of this row: an empty partial, skipped by the merge
+      if (lane < RW) {
+        const size_t slot = (size_t)w * a.nsplit + split;
+        a.ws_ml[(slot * H + wave * RW + lane) * 2 + 0] = -INFINITY;
+        a.ws_ml[(slot * H + wave * RW + lane) * 2 + 1] = 0.f;
+      }
+      return;
+    }
   }
   auto tile_block = [&](int t) -> int { return OP == kGather ? tile_list[t] : rr.j_first + t; };
 

@@ -39,7 +39,7 @@ struct Blk {
 };
 
 // Document holding position p of entry b.
-__device__ __forceinline__ Doc doc_of_pos(const Geom& g, int b, int p) {
+__host__ __device__ inline Doc doc_of_pos(const Geom& g, int b, int p) {
   if (g.n_docs == 0) return Doc{0, g.kv_len[b], 0};
   int lo = 0, hi = g.n_docs - 1;
   while (lo < hi) {
@@ -71,7 +71,7 @@ __device__ __forceinline__ Blk block_rows(const Geom& g, int b, int j) {
 }
 
 // Global block id of position p inside document d.
-__device__ __forceinline__ int block_of_pos(const Geom& g, const Doc& d, int p) {
+__host__ __device__ inline int block_of_pos(const Geom& g, const Doc& d, int p) {
   return d.blk0 + (p - d.start) / g.BS;
 }
 
@@ -83,13 +83,13 @@ struct RowRange {
   int pos, lo, hi, j_first, j_last;
 };
 
-__device__ __forceinline__ RowRange row_range(const Geom& g, int op, int b, int r, int window) {
+__host__ __device__ inline RowRange row_range(const Geom& g, int op, int b, int r, int window) {
   RowRange rr;
   rr.pos = g.kv_len[b] - g.Sq + r;
   Doc d = doc_of_pos(g, b, rr.pos);
   rr.lo = d.start;
   rr.hi = rr.pos;
-  if (op == kSwa) rr.lo = max(rr.lo, rr.pos - window + 1);
+  if (op == kSwa && rr.pos - window + 1 > rr.lo) rr.lo = rr.pos - window + 1;
   rr.j_first = block_of_pos(g, d, rr.lo);
   rr.j_last = block_of_pos(g, d, rr.hi);
   return rr;

@@ -20,6 +20,7 @@ struct AttnArgs {
   int top_k;
   int window;
   int nsplit;                // > 1: split key range, partials merged after
+  int split_tiles;           // tiles per split: split s covers [s, s+1) * split_tiles
   float* ws_o;               // [items * nsplit, H, Dv] fp32 partial O
   float* ws_ml;              // [items * nsplit, H, 2] fp32 (max, denominator)
   Geom g;
