@@ -40,6 +40,7 @@ class HsProblem(ctypes.Structure):
         ("kv_lens", ctypes.POINTER(ctypes.c_int32)), ("n_kv_lens", ctypes.c_int32),
         ("doc_start", ctypes.POINTER(ctypes.c_int32)),
         ("doc_end", ctypes.POINTER(ctypes.c_int32)), ("n_docs", ctypes.c_int32),
+        ("page_table", ctypes.c_void_p), ("max_pages", ctypes.c_int32),
     ]
 
 
@@ -96,8 +97,16 @@ class Problem:
                  block_size: int = 64, scale: float = 0.0, dtype: str = "bf16",
                  kv_lens: Optional[Sequence[int]] = None,
                  doc_start: Optional[Sequence[int]] = None,
-                 doc_end: Optional[Sequence[int]] = None):
+                 doc_end: Optional[Sequence[int]] = None,
+                 page_table=None):
+        """page_table: optional int32 device tensor [B, max_pages] (paged KV: kv is
+        then a pool [n_pages, block_size, Dk]); the tensor must outlive the calls."""
         self.B, self.Sq, self.Skv, self.H, self.Dk, self.Dv = B, Sq, Skv, H, Dk, Dv
+        self.page_table = page_table
+        if page_table is not None:
+            _dev("page_table", page_table)
+            if page_table.dim() != 2 or page_table.shape[0] != B:
+                raise ValueError("page_table must be [B, max_pages]")
         self.dtype = dtype
         self._kv = (ctypes.c_int32 * len(kv_lens))(*kv_lens) if kv_lens is not None else None
         self._ds = (ctypes.c_int32 * len(doc_start))(*doc_start) if doc_start is not None else None
@@ -110,7 +119,9 @@ class Problem:
             n_kv_lens=len(kv_lens) if kv_lens is not None else 0,
             doc_start=ctypes.cast(self._ds, ctypes.POINTER(ctypes.c_int32)) if self._ds else None,
             doc_end=ctypes.cast(self._de, ctypes.POINTER(ctypes.c_int32)) if self._de else None,
-            n_docs=len(doc_start) if doc_start is not None else 0)
+            n_docs=len(doc_start) if doc_start is not None else 0,
+            page_table=None if page_table is None else page_table.data_ptr(),
+            max_pages=0 if page_table is None else int(page_table.shape[1]))
 
     @property
     def ref(self):

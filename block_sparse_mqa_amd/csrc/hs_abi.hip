@@ -127,6 +127,19 @@ hs_status prepare(const hs_problem* p, hs::Geom& g) {
     for (int b = 0; b < p->batch; ++b) nb = std::max(nb, (g.kv_len[b] + g.BS - 1) / g.BS);
     g.NB = nb;
   }
+
+  if (p->page_table || p->max_pages != 0) {
+    if (!p->page_table || p->max_pages < 1)
+      return fail(HS_ERR_INVALID_ARG, "paged KV needs page_table and max_pages >= 1");
+    if (reinterpret_cast<uintptr_t>(p->page_table) % 4 != 0)
+      return fail(HS_ERR_INVALID_ARG, "page_table is not 4-byte aligned");
+    if (p->dtype != HS_BF16) return fail(HS_ERR_UNSUPPORTED, "paged KV is built for bf16 only");
+    if (g.n_docs != 0) return fail(HS_ERR_INVALID_ARG, "paged KV does not take documents");
+    for (int b = 0; b < p->batch; ++b)
+      if (g.kv_len[b] > p->max_pages * g.BS)
+        return fail(HS_ERR_INVALID_ARG, "entry %d holds %d keys, more than max_pages * %d", b,
+                    g.kv_len[b], g.BS);
+  }
   return HS_OK;
 }
 
@@ -235,6 +248,8 @@ hs_status launch_attn(int op, const hs_problem* p, const void* q, const void* kv
       a.ws_o = static_cast<float*>(ws);
       a.ws_ml = static_cast<float*>(ws) + slots * g.Dv;
     }
+    a.page_table = p->page_table;
+    a.max_pages = p->page_table ? p->max_pages : 0;
     a.g = g;
     return hip_status(hs::attn_bf16_launch(op, a, s), "attention launch");
   }
@@ -257,7 +272,7 @@ hs_status launch_attn(int op, const hs_problem* p, const void* q, const void* kv
 
 extern "C" {
 
-int32_t hs_version(void) { return 100; }
+int32_t hs_version(void) { return 101; }
 
 const char* hs_status_string(int32_t status) {
   switch (status) {

@@ -131,21 +131,22 @@ __device__ __forceinline__ int swz(int k) { return 2 * ((k >> 1) & 3) + ((k >> 3
 // their maxima so in-flight tile copies keep running).
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// Copy one 64-key tile (rows [start, start+len), clamped) into an LDS buffer.
+// Copy one 64-key tile (KV rows base + start .. + len - 1, clamped) into an
+// LDS buffer.
 // Instruction n = (G, kq) = (n / 8, n % 8) fills keys 8kq .. 8kq+7 of column
 // group G; lane l takes key 8kq + l/8 and stores slot l%8, i.e. chunk
 // (l%8) ^ sw(key). Wave w issues n = w + 4i, so kq alternates between w and
 // w + 4 (same key bit 3) and G = i / 2: two source rows per lane, immediate
 // offsets otherwise.
-__device__ __forceinline__ void stage_tile(char* buf, const bf16* kv_entry, const Blk& blk,
+__device__ __forceinline__ void stage_tile(char* buf, const bf16* base, int start, int len,
                                            int wave_u, int lane) {
   using namespace mla;
   const int kl = lane >> 3;                                    // key inside the octet
   const int c8 = (lane & 7) ^ swz(8 * wave_u + kl);
-  const int ka = min(8 * wave_u + kl, blk.len - 1);           // kq = w
-  const int kb = min(8 * (wave_u + 4) + kl, blk.len - 1);     // kq = w + 4
-  const char* src_a = (const char*)(kv_entry + (size_t)(blk.start + ka) * DK) + 16 * c8;
-  const char* src_b = (const char*)(kv_entry + (size_t)(blk.start + kb) * DK) + 16 * c8;
+  const int ka = min(8 * wave_u + kl, len - 1);               // kq = w
+  const int kb = min(8 * (wave_u + 4) + kl, len - 1);         // kq = w + 4
+  const char* src_a = (const char*)(base + (size_t)(start + ka) * DK) + 16 * c8;
+  const char* src_b = (const char*)(base + (size_t)(start + kb) * DK) + 16 * c8;
   char* dst = buf + wave_u * 1024;
 #pragma unroll
   for (int G = 0; G < NGR; ++G) {
@@ -156,7 +157,7 @@ __device__ __forceinline__ void stage_tile(char* buf, const bf16* kv_entry, cons
   }
 }
 
-template <int OP, bool SPLIT>
+template <int OP, bool SPLIT, bool PAGED>
 __global__ __launch_bounds__(mla::NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_bf16_kernel(AttnArgs a) {
   using namespace mla;
@@ -234,7 +235,17 @@ void attn_bf16_kernel(AttnArgs a) {
   }
 
   const bf16* kv_entry = a.kv + (size_t)b * g.Skv * DK;
-  if (t_begin < t_end) stage_tile(buf_a, kv_entry, block_rows(g, b, tile_block(t_begin)), wave, lane);
+  // Key block j's rows are base + start .. : the entry's rows in place, or row 0
+  // onwards of the block's page in the pool.
+  auto block_base = [&](int j) -> const bf16* {
+    if (PAGED) return a.kv + (size_t)a.page_table[(size_t)b * a.max_pages + j] * (BS * DK);
+    return kv_entry;
+  };
+  if (t_begin < t_end) {
+    const int j0 = tile_block(t_begin);
+    const Blk b0 = block_rows(g, b, j0);
+    stage_tile(buf_a, block_base(j0), PAGED ? 0 : b0.start, b0.len, wave, lane);
+  }
 
   // Q rows of this wave as MFMA B operands: lane holds q[row, head, 32ks + 8grp .. +8].
   bf16x8 qreg[KSTEPS];
@@ -294,11 +305,14 @@ void attn_bf16_kernel(AttnArgs a) {
     const char* cp_b = nullptr;
     char* cp_dst = nxt + wave * 1024;
     if (has_next) {
-      const Blk nb = block_rows(g, b, tile_block(t + 1));
+      const int jn = tile_block(t + 1);
+      const Blk nb = block_rows(g, b, jn);
+      const bf16* base = block_base(jn);
+      const int st = PAGED ? 0 : nb.start;
       const int ka = min(8 * wave + (lane >> 3), nb.len - 1);
       const int kb2 = min(8 * (wave + 4) + (lane >> 3), nb.len - 1);
-      cp_a = (const char*)(kv_entry + (size_t)(nb.start + ka) * DK) + 16 * cp_c8;
-      cp_b = (const char*)(kv_entry + (size_t)(nb.start + kb2) * DK) + 16 * cp_c8;
+      cp_a = (const char*)(base + (size_t)(st + ka) * DK) + 16 * cp_c8;
+      cp_b = (const char*)(base + (size_t)(st + kb2) * DK) + 16 * cp_c8;
     }
 
     const HS_LDS char* kbe = (const HS_LDS char*)(cur + koff_e);
@@ -590,20 +604,29 @@ __global__ __launch_bounds__(64) void merge_bf16_kernel(AttnArgs a) {
   if (lane == 0) a.lse[row * H + head] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
 }
 
+template <bool PAGED>
+void launch_attn_kernels(int op, const AttnArgs& a, dim3 grid, dim3 block, hipStream_t stream) {
+  if (a.nsplit == 1) {
+    if (op == kScore) hipLaunchKernelGGL((attn_bf16_kernel<kScore, false, PAGED>), grid, block, 0, stream, a);
+    else if (op == kGather) hipLaunchKernelGGL((attn_bf16_kernel<kGather, false, PAGED>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<kSwa, false, PAGED>), grid, block, 0, stream, a);
+  } else {
+    if (op == kScore) hipLaunchKernelGGL((attn_bf16_kernel<kScore, true, PAGED>), grid, block, 0, stream, a);
+    else if (op == kGather) hipLaunchKernelGGL((attn_bf16_kernel<kGather, true, PAGED>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<kSwa, true, PAGED>), grid, block, 0, stream, a);
+  }
+}
+
 int attn_bf16_launch(int op, const AttnArgs& a, hipStream_t stream) {
   const int items = a.g.B * a.g.Sq;
   const dim3 block(mla::NTHREADS);
   const dim3 grid((unsigned)(items * a.nsplit));
-  if (a.nsplit == 1) {
-    if (op == kScore) hipLaunchKernelGGL((attn_bf16_kernel<kScore, false>), grid, block, 0, stream, a);
-    else if (op == kGather) hipLaunchKernelGGL((attn_bf16_kernel<kGather, false>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<kSwa, false>), grid, block, 0, stream, a);
-  } else {
-    if (op == kScore) hipLaunchKernelGGL((attn_bf16_kernel<kScore, true>), grid, block, 0, stream, a);
-    else if (op == kGather) hipLaunchKernelGGL((attn_bf16_kernel<kGather, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<kSwa, true>), grid, block, 0, stream, a);
+  // Paged KV is a separate instantiation, so the in-place path carries no
+  // page-table code at all.
+  if (a.page_table != nullptr) launch_attn_kernels<true>(op, a, grid, block, stream);
+  else launch_attn_kernels<false>(op, a, grid, block, stream);
+  if (a.nsplit > 1)
     hipLaunchKernelGGL(merge_bf16_kernel, dim3((unsigned)(items * mla::H)), dim3(64), 0, stream, a);
-  }
   return (int)hipGetLastError();
 }
 

@@ -23,6 +23,8 @@ struct AttnArgs {
   int split_tiles;           // tiles per split: split s covers [s, s+1) * split_tiles
   float* ws_o;               // [items * nsplit, H, Dv] fp32 partial O
   float* ws_ml;              // [items * nsplit, H, 2] fp32 (max, denominator)
+  const int* page_table;     // [B, max_pages] page of each key block, or nullptr
+  int max_pages;
   Geom g;
 };
 

@@ -44,6 +44,15 @@
  * allocates nothing, keeps no pointer after return, and copies the small host
  * arrays of hs_problem (kv_lens, doc_start, doc_end) by value into kernel
  * arguments before returning.
+ * Paged KV (serving-style decode; the blog page on the unified sparse-attention
+ * dispatcher, the paragraph on batched and paged serving; page "Support attn
+ * sink in fa3", the KV-cache decode review): when page_table is set, kv is a
+ * pool of pages [n_pages, block_size, Dk] and key block j of entry b (its rows
+ * block_size*j .. +block_size-1) is page page_table[b * max_pages + j]. One
+ * page holds exactly one key block. Block ids, top-k indices and masks stay
+ * logical. Paged KV needs HS_BF16, no documents, and
+ * L_b <= max_pages * block_size for every entry (checked); the page ids must
+ * lie in the pool (device data, not checked).
  * Streams: `stream` is a hipStream_t passed as void* (NULL = default stream).
  * Calls enqueue work and return without synchronising; a fault inside a
  * kernel surfaces at the caller's next synchronisation.
@@ -91,6 +100,8 @@ typedef struct {
   const int32_t* doc_start; /* HOST [n_docs] packed documents, or NULL          */
   const int32_t* doc_end;   /* HOST [n_docs]                                     */
   int32_t n_docs;         /* 0, or 1..64 with B == 1 and kv_lens == NULL        */
+  const int32_t* page_table; /* DEVICE [B, max_pages] int32, or NULL: paged KV  */
+  int32_t max_pages;      /* pages per entry in page_table (paged KV only)      */
 } hs_problem;
 
 /* Number of key blocks NB = columns of block_logit: the largest, over the

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(hs.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.hs_version() == 100
+    assert lib.hs_version() == 101
 
 
 def _mla(**kw):
@@ -127,3 +127,31 @@ def test_probe_library_exports_every_declared_symbol():
     assert lib.hs_probe_mfma_bf16(1, 1, ctypes.c_void_p(256), ctypes.c_void_p(260), None) == -1
     assert lib.hs_probe_copy(ctypes.c_void_p(256), ctypes.c_void_p(4096), 15, None) == -1
     assert lib.hs_probe_copy(ctypes.c_void_p(256), ctypes.c_void_p(272), 64, None) == -1  # overlap
+
+
+def _raw_problem(**kw):
+    """An hs_problem built directly (no device tensors needed): paged-KV
+    validation happens on the host before any launch."""
+    f = dict(batch=1, seqlen_q=1, seqlen_kv=640, num_heads=64, head_dim_qk=576, head_dim_v=512,
+             block_size=64, scale=0.0, dtype=hs.HS_BF16, kv_lens=None, n_kv_lens=0,
+             doc_start=None, doc_end=None, n_docs=0, page_table=256, max_pages=10)
+    f.update(kw)
+    return hs.HsProblem(**f)
+
+
+def test_paged_kv_validation():
+    lib = hs.load_library()
+    assert lib.hs_num_blocks(ctypes.byref(_raw_problem())) == 10
+    assert lib.hs_num_blocks(ctypes.byref(_raw_problem(max_pages=9))) == hs.HS_ERR_INVALID_ARG
+    assert lib.hs_num_blocks(ctypes.byref(_raw_problem(max_pages=0))) == hs.HS_ERR_INVALID_ARG
+    assert lib.hs_num_blocks(ctypes.byref(_raw_problem(page_table=None))) == hs.HS_ERR_INVALID_ARG
+    assert lib.hs_num_blocks(ctypes.byref(_raw_problem(page_table=258))) == hs.HS_ERR_INVALID_ARG
+    assert lib.hs_num_blocks(ctypes.byref(_raw_problem(
+        dtype=hs.HS_F32, num_heads=8, head_dim_qk=96, head_dim_v=64))) == hs.HS_ERR_UNSUPPORTED
+    ds = (ctypes.c_int32 * 1)(0)
+    de = (ctypes.c_int32 * 1)(640)
+    assert lib.hs_num_blocks(ctypes.byref(_raw_problem(
+        seqlen_q=640, doc_start=ds, doc_end=de, n_docs=1))) == hs.HS_ERR_INVALID_ARG
+    lens = (ctypes.c_int32 * 2)(100, 640)
+    assert lib.hs_num_blocks(ctypes.byref(_raw_problem(
+        batch=2, kv_lens=lens, n_kv_lens=2))) == 10
