@@ -41,6 +41,7 @@ class HsProblem(ctypes.Structure):
         ("doc_start", ctypes.POINTER(ctypes.c_int32)),
         ("doc_end", ctypes.POINTER(ctypes.c_int32)), ("n_docs", ctypes.c_int32),
         ("page_table", ctypes.c_void_p), ("max_pages", ctypes.c_int32),
+        ("kv_lens_device", ctypes.c_void_p),
     ]
 
 
@@ -98,15 +99,20 @@ class Problem:
                  kv_lens: Optional[Sequence[int]] = None,
                  doc_start: Optional[Sequence[int]] = None,
                  doc_end: Optional[Sequence[int]] = None,
-                 page_table=None):
+                 page_table=None, kv_lens_device=None):
         """page_table: optional int32 device tensor [B, max_pages] (paged KV: kv is
-        then a pool [n_pages, block_size, Dk]); the tensor must outlive the calls."""
+        then a pool [n_pages, block_size, Dk]); kv_lens_device: optional int32
+        device tensor [B] of lengths read at run time (paged KV only; Skv is
+        then the capacity). Both tensors must outlive the calls."""
         self.B, self.Sq, self.Skv, self.H, self.Dk, self.Dv = B, Sq, Skv, H, Dk, Dv
         self.page_table = page_table
         if page_table is not None:
             _dev("page_table", page_table)
             if page_table.dim() != 2 or page_table.shape[0] != B:
                 raise ValueError("page_table must be [B, max_pages]")
+        self.kv_lens_device = kv_lens_device
+        if kv_lens_device is not None:
+            _dev("kv_lens_device", kv_lens_device, shape=(B,))
         self.dtype = dtype
         self._kv = (ctypes.c_int32 * len(kv_lens))(*kv_lens) if kv_lens is not None else None
         self._ds = (ctypes.c_int32 * len(doc_start))(*doc_start) if doc_start is not None else None
@@ -121,7 +127,8 @@ class Problem:
             doc_end=ctypes.cast(self._de, ctypes.POINTER(ctypes.c_int32)) if self._de else None,
             n_docs=len(doc_start) if doc_start is not None else 0,
             page_table=None if page_table is None else page_table.data_ptr(),
-            max_pages=0 if page_table is None else int(page_table.shape[1]))
+            max_pages=0 if page_table is None else int(page_table.shape[1]),
+            kv_lens_device=None if kv_lens_device is None else kv_lens_device.data_ptr())
 
     @property
     def ref(self):

@@ -128,6 +128,15 @@ hs_status prepare(const hs_problem* p, hs::Geom& g) {
     g.NB = nb;
   }
 
+  if (p->kv_lens_device) {
+    if (!p->page_table)
+      return fail(HS_ERR_INVALID_ARG, "kv_lens_device needs paged KV (page_table)");
+    if (p->kv_lens)
+      return fail(HS_ERR_INVALID_ARG, "kv_lens and kv_lens_device are exclusive");
+    if (reinterpret_cast<uintptr_t>(p->kv_lens_device) % 4 != 0)
+      return fail(HS_ERR_INVALID_ARG, "kv_lens_device is not 4-byte aligned");
+    g.kv_len_dev = p->kv_lens_device;  // kv_len[] keeps the capacity seqlen_kv
+  }
   if (p->page_table || p->max_pages != 0) {
     if (!p->page_table || p->max_pages < 1)
       return fail(HS_ERR_INVALID_ARG, "paged KV needs page_table and max_pages >= 1");

@@ -184,8 +184,8 @@ void attn_bf16_kernel(AttnArgs a) {
   const int r = g.Sq - 1 - (w % g.Sq);
   const size_t row = (size_t)b * g.Sq + r;
 
-  const RowRange rr = row_range(g, OP, b, r, a.window);
-  const int nb_b = nb_of_entry(g, b);
+  const RowRange rr = row_range<PAGED>(g, OP, b, r, a.window);
+  const int nb_b = nb_of_entry<PAGED>(g, b);
 
   // Tile sequence: a block range, or the listed blocks that intersect the
   // allowed key range (compacted in order of the list).
@@ -197,7 +197,7 @@ void attn_bf16_kernel(AttnArgs a) {
       if (lane < a.top_k) {
         j = a.block_idx[row * a.top_k + lane];
         if (j >= 0 && j < nb_b) {
-          const Blk bk = block_rows(g, b, j);
+          const Blk bk = block_rows<PAGED>(g, b, j);
           ok = !(bk.start > rr.hi || bk.start + bk.len - 1 < rr.lo);
         }
       }
@@ -243,7 +243,7 @@ void attn_bf16_kernel(AttnArgs a) {
   };
   if (t_begin < t_end) {
     const int j0 = tile_block(t_begin);
-    const Blk b0 = block_rows(g, b, j0);
+    const Blk b0 = block_rows<PAGED>(g, b, j0);
     stage_tile(buf_a, block_base(j0), PAGED ? 0 : b0.start, b0.len, wave, lane);
   }
 
@@ -289,7 +289,7 @@ void attn_bf16_kernel(AttnArgs a) {
   // is spread over the score MFMAs of half 0.
   auto step = [&](char* cur, char* nxt, int t) __attribute__((always_inline)) {
     const int j = tile_block(t);
-    const Blk blk = block_rows(g, b, j);
+    const Blk blk = block_rows<PAGED>(g, b, j);
     const int klo = rr.lo - blk.start, khi = min(rr.hi - blk.start, blk.len - 1);
 
     __builtin_amdgcn_s_waitcnt(0);
@@ -306,7 +306,7 @@ void attn_bf16_kernel(AttnArgs a) {
     char* cp_dst = nxt + wave * 1024;
     if (has_next) {
       const int jn = tile_block(t + 1);
-      const Blk nb = block_rows(g, b, jn);
+      const Blk nb = block_rows<PAGED>(g, b, jn);
       const bf16* base = block_base(jn);
       const int st = PAGED ? 0 : nb.start;
       const int ka = min(8 * wave + (lane >> 3), nb.len - 1);

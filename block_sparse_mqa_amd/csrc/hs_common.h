@@ -28,7 +28,20 @@ struct Geom {
   int doc_start[kMaxDocs];
   int doc_end[kMaxDocs];
   int doc_blk0[kMaxDocs + 1];    // first global block id of each document
+  const int* kv_len_dev;         // device [B] valid KV rows (paged decode), or nullptr:
+                                 // then kv_len holds the capacity the host planned with
 };
+
+// Valid KV rows of entry b. Launches given device lengths (DEV and
+// kv_len_dev set) read them at run time; otherwise, and always on the host,
+// the value in the arguments.
+template <bool DEV = false>
+__host__ __device__ inline int kv_len_of(const Geom& g, int b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  if (DEV && g.kv_len_dev != nullptr) return g.kv_len_dev[b];
+#endif
+  return g.kv_len[b];
+}
 
 struct Doc {
   int start, end, blk0;
@@ -39,8 +52,9 @@ struct Blk {
 };
 
 // Document holding position p of entry b.
+template <bool DEV = false>
 __host__ __device__ inline Doc doc_of_pos(const Geom& g, int b, int p) {
-  if (g.n_docs == 0) return Doc{0, g.kv_len[b], 0};
+  if (g.n_docs == 0) return Doc{0, kv_len_of<DEV>(g, b), 0};
   int lo = 0, hi = g.n_docs - 1;
   while (lo < hi) {
     int mid = (lo + hi + 1) >> 1;
@@ -50,16 +64,18 @@ __host__ __device__ inline Doc doc_of_pos(const Geom& g, int b, int p) {
 }
 
 // Number of key blocks of entry b.
+template <bool DEV = false>
 __device__ __forceinline__ int nb_of_entry(const Geom& g, int b) {
-  if (g.n_docs == 0) return (g.kv_len[b] + g.BS - 1) / g.BS;
+  if (g.n_docs == 0) return (kv_len_of<DEV>(g, b) + g.BS - 1) / g.BS;
   return g.doc_blk0[g.n_docs];
 }
 
 // Rows [start, start + len) of block j of entry b (j must be valid).
+template <bool DEV = false>
 __device__ __forceinline__ Blk block_rows(const Geom& g, int b, int j) {
   if (g.n_docs == 0) {
     int s = j * g.BS;
-    return Blk{s, min(g.BS, g.kv_len[b] - s)};
+    return Blk{s, min(g.BS, kv_len_of<DEV>(g, b) - s)};
   }
   int lo = 0, hi = g.n_docs - 1;
   while (lo < hi) {
@@ -83,10 +99,11 @@ struct RowRange {
   int pos, lo, hi, j_first, j_last;
 };
 
+template <bool DEV = false>
 __host__ __device__ inline RowRange row_range(const Geom& g, int op, int b, int r, int window) {
   RowRange rr;
-  rr.pos = g.kv_len[b] - g.Sq + r;
-  Doc d = doc_of_pos(g, b, rr.pos);
+  rr.pos = kv_len_of<DEV>(g, b) - g.Sq + r;
+  Doc d = doc_of_pos<DEV>(g, b, rr.pos);
   rr.lo = d.start;
   rr.hi = rr.pos;
   if (op == kSwa && rr.pos - window + 1 > rr.lo) rr.lo = rr.pos - window + 1;

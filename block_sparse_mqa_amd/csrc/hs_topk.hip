@@ -38,8 +38,8 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   const int rowi = blockIdx.x * 4 + wave;
   if (rowi >= g.B * g.Sq) return;
   const int b = rowi / g.Sq, r = rowi % g.Sq;
-  const int pos = g.kv_len[b] - g.Sq + r;
-  const Doc d = doc_of_pos(g, b, pos);
+  const int pos = kv_len_of<true>(g, b) - g.Sq + r;
+  const Doc d = doc_of_pos<true>(g, b, pos);
   const int own = block_of_pos(g, d, pos);
   const int K = a.top_k;
   const float* bl = a.block_logit + (size_t)rowi * g.NB;

@@ -53,6 +53,13 @@
  * logical. Paged KV needs HS_BF16, no documents, and
  * L_b <= max_pages * block_size for every entry (checked); the page ids must
  * lie in the pool (device data, not checked).
+ * Device-resident lengths (paged KV only): with kv_lens_device set, L_b is
+ * read from device memory when the kernels run, so one recorded launch (for
+ * instance a captured HIP graph) serves changing cache lengths. The host
+ * then plans with the capacity seqlen_kv (<= max_pages * block_size,
+ * checked): hs_num_blocks and hs_workspace_size use it, block_logit has
+ * ceil(seqlen_kv / block_size) columns (-inf past each entry's blocks), and
+ * seqlen_q <= L_b <= seqlen_kv must hold (device data, not checked).
  * Streams: `stream` is a hipStream_t passed as void* (NULL = default stream).
  * Calls enqueue work and return without synchronising; a fault inside a
  * kernel surfaces at the caller's next synchronisation.
@@ -102,6 +109,8 @@ typedef struct {
   int32_t n_docs;         /* 0, or 1..64 with B == 1 and kv_lens == NULL        */
   const int32_t* page_table; /* DEVICE [B, max_pages] int32, or NULL: paged KV  */
   int32_t max_pages;      /* pages per entry in page_table (paged KV only)      */
+  const int32_t* kv_lens_device; /* DEVICE [B] int32 valid KV lengths, read at  */
+                          /* run time (paged KV only; kv_lens must be NULL)     */
 } hs_problem;
 
 /* Number of key blocks NB = columns of block_logit: the largest, over the

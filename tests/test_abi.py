@@ -155,3 +155,18 @@ def test_paged_kv_validation():
     lens = (ctypes.c_int32 * 2)(100, 640)
     assert lib.hs_num_blocks(ctypes.byref(_raw_problem(
         batch=2, kv_lens=lens, n_kv_lens=2))) == 10
+
+
+def test_device_lengths_validation():
+    lib = hs.load_library()
+    ok = _raw_problem(batch=2, kv_lens_device=512)
+    assert lib.hs_num_blocks(ctypes.byref(ok)) == 10            # capacity 640 -> 10 blocks
+    assert lib.hs_num_blocks(ctypes.byref(_raw_problem(page_table=None, max_pages=0,
+                                                       kv_lens_device=512))) == hs.HS_ERR_INVALID_ARG
+    lens = (ctypes.c_int32 * 1)(100)
+    assert lib.hs_num_blocks(ctypes.byref(_raw_problem(kv_lens=lens, n_kv_lens=1,
+                                                       kv_lens_device=512))) == hs.HS_ERR_INVALID_ARG
+    assert lib.hs_num_blocks(ctypes.byref(_raw_problem(kv_lens_device=514))) == hs.HS_ERR_INVALID_ARG
+    n = ctypes.c_size_t(0)
+    assert lib.hs_workspace_size(ctypes.byref(ok), hs.HS_OP_BLOCK_SCORE, 0, 0, ctypes.byref(n)) == 0
+    assert n.value > 0                                          # decode split planned at capacity

@@ -69,3 +69,75 @@ def test_paged_kv_matches_contiguous(case):
     res["swa_out"] = assert_close(np64(osw), os_ref, tol, "paged swa out")
     res["swa_lse"] = assert_close(np64(lsw), ls_ref, tol, "paged swa lse")
     say(f"[gpu] paged {case}: {res}")
+
+
+def _decode_reference(p, lens, NB):
+    """Oracle results for lengths `lens`; block_logit padded with -inf to the
+    NB columns the capacity gives (the ABI writes -inf past each entry's blocks)."""
+    kw = dict(block_size=p.block_size, kv_lens=lens)
+    o, l, b = ref.block_score(p.q, p.kv, p.sink, p.Dv, p.scale, **kw)
+    pad = np.full(b.shape[:-1] + (NB - b.shape[-1],), -np.inf)
+    b = np.concatenate([b, pad], axis=-1)
+    os_, ls = ref.swa(p.q, p.kv, p.sink, p.Dv, p.scale, p.window, **kw)
+    return o, l, b, os_, ls
+
+
+def test_paged_device_lengths_and_graph_replay():
+    """Lengths in device memory, read at run time: one captured graph of the
+    decode calls replayed with different lengths matches the oracle each time."""
+    say("[gpu] paged KV with device lengths, captured graph")
+    B, cap = 8, 2048
+    rng = np.random.default_rng(44)
+    full = [cap] * B
+    p = inputs.make(B, 1, cap, MLA["H"], MLA["Dk"], MLA["Dv"], seed=44, kv_lens=full, top_k=4,
+                    window=200, name="paged_devlen")
+    pool, pt = _paged(p, seed=45)
+    pool, pt = pool.cuda(), pt.cuda()
+    q, sink = p.q.cuda(), p.sink.cuda()
+    lens_dev = torch.full((B,), cap, dtype=torch.int32, device="cuda")
+    prob = hs.Problem(B, 1, cap, p.H, p.Dk, p.Dv, page_table=pt, kv_lens_device=lens_dev)
+    NB = hs.hs_num_blocks(prob)
+    assert NB == cap // 64
+    out = torch.empty((B, 1, p.H, p.Dv), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, 1, p.H), dtype=torch.float32, device="cuda")
+    bl = torch.empty((B, 1, NB), dtype=torch.float32, device="cuda")
+    osw, lsw = torch.empty_like(out), torch.empty_like(lse)
+    ws1 = hs._workspace(prob, hs.HS_OP_BLOCK_SCORE)
+    ws4 = hs._workspace(prob, hs.HS_OP_SWA, window=p.window)
+
+    def calls():
+        hs.hs_block_score_fwd(prob, q, pool, sink, out, lse, bl, ws1)
+        hs.hs_swa_fwd(prob, q, pool, sink, p.window, osw, lsw, ws4)
+
+    tol = tol_for(p)
+    # eager first, at full length
+    calls()
+    torch.cuda.synchronize()
+    o, l, b, os_, ls = _decode_reference(p, full, NB)
+    assert_close(np64(out), o, tol, "eager out")
+    assert_close(np64(bl), b, 2e-4, "eager block_logit")
+    # capture once, replay with other lengths
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        calls()                      # warm the side stream before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        calls()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        lens = [int(x) for x in rng.integers(1, cap + 1, size=B)]
+        lens_dev.copy_(torch.tensor(lens, dtype=torch.int32))
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        o, l, b, os_, ls = _decode_reference(p, lens, NB)
+        e = {"out": assert_close(np64(out), o, tol, f"replay {rep} out"),
+             "lse": assert_close(np64(lse), l, tol, f"replay {rep} lse"),
+             "block_logit": assert_close(np64(bl), b, 2e-4, f"replay {rep} block_logit"),
+             "swa_out": assert_close(np64(osw), os_, tol, f"replay {rep} swa out"),
+             "swa_lse": assert_close(np64(lsw), ls, tol, f"replay {rep} swa lse")}
+        say(f"[gpu] graph replay {rep} lengths {min(lens)}..{max(lens)}: {e}")
