@@ -15,9 +15,10 @@
 //   reduction over a tile is that block's log-sum-exp. Four waves split the
 //   heads (wave w owns heads 16w .. 16w+15) and share each KV tile, which is
 //   staged once in LDS (the one KV head serves every query head). One
-//   workgroup per CU, one wave per SIMD: Q stays in 72 VGPRs, the O
-//   accumulator takes 128, the scores 16. Tiles are double-buffered so the
-//   copy of tile t+1 overlaps the MFMAs of tile t.
+//   workgroup per CU, one wave per SIMD with the whole register file: the O
+//   accumulator takes 128 VGPRs and the scores 16; Q (72 registers) is held
+//   for the whole row in AGPRs and copied to VGPRs per k-step. Tiles are
+//   double-buffered so the copy of tile t+1 overlaps the MFMAs of tile t.
 //
 // Contractions (v_mfma_f32_16x16x32_bf16)
 //   S^T[key, row] = K_tile[key, :] . Q[row, :]     A = K (LDS), B = Q (VGPRs)
@@ -40,10 +41,9 @@
 //   runs, but with the copy in flight they are slower end to end: the LDS DMA
 //   returns then find fewer free LDS cycles and hold up the next tile. Moving
 //   the copy elsewhere in the tile, or staging it through registers, costs
-//   more than the conflicts do.
-//   Tiles are filled with
-//   global_load_lds_dwordx4 (lane l of a wave instruction writes 16 B at base
-//   + 16 l): one instruction covers 8 keys x one full 128 B line each.
+//   more than the conflicts do. Tiles are filled with global_load_lds_dwordx4
+//   (lane l of a wave instruction writes 16 B at base + 16 l): one
+//   instruction covers 8 keys x one full 128 B line each.
 //
 // Softmax: scores live in the log2 domain (scale * log2 e folded in). Per
 //   tile, p = exp2(x - m_tile): the tile max is the stabiliser of the block
@@ -79,14 +79,8 @@ constexpr int TILE_BYTES = NGR * GR_BYTES;   // 73728
 constexpr int KSTEPS = DK / 32;              // 18 k-steps of the score MFMA
 constexpr int DBLK = DV / 16;                // 32 column blocks of O
 constexpr float TAU = 8.0f;                  // lazy-rescale threshold (log2 units)
-#ifndef HS_SG
-#define HS_SG 2
-#endif
-#ifndef HS_PG
-#define HS_PG 8
-#endif
-constexpr int SG = HS_SG;                    // k-steps per score prefetch group
-constexpr int PG = HS_PG;                    // column blocks per PV prefetch group
+constexpr int SG = 2;                        // k-steps per score prefetch group
+constexpr int PG = 8;                        // column blocks per PV prefetch group
 }  // namespace mla
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
