@@ -17,11 +17,11 @@
 //   staged once in LDS (the one KV head serves every query head). One
 //   workgroup per CU, one wave per SIMD with the whole register file: the O
 //   accumulator takes 128 VGPRs and the scores 16; Q (72 registers) is held
-//   for the whole row in AGPRs and copied to VGPRs per k-step. Tiles are
+//   for the whole row in AGPRs, which the score MFMA reads directly. Tiles are
 //   double-buffered so the copy of tile t+1 overlaps the MFMAs of tile t.
 //
 // Contractions (v_mfma_f32_16x16x32_bf16)
-//   S^T[key, row] = K_tile[key, :] . Q[row, :]     A = K (LDS), B = Q (VGPRs)
+//   S^T[key, row] = K_tile[key, :] . Q[row, :]     A = K (LDS), B = Q (AGPRs)
 //   Lane l then holds 16 scores of ONE row (head l%16): the softmax row
 //   statistics are in-register reductions plus two exchanges across the four
 //   16-lane groups.
@@ -33,17 +33,20 @@
 // LDS tile layout: 9 groups of 64 columns; group G holds, for each key k, the
 //   128 B of columns 64G .. 64G+63 at [G * 8192 + k * 128]. Inside those
 //   128 B, 16-byte chunk c8 (8 columns) sits in slot c8 ^ sw(k), with
-//   sw(k) = 2 * ((k >> 1) & 3) + ((k >> 3) & 1). Transpose reads are
-//   bank-conflict free under it; the score-fragment ds_read_b128 reads
-//   conflict 2-way (lanes {0-7, 32-39}, {8-15, 40-47}, ... share a cycle), so
-//   they run at about half the LDS rate. Swizzles free of conflicts for both
-//   reads exist (e.g. 3 * bit2 + 4 * bit1) and are faster when no tile copy
-//   runs, but with the copy in flight they are slower end to end: the LDS DMA
-//   returns then find fewer free LDS cycles and hold up the next tile. Moving
-//   the copy elsewhere in the tile, or staging it through registers, costs
-//   more than the conflicts do. Tiles are filled with global_load_lds_dwordx4
-//   (lane l of a wave instruction writes 16 B at base + 16 l): one
-//   instruction covers 8 keys x one full 128 B line each.
+//   sw(k) = 3 * bit2(k) + 4 * bit1(k): both the score-fragment ds_read_b128
+//   reads (lanes {0-7, 32-39}, {8-15, 40-47}, ... share an LDS cycle) and the
+//   transpose reads (lanes 0-31, 32-63) are free of bank conflicts. Tiles are
+//   filled with global_load_lds_dwordx4 (lane l of a wave instruction writes
+//   16 B at base + 16 l): one instruction covers 8 keys x one full 128 B line
+//   each.
+//
+// Issue: with one wave per SIMD, the wave issues at most one instruction per
+//   four cycles, and a 16x16x32 MFMA lasts 16. The tile is therefore written
+//   as one straight-line stream of 136 MFMAs in which every other instruction
+//   counts: each MFMA is followed by the LDS read of the operand six places
+//   ahead and preceded by a wait for its own operand only (LDS reads complete
+//   in order), the score MFMA takes Q from AGPRs without copies, and the tile
+//   copy has no branches.
 //
 // Softmax: scores live in the log2 domain (scale * log2 e folded in). Per
 //   tile, p = exp2(x - m_tile): the tile max is the stabiliser of the block
@@ -53,6 +56,8 @@
 //   same up to rounding. The sink enters as the initial reference max
 //   sigma * log2 e with weight 1, counted once per row.
 #include <hip/hip_runtime.h>
+
+#include <utility>
 
 #include "hs_common.h"
 #include "hs_kernels.h"
@@ -65,7 +70,6 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #define HS_LDS __attribute__((address_space(3)))
-#define HS_GLB __attribute__((address_space(1)))
 
 namespace mla {
 constexpr int H = 64, DK = 576, DV = 512, BS = 64;
@@ -79,8 +83,6 @@ constexpr int TILE_BYTES = NGR * GR_BYTES;   // 73728
 constexpr int KSTEPS = DK / 32;              // 18 k-steps of the score MFMA
 constexpr int DBLK = DV / 16;                // 32 column blocks of O
 constexpr float TAU = 8.0f;                  // lazy-rescale threshold (log2 units)
-constexpr int SG = 2;                        // k-steps per score prefetch group
-constexpr int PG = 8;                        // column blocks per PV prefetch group
 }  // namespace mla
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -118,12 +120,60 @@ __device__ __forceinline__ float max_row16(float v) {
   return v;
 }
 
-// Chunk swizzle of key k inside a tile row (depends on bits 1 to 3 only).
-__device__ __forceinline__ int swz(int k) { return 2 * ((k >> 1) & 3) + ((k >> 3) & 1); }
+// Chunk swizzle of key k inside a tile row (depends on bits 1 and 2 only).
+__device__ __forceinline__ int swz(int k) { return 3 * ((k >> 2) & 1) + 4 * ((k >> 1) & 1); }
 
-// Wait for outstanding LDS reads only (lgkmcnt(0); vmcnt and expcnt left at
-// their maxima so in-flight tile copies keep running).
-__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// Wait until at most N LDS operations are outstanding (vmcnt and expcnt left
+// at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_lgkm() {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+  __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));
+}
+// LDS operations issued after fragment i of the tile's operand stream that
+// may still be pending when MFMA i issues: the fragments requested up to LA - 1
+// places ahead (score fragments are one read, V^T fragments two), plus the
+// block-score slot write issued at stream position iw.
+__host__ __device__ constexpr int stream_pending(int i, int la, int nsf, int nf, int iw) {
+  int n = 0;
+  for (int f = i + 1; f <= i + la - 1 && f < nf; ++f) n += f < nsf ? 1 : 2;
+  if (iw >= 0 && i > iw && i <= iw + la) n += 1;
+  return n;
+}
+// One LDS DMA instruction: lane l copies 16 B from src (per lane) to LDS
+// byte lds + 16 l, the LDS base taken from M0 (the compiler sets it from the
+// operand; one wait state separates that write from the DMA). Issued as
+// inline assembly so that the compiler's wait analysis does not take it for
+// an out-of-order LDS operation and drain every LDS read in flight; it is
+// counted by vmcnt only, and callers wait for it with s_waitcnt vmcnt.
+__device__ __forceinline__ void dma16(const char* src, char* lds) {
+  const unsigned m = (unsigned)(uintptr_t)(HS_LDS char*)lds;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m) : "memory");
+}
+// Score MFMA with the Q operand read straight from AGPRs (the builtin in the
+// VGPR-accumulator form copies it to VGPRs first: 72 extra instructions per
+// tile). Dependent MFMAs on one accumulator are interlocked by the hardware,
+// but the compiler inserts no wait states for VALU instructions around inline
+// assembly: the score stream below reads these results with VALU code only
+// after at least three further MFMAs.
+__device__ __forceinline__ f32x4 mfma_q0(bf16x8 k, bf16x8 q) {
+  f32x4 d;
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=v"(d) : "v"(k), "a"(q));
+  return d;
+}
+__device__ __forceinline__ f32x4 mfma_q(bf16x8 k, bf16x8 q, f32x4 c) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(k), "a"(q));
+  return c;
+}
+template <typename Fn, int... Is>
+__device__ __forceinline__ void static_for_impl(Fn&& fn, std::integer_sequence<int, Is...>) {
+  (fn(std::integral_constant<int, Is>{}), ...);
+}
+// fn(std::integral_constant<int, i>) for i = 0 .. N-1, with i a constant.
+template <int N, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& fn) {
+  static_for_impl(fn, std::make_integer_sequence<int, N>{});
+}
 
 // Copy one 64-key tile (KV rows base + start .. + len - 1, clamped) into an
 // LDS buffer.
@@ -144,10 +194,8 @@ __device__ __forceinline__ void stage_tile(char* buf, const bf16* base, int star
   char* dst = buf + wave_u * 1024;
 #pragma unroll
   for (int G = 0; G < NGR; ++G) {
-    __builtin_amdgcn_global_load_lds((const HS_GLB void*)(src_a + 128 * G),
-                                     (HS_LDS void*)(dst + G * GR_BYTES), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const HS_GLB void*)(src_b + 128 * G),
-                                     (HS_LDS void*)(dst + G * GR_BYTES + 4096), 16, 0, 0);
+    dma16(src_a + 128 * G, dst + G * GR_BYTES);
+    dma16(src_b + 128 * G, dst + G * GR_BYTES + 4096);
   }
 }
 
@@ -294,20 +342,19 @@ void attn_bf16_kernel(AttnArgs a) {
       for (int k = 1; k < NW; ++k) v = fmaxf(v, bl_slot[par ^ 1][k]);
       a.block_logit[row * g.NB + j_prev] = v * kLn2;
     }
+    // Copy source: the next tile's block, or on the last tile the current
+    // block again into the idle buffer (harmless, and it keeps the copy free
+    // of branches inside the MFMA stream).
     const bool has_next = t + 1 < t_end;
-    const char* cp_a = nullptr;
-    const char* cp_b = nullptr;
     char* cp_dst = nxt + wave * 1024;
-    if (has_next) {
-      const int jn = tile_block(t + 1);
-      const Blk nb = block_rows<PAGED>(g, b, jn);
-      const bf16* base = block_base(jn);
-      const int st = PAGED ? 0 : nb.start;
-      const int ka = min(8 * wave + (lane >> 3), nb.len - 1);
-      const int kb2 = min(8 * (wave + 4) + (lane >> 3), nb.len - 1);
-      cp_a = (const char*)(base + (size_t)(st + ka) * DK) + 16 * cp_c8;
-      cp_b = (const char*)(base + (size_t)(st + kb2) * DK) + 16 * cp_c8;
-    }
+    const int jn = has_next ? tile_block(t + 1) : j;
+    const Blk nb = has_next ? block_rows<PAGED>(g, b, jn) : blk;
+    const bf16* nbase = block_base(jn);
+    const int nst = PAGED ? 0 : nb.start;
+    const int ka = min(8 * wave + (lane >> 3), nb.len - 1);
+    const int kb2 = min(8 * (wave + 4) + (lane >> 3), nb.len - 1);
+    const char* cp_a = (const char*)(nbase + (size_t)(nst + ka) * DK) + 16 * cp_c8;
+    const char* cp_b = (const char*)(nbase + (size_t)(nst + kb2) * DK) + 16 * cp_c8;
 
     const HS_LDS char* kbe = (const HS_LDS char*)(cur + koff_e);
     const HS_LDS char* kbo = (const HS_LDS char*)(cur + koff_o);
@@ -410,99 +457,77 @@ void attn_bf16_kernel(AttnArgs a) {
       l_run += lph[h];
     };
 
-    f32x4 s[4] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f},
-                  f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    constexpr int NG = KSTEPS / SG;  // 9 groups per half
-    bf16x8 fa[2 * SG], fb[2 * SG];
-#pragma unroll
-    for (int u = 0; u < SG; ++u)
-#pragma unroll
-      for (int k = 0; k < 2; ++k) fa[2 * u + k] = kfrag(u, k);
-    // Scores, both halves: group gi of half h uses key blocks 2h, 2h+1.
-#pragma unroll
-    for (int n = 0; n < 2 * NG; ++n) {
-      const int h = n / NG, gi = n % NG;
-      bf16x8* fc = (n & 1) ? fb : fa;
-      bf16x8* fn = (n & 1) ? fa : fb;
-      wait_lds();
-      if (n + 1 < 2 * NG) {
-        const int h1 = (n + 1) / NG, g1 = (n + 1) % NG;
-#pragma unroll
-        for (int u = 0; u < SG; ++u)
-#pragma unroll
-          for (int k = 0; k < 2; ++k) fn[2 * u + k] = kfrag(g1 * SG + u, 2 * h1 + k);
-      }
+    // Operand stream of one tile: 72 score fragments (half h, k-step ks, key
+    // block 2h + k), one ds_read_b128 each, then 64 V^T fragments (k-step kk,
+    // column block db), two transpose reads each. The fragment LA places ahead
+    // is requested right after each MFMA, so LA fragments stay in flight, and
+    // each MFMA waits only for its own operand (LDS reads complete in order).
+    f32x4 s[4];
+    constexpr int NSF = 2 * KSTEPS * 2;  // 72 score fragments
+    constexpr int NF = NSF + 2 * DBLK;   // + 64 V^T fragments
+    constexpr int LA = 6;
+    constexpr int R = LA + 1;
+    bf16x8 fr[R];
+    auto load_frag = [&](int f) __attribute__((always_inline)) -> bf16x8 {
+      if (f < NSF) return kfrag((f % (2 * KSTEPS)) / 2, 2 * (f / (2 * KSTEPS)) + (f & 1));
+      return vfrag((f - NSF) / DBLK, (f - NSF) % DBLK);
+    };
+    wait_lgkm<0>();
+    static_for<LA>([&](auto F) __attribute__((always_inline)) {
+      constexpr int f = decltype(F)::value;
+      fr[f % R] = load_frag(f);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < SG; ++u)
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-          s[2 * h + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fc[2 * u + k], qreg[gi * SG + u],
-                                                                 s[2 * h + k], 0, 0, 0);
-      if (h == 0) {
-        // copy column groups G of the next tile in the shadow of these MFMAs
-        if (has_next) {
-#pragma unroll
-          for (int G = (NGR * gi) / NG; G < (NGR * (gi + 1)) / NG; ++G) {
-            __builtin_amdgcn_global_load_lds((const HS_GLB void*)(cp_a + 128 * G),
-                                             (HS_LDS void*)(cp_dst + G * GR_BYTES), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const HS_GLB void*)(cp_b + 128 * G),
-                                             (HS_LDS void*)(cp_dst + G * GR_BYTES + 4096), 16,
-                                             0, 0);
+    });
+    __builtin_amdgcn_sched_barrier(0);
+
+    static_for<NF>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      if constexpr (i == NSF + DBLK) commit_half(1);
+      wait_lgkm<stream_pending(i, LA, NSF, NF, OP == kScore ? NSF + DBLK + 7 : -1)>();
+      if constexpr (i < NSF) {
+        constexpr int h = i / (2 * KSTEPS), ks = (i % (2 * KSTEPS)) / 2, k = i & 1;
+        if constexpr (ks == 0)
+          s[2 * h + k] = mfma_q0(fr[i % R], qreg[ks]);
+        else
+          s[2 * h + k] = mfma_q(fr[i % R], qreg[ks], s[2 * h + k]);
+      } else {
+        constexpr int kk = (i - NSF) / DBLK, db = (i - NSF) % DBLK;
+        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[i % R], pbh[kk], oacc[db], 0, 0, 0);
+      }
+      if constexpr (i + LA < NF) fr[(i + LA) % R] = load_frag(i + LA);
+      if constexpr (i < NSF / 2) {
+        // copy column group G of the next tile in the shadow of the half-0 score MFMAs
+        if ((i & 3) == 3) {
+          const int G = i >> 2;
+          dma16(cp_a + 128 * G, cp_dst + G * GR_BYTES);
+          dma16(cp_b + 128 * G, cp_dst + G * GR_BYTES + 4096);
+        }
+      } else if constexpr (i < NSF) {
+        // softmax of half 0 in the shadow of the half-1 score MFMAs
+        if ((i & 3) == 3) {
+          const int gi = (i - NSF / 2) >> 2;
+          soft_piece(0, gi, s);
+          if (gi == 8) {
+            prepare_half(0);
+            commit_half(0);
           }
         }
-      } else {
-#pragma unroll
-        for (int piece = (9 * gi) / NG; piece < (9 * (gi + 1)) / NG; ++piece)
-          soft_piece(0, piece, s);
-        if (gi == NG - 1) {
-          prepare_half(0);
-          commit_half(0);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // PV over the two 32-key k-steps; V^T fragments one group ahead.
-    constexpr int NGRP = DBLK / PG;  // groups per k-step
-    bf16x8 va[PG], vb2[PG];
-#pragma unroll
-    for (int u = 0; u < PG; ++u) va[u] = vfrag(0, u);
-
-#pragma unroll
-    for (int n = 0; n < 2 * NGRP; ++n) {
-      const int kk = n / NGRP, gi = n % NGRP;
-      bf16x8* vc = (n & 1) ? vb2 : va;
-      bf16x8* vn = (n & 1) ? va : vb2;
-      if (n == NGRP) commit_half(1);
-      wait_lds();
-      if (n + 1 < 2 * NGRP) {
-        const int kk1 = (n + 1) / NGRP, g1 = (n + 1) % NGRP;
-#pragma unroll
-        for (int u = 0; u < PG; ++u) vn[u] = vfrag(kk1, g1 * PG + u);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < PG; ++u) {
-        const int db = gi * PG + u;
-        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vc[u], pbh[kk], oacc[db], 0, 0, 0);
-      }
-      if (kk == 0) {
+      } else if constexpr (i < NSF + DBLK) {
         // softmax of half 1 in the shadow of the half-0 PV MFMAs
-        for (int piece = (9 * gi) / NGRP; piece < (9 * (gi + 1)) / NGRP; ++piece)
-          soft_piece(1, piece, s);
-        if (gi == NGRP - 1) prepare_half(1);
-      } else if (OP == kScore && gi == 0) {
+        const int v = i - NSF;
+        if (v % 3 == 2 && v / 3 < 9) soft_piece(1, v / 3, s);
+        if (v == 29) prepare_half(1);
+      } else if constexpr (OP == kScore && i == NSF + DBLK + 7) {
         // block log-sum-exp over both halves, then max over the wave's heads
         const float M = fmaxf(mh[0], mh[1]);
         float bl = -INFINITY;
         if (M > -INFINITY)
           bl = M + fast_log2(sh[0] * fast_exp2(mh[0] - M) + sh[1] * fast_exp2(mh[1] - M));
         bl = max_row16(bl);
-        if (lane == 0) bl_slot[par][wave] = bl;
+        bl_slot[par][wave] = bl;  // every lane holds the same value
       }
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
     if (OP == kScore) {
       j_prev = j;
       par ^= 1;
@@ -513,6 +538,7 @@ void attn_bf16_kernel(AttnArgs a) {
     step(buf_a, buf_b, t);
     if (t + 1 < t_end) step(buf_b, buf_a, t + 1);
   }
+  __builtin_amdgcn_s_waitcnt(0);  // the last tile's spare copy has landed
 
   if (OP == kScore) {
     __syncthreads();
