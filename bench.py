@@ -295,6 +295,8 @@ def suite_config(c, dev, stream, peaks, oracle_budget):
     calls = {
         "block_score": lambda: hs.hs_block_score_fwd(prob, q, kv, sink, out, lse, bl, w1, stream),
         "topk": lambda: hs.hs_topk_blocks(prob, bl, p.top_k, idx, stream),
+        "score_topk_fused": lambda: hs.hs_block_score_topk_fwd(prob, q, kv, sink, p.top_k, out, lse,
+                                                               bl, idx, w1, stream),
         "sparse_gather": lambda: hs.hs_sparse_gather_fwd(prob, q, kv, sink, idx, p.top_k, out, lse,
                                                          w3, stream),
         "swa": lambda: hs.hs_swa_fwd(prob, q, kv, sink, p.window, out, lse, w4, stream),
@@ -308,6 +310,8 @@ def suite_config(c, dev, stream, peaks, oracle_budget):
         "block_score": (int(causal.sum()) * H * fpp,
                         qb + kv_rows["score"] * p.Dk * es + ob + lb + p.B * p.Sq * NB * 4),
         "topk": (0, p.B * p.Sq * (NB + p.top_k) * 4),
+        "score_topk_fused": (int(causal.sum()) * H * fpp,
+                             qb + kv_rows["score"] * p.Dk * es + ob + lb + p.B * p.Sq * NB * 4),
         "sparse_gather": (int(gather.sum()) * H * fpp,
                           qb + ob + lb + p.B * p.Sq * p.top_k * 4 + int(gather.sum()) * p.Dk * es),
         "swa": (int(window.sum()) * H * fpp, qb + kv_rows["swa"] * p.Dk * es + ob + lb),
@@ -338,6 +342,7 @@ def suite_config(c, dev, stream, peaks, oracle_budget):
     path_ms = rows["block_score"]["ms_warm"] + rows["topk"]["ms_warm"] + rows["sparse_gather"]["ms_warm"]
     res = {"workload": p.name, "dtype": p.dtype, "kernels": rows,
            "metric_path_ms": round(path_ms, 4),
+           "fused_path_ms": round(rows["score_topk_fused"]["ms_warm"] + rows["sparse_gather"]["ms_warm"], 4),
            "tokens_s": round(p.B * p.Sq / (path_ms * 1e-3), 1),
            "metric_tflop_s": round((work["block_score"][0] + work["sparse_gather"][0]) /
                                    (path_ms * 1e-3) / 1e12, 2)}
@@ -389,9 +394,11 @@ def write_suite_md(path, peaks, results, args):
                      f"{v['tflop']:.3f} | {v['gb_alg']:.3f} | {v['bound']} | {ts} | {v['gb_s_alg']:.0f} | "
                      f"{v['frac_vendor']:.3f} | {fm} |")
     L.append("")
-    L.append("Metric path (block score + top-k + gather) and the float64 oracle on the host:\n")
-    L.append("| Workload | Path ms | tokens/s | TFLOP/s | Oracle tokens/s | Oracle rows | Oracle full-run s |")
-    L.append("|---|---|---|---|---|---|---|")
+    L.append("`score_topk_fused` is `hs_block_score_topk_fwd` (block scores and the top-k in one call; "
+             "its work is counted as the block score's). Metric path (block score + top-k + gather; "
+             "with the fused call in place of the first two) and the float64 oracle on the host:\n")
+    L.append("| Workload | Path ms | Path ms, fused | tokens/s | TFLOP/s | Oracle tokens/s | Oracle rows | Oracle full-run s |")
+    L.append("|---|---|---|---|---|---|---|---|")
     for r in results:
         o = r.get("oracle")
         if o:
@@ -403,7 +410,7 @@ def write_suite_md(path, peaks, results, args):
             ofull = f"{o['full_run_s']} ({o['full_run_s_is']})"
         else:
             ot = orow = ofull = "—"
-        L.append(f"| {r['workload']} | {r['metric_path_ms']:.3f} | {r['tokens_s']:.0f} | "
+        L.append(f"| {r['workload']} | {r['metric_path_ms']:.3f} | {r['fused_path_ms']:.3f} | {r['tokens_s']:.0f} | "
                  f"{r['metric_tflop_s']:.1f} | {ot} | {orow} | {ofull} |")
     L.append("")
     with open(path, "w") as f:

@@ -27,8 +27,8 @@ HS_BF16, HS_F32 = 0, 1
 HS_OP_BLOCK_SCORE, HS_OP_SPARSE_GATHER, HS_OP_SWA = 0, 1, 2
 
 EXPORTS = ("hs_num_blocks", "hs_workspace_size", "hs_block_score_fwd", "hs_topk_blocks",
-           "hs_sparse_gather_fwd", "hs_swa_fwd", "hs_status_string", "hs_last_error",
-           "hs_version")
+           "hs_block_score_topk_fwd", "hs_sparse_gather_fwd", "hs_swa_fwd", "hs_status_string",
+           "hs_last_error", "hs_version")
 
 
 class HsProblem(ctypes.Structure):
@@ -68,6 +68,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hs_block_score_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hs_block_score_fwd.restype = i32
     lib.hs_topk_blocks.argtypes, lib.hs_topk_blocks.restype = [P, vp, i32, vp, vp], i32
+    lib.hs_block_score_topk_fwd.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.hs_block_score_topk_fwd.restype = i32
     lib.hs_sparse_gather_fwd.argtypes = [P, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
     lib.hs_sparse_gather_fwd.restype = i32
     lib.hs_swa_fwd.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, sz, vp]
@@ -191,6 +193,17 @@ def hs_topk_blocks(prob, block_logit, top_k, block_idx, stream=None):
                                          _ptr(block_idx), _stream(stream)))
 
 
+def hs_block_score_topk_fwd(prob, q, kv, sink, top_k, out, lse, block_logit, block_idx, ws=None,
+                            stream=None):
+    for n, t in (("q", q), ("kv", kv), ("sink", sink), ("out", out), ("lse", lse),
+                 ("block_logit", block_logit), ("block_idx", block_idx), ("ws", ws)):
+        _dev(n, t)
+    _check(load_library().hs_block_score_topk_fwd(
+        prob.ref, _ptr(q), _ptr(kv), _ptr(sink), int(top_k), _ptr(out), _ptr(lse),
+        _ptr(block_logit), _ptr(block_idx), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
 def hs_sparse_gather_fwd(prob, q, kv, sink, block_idx, top_k, out, lse, ws=None, stream=None):
     for n, t in (("q", q), ("kv", kv), ("sink", sink), ("block_idx", block_idx), ("out", out),
                  ("lse", lse), ("ws", ws)):
@@ -230,6 +243,17 @@ def block_score(prob, q, kv, sink=None, stream=None):
     bl = torch.empty((prob.B, prob.Sq, hs_num_blocks(prob)), dtype=torch.float32, device=q.device)
     hs_block_score_fwd(prob, q, kv, sink, out, lse, bl, _workspace(prob, HS_OP_BLOCK_SCORE), stream)
     return out, lse, bl
+
+
+def block_score_topk(prob, q, kv, sink, top_k, stream=None):
+    import torch
+    out = torch.empty((prob.B, prob.Sq, prob.H, prob.Dv), dtype=_torch_dtype(prob), device=q.device)
+    lse = torch.empty((prob.B, prob.Sq, prob.H), dtype=torch.float32, device=q.device)
+    bl = torch.empty((prob.B, prob.Sq, hs_num_blocks(prob)), dtype=torch.float32, device=q.device)
+    idx = torch.empty((prob.B, prob.Sq, top_k), dtype=torch.int32, device=q.device)
+    hs_block_score_topk_fwd(prob, q, kv, sink, top_k, out, lse, bl, idx,
+                            _workspace(prob, HS_OP_BLOCK_SCORE), stream)
+    return out, lse, bl, idx
 
 
 def topk_blocks(prob, block_logit, top_k, stream=None):

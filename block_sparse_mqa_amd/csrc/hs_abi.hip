@@ -208,9 +208,11 @@ hs_status hip_status(int err, const char* what) {
   return HS_OK;
 }
 
+// sel_idx (score operation only): also select each row's top sel_k blocks.
 hs_status launch_attn(int op, const hs_problem* p, const void* q, const void* kv, const float* sink,
                       const int32_t* block_idx, int32_t top_k, int32_t window, void* out,
-                      float* lse, float* block_logit, void* ws, size_t ws_bytes, void* stream) {
+                      float* lse, float* block_logit, void* ws, size_t ws_bytes, void* stream,
+                      int32_t* sel_idx = nullptr, int32_t sel_k = 0) {
   hs::Geom g;
   hs_status st = prepare(p, g);
   if (st != HS_OK) return st;
@@ -218,6 +220,12 @@ hs_status launch_attn(int op, const hs_problem* p, const void* q, const void* kv
       (st = check_ptr(lse, "lse", 4)))
     return st;
   if (op == HS_OP_BLOCK_SCORE && (st = check_ptr(block_logit, "block_logit", 4))) return st;
+  if (sel_idx != nullptr || sel_k != 0) {
+    if ((st = check_ptr(sel_idx, "block_idx", 4))) return st;
+    if (sel_k < 1) return fail(HS_ERR_INVALID_ARG, "top_k must be >= 1 (got %d)", sel_k);
+    if (sel_k > 64) return fail(HS_ERR_UNSUPPORTED, "top_k %d exceeds 64", sel_k);
+    if (g.NB > 4096) return fail(HS_ERR_UNSUPPORTED, "%d blocks exceed 4096", g.NB);
+  }
   if (op == HS_OP_SPARSE_GATHER) {
     if ((st = check_ptr(block_idx, "block_idx", 4))) return st;
     if (top_k < 1) return fail(HS_ERR_INVALID_ARG, "top_k must be >= 1 (got %d)", top_k);
@@ -259,6 +267,8 @@ hs_status launch_attn(int op, const hs_problem* p, const void* q, const void* kv
     }
     a.page_table = p->page_table;
     a.max_pages = p->page_table ? p->max_pages : 0;
+    a.topk_idx = sel_idx;
+    a.topk_k = sel_k;
     a.g = g;
     return hip_status(hs::attn_bf16_launch(op, a, s), "attention launch");
   }
@@ -274,14 +284,22 @@ hs_status launch_attn(int op, const hs_problem* p, const void* q, const void* kv
   a.top_k = top_k;
   a.window = window;
   a.g = g;
-  return hip_status(hs::attn_f32_launch(op, a, s), "attention launch");
+  st = hip_status(hs::attn_f32_launch(op, a, s), "attention launch");
+  if (st != HS_OK || sel_idx == nullptr) return st;
+  hs::TopkArgs t;
+  std::memset(&t, 0, sizeof(t));
+  t.block_logit = block_logit;
+  t.block_idx = sel_idx;
+  t.top_k = sel_k;
+  t.g = g;
+  return hip_status(hs::topk_launch(t, s), "top-k launch");
 }
 
 }  // namespace
 
 extern "C" {
 
-int32_t hs_version(void) { return 101; }
+int32_t hs_version(void) { return 102; }
 
 const char* hs_status_string(int32_t status) {
   switch (status) {
@@ -318,6 +336,14 @@ hs_status hs_block_score_fwd(const hs_problem* p, const void* q, const void* kv,
                              void* stream) {
   return launch_attn(HS_OP_BLOCK_SCORE, p, q, kv, sink, nullptr, 0, 0, out, lse, block_logit, ws,
                      ws_bytes, stream);
+}
+
+hs_status hs_block_score_topk_fwd(const hs_problem* p, const void* q, const void* kv,
+                                  const float* sink, int32_t top_k, void* out, float* lse,
+                                  float* block_logit, int32_t* block_idx, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  return launch_attn(HS_OP_BLOCK_SCORE, p, q, kv, sink, nullptr, 0, 0, out, lse, block_logit, ws,
+                     ws_bytes, stream, block_idx, top_k);
 }
 
 hs_status hs_sparse_gather_fwd(const hs_problem* p, const void* q, const void* kv,

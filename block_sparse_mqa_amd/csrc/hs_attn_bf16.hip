@@ -61,6 +61,7 @@
 
 #include "hs_common.h"
 #include "hs_kernels.h"
+#include "hs_topk_row.h"
 
 namespace hs {
 
@@ -579,9 +580,19 @@ void attn_bf16_kernel(AttnArgs a) {
   }
 }
 
-// Merge split partials: one wave per (item, head); lane owns 8 columns.
+// Merge split partials: one wave per (item, head); lane owns 8 columns. With
+// PER > 0 the launch has one more wave per row that selects the row's top-k
+// blocks from the complete block scores (PER = ceil(NB / 64)).
+template <int PER>
 __global__ __launch_bounds__(64) void merge_bf16_kernel(AttnArgs a) {
   using namespace mla;
+  if constexpr (PER > 0) {
+    if ((int)blockIdx.x >= a.g.B * a.g.Sq * H) {
+      topk_row<PER>(a.g, a.block_logit, a.topk_idx, a.topk_k, blockIdx.x - a.g.B * a.g.Sq * H,
+                    threadIdx.x);
+      return;
+    }
+  }
   const int item = blockIdx.x / H;
   const int head = blockIdx.x % H;
   const int lane = threadIdx.x;
@@ -645,8 +656,35 @@ int attn_bf16_launch(int op, const AttnArgs& a, hipStream_t stream) {
   // page-table code at all.
   if (a.page_table != nullptr) launch_attn_kernels<true>(op, a, grid, block, stream);
   else launch_attn_kernels<false>(op, a, grid, block, stream);
-  if (a.nsplit > 1)
-    hipLaunchKernelGGL(merge_bf16_kernel, dim3((unsigned)(items * mla::H)), dim3(64), 0, stream, a);
+  if (a.nsplit > 1) {
+    const unsigned waves = (unsigned)(items * mla::H);
+    if (a.topk_idx == nullptr) {
+      hipLaunchKernelGGL(merge_bf16_kernel<0>, dim3(waves), dim3(64), 0, stream, a);
+    } else {
+      // the block scores are complete once the split kernel has finished: the
+      // top-k runs as extra waves of the merge launch
+      const dim3 grid(waves + (unsigned)items);
+      const int NB = a.g.NB;
+      if (NB <= 64) hipLaunchKernelGGL(merge_bf16_kernel<1>, grid, dim3(64), 0, stream, a);
+      else if (NB <= 128) hipLaunchKernelGGL(merge_bf16_kernel<2>, grid, dim3(64), 0, stream, a);
+      else if (NB <= 256) hipLaunchKernelGGL(merge_bf16_kernel<4>, grid, dim3(64), 0, stream, a);
+      else if (NB <= 512) hipLaunchKernelGGL(merge_bf16_kernel<8>, grid, dim3(64), 0, stream, a);
+      else if (NB <= 1024) hipLaunchKernelGGL(merge_bf16_kernel<16>, grid, dim3(64), 0, stream, a);
+      else if (NB <= 2048) hipLaunchKernelGGL(merge_bf16_kernel<32>, grid, dim3(64), 0, stream, a);
+      else hipLaunchKernelGGL(merge_bf16_kernel<64>, grid, dim3(64), 0, stream, a);
+    }
+  } else if (a.topk_idx != nullptr) {
+    // One row per workgroup: the standalone top-k kernel, whose many waves per
+    // CU hide the per-row search latency that an epilogue would expose.
+    TopkArgs t;
+    t.block_logit = a.block_logit;
+    t.block_idx = a.topk_idx;
+    t.top_k = a.topk_k;
+    t.g = a.g;
+    const int err = (int)hipGetLastError();
+    if (err != 0) return err;
+    return topk_launch(t, stream);
+  }
   return (int)hipGetLastError();
 }
 

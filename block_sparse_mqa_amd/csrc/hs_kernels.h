@@ -25,6 +25,8 @@ struct AttnArgs {
   float* ws_ml;              // [items * nsplit, H, 2] fp32 (max, denominator)
   const int* page_table;     // [B, max_pages] page of each key block, or nullptr
   int max_pages;
+  int* topk_idx;             // score operation: [B, Sq, topk_k] selection, or nullptr
+  int topk_k;
   Geom g;
 };
 

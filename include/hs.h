@@ -150,6 +150,21 @@ hs_status hs_block_score_fwd(const hs_problem* p, const void* q, const void* kv,
 hs_status hs_topk_blocks(const hs_problem* p, const float* block_logit, int32_t top_k,
                          int32_t* block_idx, void* stream);
 
+/* Block scores and the per-token top-k in one call: writes exactly what
+ * hs_block_score_fwd followed by hs_topk_blocks writes (out, lse, block_logit
+ * and block_idx [B, Sq, top_k] int32, 4-byte aligned). The selection is fused
+ * into the attention launch sequence, as the page "TileLang CSA compressed
+ * indexer for DSv4" (description, item 2) fuses its indexer's top-k into the
+ * forward: when decode splits the key range, the top-k runs inside the launch
+ * that merges the partial results, once every block score of the row is
+ * final, so the call costs no separate launch; otherwise the top-k kernel
+ * follows the attention kernel on the stream. 1 <= top_k <= 64, at most 4096
+ * blocks; ws/ws_bytes as for hs_block_score_fwd. */
+hs_status hs_block_score_topk_fwd(const hs_problem* p, const void* q, const void* kv,
+                                  const float* sink, int32_t top_k, void* out, float* lse,
+                                  float* block_logit, int32_t* block_idx, void* ws,
+                                  size_t ws_bytes, void* stream);
+
 /* Block-sparse gather attention (same page, "Core", block-sparse DSA gather
  * bullet; per-file table row for block_sparse_mqa_dsa.py): attention with
  * sink over the union of the listed blocks intersected with the allowed keys.

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(hs.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.hs_version() == 101
+    assert lib.hs_version() == 102
 
 
 def _mla(**kw):
@@ -85,6 +85,24 @@ def test_entry_points_reject_before_launch():
     st = lib.hs_block_score_fwd(d.ref, fake, fake, None, fake, fake, fake, None, 0, None)
     assert st == hs.HS_ERR_WORKSPACE
     assert lib.hs_status_string(-2) == b"HS_ERR_UNSUPPORTED"
+
+
+def test_fused_score_topk_rejects_before_launch():
+    lib = hs.load_library()
+    p = _mla()
+    fake = ctypes.c_void_p(4096)
+    call = lambda k, idx, prob=p: lib.hs_block_score_topk_fwd(
+        prob.ref, fake, fake, None, k, fake, fake, fake, idx, None, 0, None)
+    assert call(0, fake) == hs.HS_ERR_INVALID_ARG and b"top_k" in lib.hs_last_error()
+    assert call(65, fake) == hs.HS_ERR_UNSUPPORTED
+    assert call(4, None) == hs.HS_ERR_INVALID_ARG and b"block_idx is NULL" in lib.hs_last_error()
+    assert call(4, ctypes.c_void_p(4098)) == hs.HS_ERR_INVALID_ARG
+    # more than 4096 blocks cannot be selected from
+    big = _mla(B=1, Sq=1, Skv=4097 * 64, kv_lens=[4097 * 64])
+    assert call(4, fake, big) == hs.HS_ERR_UNSUPPORTED and b"4096" in lib.hs_last_error()
+    # split decode without its workspace
+    d = _mla(B=2, Sq=1, Skv=4096, kv_lens=[4096, 2000])
+    assert call(4, fake, d) == hs.HS_ERR_WORKSPACE
 
 
 @pytest.mark.parametrize("case", [
