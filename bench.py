@@ -373,7 +373,8 @@ def write_suite_md(path, peaks, results, args):
     L = ["# Per-workload measurements (all kernels, warm and cold)\n",
          "Command (from the repository root, on one MI355X):\n",
          "```\npython3 bench.py --suite --suite-md " + os.path.relpath(path, ROOT) +
-         f" --oracle-budget {args.oracle_budget:g}\n```\n",
+         (" --oracle-full" if args.oracle_full else f" --oracle-budget {args.oracle_budget:g}") +
+         "\n```\n",
          f"Attainable peaks measured by the probe kernels (`include/hs_probe.h`): dense bf16 MFMA "
          f"{peaks['mfma_bf16_tflop_s']:.0f} TFLOP/s ({peaks['mfma_probe']}; shader clock while it ran: "
          f"{peaks['shader_clock_ghz_under_mfma']} GHz by s_memtime against the 100 MHz reference); copy "
@@ -436,7 +437,12 @@ def main():
     ap.add_argument("--suite-md", default=None, help="also write the suite as a markdown table")
     ap.add_argument("--oracle-budget", type=float, default=20.0,
                     help="seconds of oracle time per workload in the suite (0 = skip)")
+    ap.add_argument("--oracle-full", action="store_true",
+                    help="suite: run the oracle over every row of every workload (no sampling; "
+                         "the S=32768 workload takes about an hour on 16 cores)")
     args = ap.parse_args()
+    if args.oracle_full:
+        args.oracle_budget = float("inf")
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the path is built and measured on a single "

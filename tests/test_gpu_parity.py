@@ -94,6 +94,19 @@ def test_config2_full():
     say(f"[gpu] S=4096: {res}")
 
 
+def test_tail_tile_S4097_sampled():
+    """S = 4097 (a one-row tail block after 64 full blocks) in the launch that
+    does not split the key range, at the absorbed-MLA shape: sampled rows,
+    including the tail row and the rows around every block edge."""
+    say("[gpu] S=4097 one-row tail block, sampled rows")
+    p = inputs.make(1, 4097, 4097, MLA["H"], MLA["Dk"], MLA["Dv"], seed=18, top_k=16,
+                    window=512, name="S4097_tail")
+    rows = sample_rows(p, 200, seed=18)
+    assert rows[-1] == 4096
+    res = _run_all(Dev(p), rows=rows)
+    say(f"[gpu] S=4097: {res}")
+
+
 def test_config4_packed_documents_sampled():
     say("[gpu] packed 8-document S=16384, sampled rows")
     p = inputs.config(4)
