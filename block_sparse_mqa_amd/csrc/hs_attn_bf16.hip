@@ -204,8 +204,9 @@ template <int OP, bool SPLIT, bool PAGED>
 __global__ __launch_bounds__(mla::NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_bf16_kernel(AttnArgs a) {
   using namespace mla;
-  // Two separate buffers (not one array with a computed offset) so that the
-  // compiler can prove a tile copy in flight never aliases the tile being read.
+  // Two separate buffers (not one array with a computed offset): each of the
+  // two unrolled step instances reads its tile at compile-time addresses (one
+  // array indexed at run time measured about 3 % slower).
   __shared__ __attribute__((aligned(16))) char buf_a[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char buf_b[TILE_BYTES];
   __shared__ float bl_slot[2][NW];
