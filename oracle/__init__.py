@@ -1,4 +1,4 @@
-"""CPU oracle for the HySparse MQA sparse-attention forward path.
+"""CPU oracle for the HySparse MQA sparse-attention path (forward and gradients).
 
 TEST INFRASTRUCTURE ONLY. This package is a plain, slow, float64 statement of
 what the path computes. Only the tests, the smoke entry point and the
@@ -16,4 +16,7 @@ from .hysparse_ref import (  # noqa: F401
     swa,
     attend_subset,
     merge_partials,
+    block_score_bwd,
+    sparse_gather_bwd,
+    swa_bwd,
 )

@@ -1,4 +1,5 @@
-"""Float64 reference of the HySparse MQA forward path (test infrastructure only).
+"""Float64 reference of the HySparse MQA path: the forward operations and the
+gradients of the three attention operations (test infrastructure only).
 
 Sources (the pages this restates, cited by title and section):
 
@@ -207,25 +208,16 @@ def _row_chunks(rows: np.ndarray, chunk: int):
         yield rows[i:i + chunk]
 
 
-def _op(kind, q, kv, sink, Dv, scale, block_size, kv_lens=None, doc_start=None,
-        doc_end=None, window=None, block_idx=None, rows=None, chunk=None):
-    """Shared driver: for each batch entry and chunk of query rows, build the
-    allowed-key mask of the requested operation and attend over it."""
-    q, kv, sk = _prepare(q, kv, sink, Dv)
-    B, Sq, H, Dk = q.shape
-    Skv = kv.shape[1]
-    rows_sel = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
+def _chunk_masks(kind, B, Sq, Skv, H, block_size, kv_lens, doc_start, doc_end, window,
+                 block_idx, rows_sel, chunk):
+    """Allowed-key masks of the requested operation, one chunk of query rows
+    at a time: yields (b, rr, L, kmin, kmax, allowed [len(rr), kmax-kmin],
+    block id of each key in [kmin, kmax))."""
     R = len(rows_sel)
-    NB = num_blocks(B, Skv, block_size, kv_lens, doc_start, doc_end)
-    out = np.zeros((B, R, H, Dv))
-    lse = np.full((B, R, H), NEG_INF)
-    blog = np.full((B, R, NB), NEG_INF) if kind == "score" else None
     for b in range(B):
         L = _valid_len(b, Skv, kv_lens)
         bt = block_table(L, block_size, doc_start, doc_end)
         blk_of_key = bt.block_of_key(L)
-        k = _to64(kv[b, :L])
-        v = k[:, :Dv]
         # Bound the [rows, H, keys] float64 score array to about 2e7 entries.
         ch = chunk or max(1, int(2e7 // (H * max(1, L))))
         for rr in _row_chunks(np.arange(R), ch):
@@ -246,24 +238,47 @@ def _op(kind, q, kv, sink, Dv, scale, block_size, kv_lens=None, doc_start=None,
                     ok = (j >= 0) & (j < bt.nb)
                     member |= ok[:, None] & (kb[None, :] == j[:, None])
                 allowed &= member
-            s = _scores(_to64(q[b, rows_sel[rr]]), k[kmin:kmax], scale)
-            o, ls = _attend_masked(s, allowed, v[kmin:kmax], sk)
-            out[b, rr] = o
-            lse[b, rr] = ls
-            if kind == "score":
-                # block_logit[p, j] = max_h ln sum_{i in blk j, i in A(p)} exp(s[h, i])
-                kb = blk_of_key[kmin:kmax]
-                for j in np.unique(kb):
-                    cols = kb == j
-                    a = allowed[:, cols]                      # [r, n_j]
-                    sj = np.where(a[:, None, :], s[:, :, cols], NEG_INF)
-                    mj = sj.max(axis=2)                       # [r, H]
-                    fin = np.isfinite(mj)
-                    mjs = np.where(fin, mj, 0.0)
-                    with np.errstate(divide="ignore"):
-                        lj = np.where(fin, mjs + np.log(np.exp(sj - mjs[:, :, None]).sum(axis=2)),
-                                      NEG_INF)
-                    blog[b, rr, j] = lj.max(axis=1)
+            yield b, rr, L, kmin, kmax, allowed, blk_of_key[kmin:kmax]
+
+
+def _op(kind, q, kv, sink, Dv, scale, block_size, kv_lens=None, doc_start=None,
+        doc_end=None, window=None, block_idx=None, rows=None, chunk=None):
+    """Shared driver: for each batch entry and chunk of query rows, build the
+    allowed-key mask of the requested operation and attend over it."""
+    q, kv, sk = _prepare(q, kv, sink, Dv)
+    B, Sq, H, Dk = q.shape
+    Skv = kv.shape[1]
+    rows_sel = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = len(rows_sel)
+    NB = num_blocks(B, Skv, block_size, kv_lens, doc_start, doc_end)
+    out = np.zeros((B, R, H, Dv))
+    lse = np.full((B, R, H), NEG_INF)
+    blog = np.full((B, R, NB), NEG_INF) if kind == "score" else None
+    k_entry, k_b = None, -1
+    for b, rr, L, kmin, kmax, allowed, kb in _chunk_masks(
+            kind, B, Sq, Skv, H, block_size, kv_lens, doc_start, doc_end, window, block_idx,
+            rows_sel, chunk):
+        if b != k_b:
+            k_entry, k_b = _to64(kv[b, :L]), b
+        k = k_entry
+        v = k[:, :Dv]
+        s = _scores(_to64(q[b, rows_sel[rr]]), k[kmin:kmax], scale)
+        o, ls = _attend_masked(s, allowed, v[kmin:kmax], sk)
+        out[b, rr] = o
+        lse[b, rr] = ls
+        if kind == "score":
+            # block_logit[p, j] = max_h ln sum_{i in blk j, i in A(p)} exp(s[h, i])
+            for j in np.unique(kb):
+                cols = kb == j
+                a = allowed[:, cols]                          # [r, n_j]
+                sj = np.where(a[:, None, :], s[:, :, cols], NEG_INF)
+                mj = sj.max(axis=2)                           # [r, H]
+                fin = np.isfinite(mj)
+                mjs = np.where(fin, mj, 0.0)
+                with np.errstate(divide="ignore"):
+                    lj = np.where(fin, mjs + np.log(np.exp(sj - mjs[:, :, None]).sum(axis=2)),
+                                  NEG_INF)
+                blog[b, rr, j] = lj.max(axis=1)
     return out, lse, blog
 
 
@@ -296,6 +311,92 @@ def sparse_gather(q, kv, sink, Dv, scale, block_idx, block_size=64, kv_lens=None
     out, lse, _ = _op("gather", q, kv, sink, Dv, scale, block_size, kv_lens, doc_start,
                       doc_end, block_idx=bi, rows=rows)
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# Gradients of the three attention operations.
+# ---------------------------------------------------------------------------
+def _op_bwd(kind, q, kv, sink, Dv, scale, dout, block_size, kv_lens=None, doc_start=None,
+            doc_end=None, window=None, block_idx=None, chunk=None):
+    """Gradients of L = sum(dout * out) for one attention operation.
+
+    The pages train through these kernels: page "HySparse MQA sparse attention
+    ...", section "Core" (block scoring with gradients routed through the
+    autograd layer, the analytic gradient of the learnable per-head sink) and
+    the per-file table rows for windowed_mqa_attn*.py and
+    block_sparse_mqa_dsa.py (forward and backward kernels); review of
+    PaddleFleet PR 1453, block-score PyLayer comments (the backward returns
+    gradients for q, k and v only: block_logit and the block table get none).
+
+    For one row and head, with P_i = exp(s_i - lse) over the allowed set,
+    P_sink = exp(sigma - lse) and out = sum_i P_i v_i, the chain rule gives
+        dP_i  = dout . v_i,          Dsum = dout . out = sum_i P_i dP_i,
+        dL/ds_i    = P_i (dP_i - Dsum),
+        dL/dsigma  = -P_sink Dsum   (the sink enters the normaliser only),
+    and through s_i = scale q . k_i:
+        dq   = scale sum_i dL/ds_i k_i,
+        dk_i = scale sum_{rows, heads} dL/ds_i q,   dv_i = sum_{rows, heads} P_i dout.
+    The latent row kv_i serves as both key and value (value = its leading Dv
+    columns), so dkv_i = dk_i + [dv_i, 0]. Reading: lse receives no incoming
+    gradient (it is a saved statistic of the forward). Returns dq [B,Sq,H,Dk],
+    dkv [B,Skv,Dk] (zero past each entry's valid length) and dsink [H]
+    (None without a sink)."""
+    q, kv, sk = _prepare(q, kv, sink, Dv)
+    B, Sq, H, Dk = q.shape
+    Skv = kv.shape[1]
+    g_all = dout
+    dq = np.zeros((B, Sq, H, Dk))
+    dkv = np.zeros((B, Skv, Dk))
+    dsink = None if sk is None else np.zeros(H)
+    rows_sel = np.arange(Sq)
+    k_entry, k_b = None, -1
+    for b, rr, L, kmin, kmax, allowed, _ in _chunk_masks(
+            kind, B, Sq, Skv, H, block_size, kv_lens, doc_start, doc_end, window, block_idx,
+            rows_sel, chunk):
+        if b != k_b:
+            k_entry, k_b = _to64(kv[b, :L]), b
+        k = k_entry[kmin:kmax]
+        v = k[:, :Dv]
+        qr = _to64(q[b, rr])                                  # [r, H, Dk]
+        g = _to64(g_all[b, rr])                               # [r, H, Dv]
+        s = _scores(qr, k, scale)                             # [r, H, n]
+        out, lse = _attend_masked(s, allowed, v, sk)
+        fin = np.isfinite(lse)
+        lse_s = np.where(fin, lse, 0.0)
+        P = np.where(allowed[:, None, :] & fin[:, :, None], np.exp(s - lse_s[:, :, None]), 0.0)
+        dP = np.einsum("rhd,id->rhi", g, v, optimize=True)
+        Dsum = np.einsum("rhd,rhd->rh", g, out, optimize=True)
+        dS = P * (dP - Dsum[:, :, None])
+        dq[b, rr] = scale * np.einsum("rhi,id->rhd", dS, k, optimize=True)
+        dkv[b, kmin:kmax] += scale * np.einsum("rhi,rhd->id", dS, qr, optimize=True)
+        dkv[b, kmin:kmax, :Dv] += np.einsum("rhi,rhd->id", P, g, optimize=True)
+        if dsink is not None:
+            psink = np.where(fin, np.exp(sk[None, :] - lse_s), 0.0)
+            dsink -= (psink * Dsum).sum(axis=0)
+    return dq, dkv, dsink
+
+
+def block_score_bwd(q, kv, sink, Dv, scale, dout, block_size=64, kv_lens=None,
+                    doc_start=None, doc_end=None, chunk=None):
+    """Gradients of the causal attention of block_score (block_logit has none)."""
+    return _op_bwd("score", q, kv, sink, Dv, scale, dout, block_size, kv_lens, doc_start,
+                   doc_end, chunk=chunk)
+
+
+def swa_bwd(q, kv, sink, Dv, scale, window, dout, block_size=64, kv_lens=None,
+            doc_start=None, doc_end=None, chunk=None):
+    """Gradients of the sliding-window attention."""
+    return _op_bwd("swa", q, kv, sink, Dv, scale, dout, block_size, kv_lens, doc_start,
+                   doc_end, window=window, chunk=chunk)
+
+
+def sparse_gather_bwd(q, kv, sink, Dv, scale, block_idx, dout, block_size=64, kv_lens=None,
+                      doc_start=None, doc_end=None, chunk=None):
+    """Gradients of the block-sparse gather attention for a fixed selection."""
+    bi = np.asarray(block_idx.cpu() if hasattr(block_idx, "cpu") else block_idx,
+                    dtype=np.int64)
+    return _op_bwd("gather", q, kv, sink, Dv, scale, dout, block_size, kv_lens, doc_start,
+                   doc_end, block_idx=bi, chunk=chunk)
 
 
 def own_blocks(B, Sq, Skv, block_size, kv_lens=None, doc_start=None, doc_end=None,
