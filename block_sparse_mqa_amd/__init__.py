@@ -1,16 +1,19 @@
 """Python binding of libhysparse.so, the HIP (gfx950) library of the HySparse
-MQA sparse-attention forward path.
+MQA sparse-attention path (forward operations and their gradients).
 
 The entry points mirror the C ABI of ``include/hs.h`` one to one
-(``hs_block_score_fwd``, ``hs_topk_blocks``, ``hs_sparse_gather_fwd``,
-``hs_swa_fwd``, ``hs_num_blocks``, ``hs_workspace_size``). They only marshal
+(``hs_block_score_fwd``, ``hs_topk_blocks``, ``hs_block_score_topk_fwd``,
+``hs_sparse_gather_fwd``, ``hs_swa_fwd``, the gradients ``hs_block_score_bwd``,
+``hs_sparse_gather_bwd`` and ``hs_swa_bwd``, ``hs_num_blocks``,
+``hs_workspace_size``). They only marshal
 arguments: tensors are device buffers owned by the caller (PyTorch provides
 memory and the current stream), and every step of the computation runs in the
 library's kernels. There is no fallback: if the library is missing, or an
 argument is rejected, the call raises.
 
-The convenience functions ``block_score``, ``topk_blocks``, ``sparse_gather``
-and ``swa`` allocate the outputs (and any workspace) with PyTorch and call the
+The convenience functions ``block_score``, ``topk_blocks``, ``sparse_gather``,
+``swa`` and the gradient functions ``block_score_bwd``, ``sparse_gather_bwd``
+and ``swa_bwd`` allocate the outputs (and any workspace) with PyTorch and call the
 entry points above.
 """
 from __future__ import annotations
@@ -25,9 +28,11 @@ LIB_PATH = os.path.join(HERE, "libhysparse.so")
 HS_OK, HS_ERR_INVALID_ARG, HS_ERR_UNSUPPORTED, HS_ERR_HIP, HS_ERR_WORKSPACE = 0, -1, -2, -3, -4
 HS_BF16, HS_F32 = 0, 1
 HS_OP_BLOCK_SCORE, HS_OP_SPARSE_GATHER, HS_OP_SWA = 0, 1, 2
+HS_OP_BLOCK_SCORE_BWD, HS_OP_SPARSE_GATHER_BWD, HS_OP_SWA_BWD = 3, 4, 5
 
 EXPORTS = ("hs_num_blocks", "hs_workspace_size", "hs_block_score_fwd", "hs_topk_blocks",
-           "hs_block_score_topk_fwd", "hs_sparse_gather_fwd", "hs_swa_fwd", "hs_status_string",
+           "hs_block_score_topk_fwd", "hs_sparse_gather_fwd", "hs_swa_fwd",
+           "hs_block_score_bwd", "hs_sparse_gather_bwd", "hs_swa_bwd", "hs_status_string",
            "hs_last_error", "hs_version")
 
 
@@ -74,6 +79,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hs_sparse_gather_fwd.restype = i32
     lib.hs_swa_fwd.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, sz, vp]
     lib.hs_swa_fwd.restype = i32
+    lib.hs_block_score_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hs_block_score_bwd.restype = i32
+    lib.hs_sparse_gather_bwd.argtypes = [P, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz,
+                                         vp]
+    lib.hs_sparse_gather_bwd.restype = i32
+    lib.hs_swa_bwd.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hs_swa_bwd.restype = i32
     lib.hs_status_string.argtypes, lib.hs_status_string.restype = [i32], ctypes.c_char_p
     lib.hs_last_error.argtypes, lib.hs_last_error.restype = [], ctypes.c_char_p
     lib.hs_version.argtypes, lib.hs_version.restype = [], i32
@@ -222,6 +234,40 @@ def hs_swa_fwd(prob, q, kv, sink, window, out, lse, ws=None, stream=None):
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def _nbytes(ws) -> int:
+    return 0 if ws is None else ws.numel() * ws.element_size()
+
+
+def hs_block_score_bwd(prob, q, kv, sink, out, lse, dout, dq, dkv, dsink, ws, stream=None):
+    for n, t in (("q", q), ("kv", kv), ("sink", sink), ("out", out), ("lse", lse),
+                 ("dout", dout), ("dq", dq), ("dkv", dkv), ("dsink", dsink), ("ws", ws)):
+        _dev(n, t)
+    _check(load_library().hs_block_score_bwd(
+        prob.ref, _ptr(q), _ptr(kv), _ptr(sink), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
+        _ptr(dkv), _ptr(dsink), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def hs_sparse_gather_bwd(prob, q, kv, sink, block_idx, top_k, out, lse, dout, dq, dkv, dsink,
+                         ws, stream=None):
+    for n, t in (("q", q), ("kv", kv), ("sink", sink), ("block_idx", block_idx), ("out", out),
+                 ("lse", lse), ("dout", dout), ("dq", dq), ("dkv", dkv), ("dsink", dsink),
+                 ("ws", ws)):
+        _dev(n, t)
+    _check(load_library().hs_sparse_gather_bwd(
+        prob.ref, _ptr(q), _ptr(kv), _ptr(sink), _ptr(block_idx), int(top_k), _ptr(out),
+        _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dkv), _ptr(dsink), _ptr(ws), _nbytes(ws),
+        _stream(stream)))
+
+
+def hs_swa_bwd(prob, q, kv, sink, window, out, lse, dout, dq, dkv, dsink, ws, stream=None):
+    for n, t in (("q", q), ("kv", kv), ("sink", sink), ("out", out), ("lse", lse),
+                 ("dout", dout), ("dq", dq), ("dkv", dkv), ("dsink", dsink), ("ws", ws)):
+        _dev(n, t)
+    _check(load_library().hs_swa_bwd(
+        prob.ref, _ptr(q), _ptr(kv), _ptr(sink), int(window), _ptr(out), _ptr(lse), _ptr(dout),
+        _ptr(dq), _ptr(dkv), _ptr(dsink), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
 # ---------------------------------------------------------------------------
 # Convenience wrappers: allocate outputs with PyTorch, then call the above.
 # ---------------------------------------------------------------------------
@@ -279,3 +325,36 @@ def swa(prob, q, kv, sink, window, stream=None):
     hs_swa_fwd(prob, q, kv, sink, window, out, lse, _workspace(prob, HS_OP_SWA, window=window),
                stream)
     return out, lse
+
+
+def _grad_buffers(prob, q, sink):
+    import torch
+    dq = torch.empty((prob.B, prob.Sq, prob.H, prob.Dk), dtype=torch.float32, device=q.device)
+    dkv = torch.empty((prob.B, prob.Skv, prob.Dk), dtype=torch.float32, device=q.device)
+    dsink = None if sink is None else torch.empty((prob.H,), dtype=torch.float32, device=q.device)
+    return dq, dkv, dsink
+
+
+def block_score_bwd(prob, q, kv, sink, out, lse, dout, stream=None):
+    """Gradients (dq, dkv, dsink) of the causal attention of block_score;
+    dsink is None without a sink. All float32."""
+    dq, dkv, dsink = _grad_buffers(prob, q, sink)
+    hs_block_score_bwd(prob, q, kv, sink, out, lse, dout, dq, dkv, dsink,
+                       _workspace(prob, HS_OP_BLOCK_SCORE_BWD), stream)
+    return dq, dkv, dsink
+
+
+def sparse_gather_bwd(prob, q, kv, sink, block_idx, top_k, out, lse, dout, stream=None):
+    """Gradients (dq, dkv, dsink) of sparse_gather for the given selection."""
+    dq, dkv, dsink = _grad_buffers(prob, q, sink)
+    hs_sparse_gather_bwd(prob, q, kv, sink, block_idx, top_k, out, lse, dout, dq, dkv, dsink,
+                         _workspace(prob, HS_OP_SPARSE_GATHER_BWD, top_k=top_k), stream)
+    return dq, dkv, dsink
+
+
+def swa_bwd(prob, q, kv, sink, window, out, lse, dout, stream=None):
+    """Gradients (dq, dkv, dsink) of swa."""
+    dq, dkv, dsink = _grad_buffers(prob, q, sink)
+    hs_swa_bwd(prob, q, kv, sink, window, out, lse, dout, dq, dkv, dsink,
+               _workspace(prob, HS_OP_SWA_BWD, window=window), stream)
+    return dq, dkv, dsink

@@ -18,13 +18,14 @@ LIB = os.path.join(HERE, "libhysparse.so")
 PROBE_LIB = os.path.join(HERE, "libhsprobe.so")
 PROBE_SOURCES = ["hs_probe.hip"]
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["hs_abi.hip", "hs_attn_bf16.hip", "hs_attn_f32.hip", "hs_topk.hip"]
+SOURCES = ["hs_abi.hip", "hs_attn_bf16.hip", "hs_attn_f32.hip", "hs_topk.hip", "hs_bwd.hip"]
 # Per-source extra flags. The bf16 engine keeps its MFMA accumulators in
 # VGPRs so that the O rescale and epilogue need no AGPR<->VGPR copies; Q and
 # other long-lived operands then go to AGPRs, which MFMA reads directly. Its
 # inputs are finite by contract, so max reductions need no NaN quieting
 # (-fno-honor-nans drops a canonicalising v_max per reduction step).
 EXTRA = {"hs_attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
+         "hs_bwd.hip": ["-fno-honor-nans"],
          "hs_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -56,7 +57,7 @@ def _link(objs, lib: str) -> None:
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     srcs = SOURCES + PROBE_SOURCES
-    with ThreadPoolExecutor(max_workers=min(5, len(srcs))) as ex:
+    with ThreadPoolExecutor(max_workers=min(6, len(srcs))) as ex:
         objs = dict(zip(srcs, ex.map(_compile, srcs)))
     _link([objs[s] for s in SOURCES], LIB)
     _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)

@@ -295,11 +295,87 @@ hs_status launch_attn(int op, const hs_problem* p, const void* q, const void* kv
   return hip_status(hs::topk_launch(t, s), "top-k launch");
 }
 
+// Gradients of one attention operation (op: HS_OP_BLOCK_SCORE, _SPARSE_GATHER
+// or _SWA; the matching _BWD workspace).
+hs_status launch_bwd(int op, const hs_problem* p, const void* q, const void* kv,
+                     const float* sink, const int32_t* block_idx, int32_t top_k, int32_t window,
+                     const void* out, const float* lse, const void* dout, float* dq, float* dkv,
+                     float* dsink, void* ws, size_t ws_bytes, void* stream) {
+  hs::Geom g;
+  hs_status st = prepare(p, g);
+  if (st != HS_OK) return st;
+  if (p->page_table || p->kv_lens_device)
+    return fail(HS_ERR_UNSUPPORTED, "gradients take a contiguous kv with host lengths (no paged KV)");
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(kv, "kv")) || (st = check_ptr(out, "out")) ||
+      (st = check_ptr(lse, "lse", 4)) || (st = check_ptr(dout, "dout")) ||
+      (st = check_ptr(dq, "dq")) || (st = check_ptr(dkv, "dkv")))
+    return st;
+  if (sink && reinterpret_cast<uintptr_t>(sink) % 4 != 0)
+    return fail(HS_ERR_INVALID_ARG, "sink is not 4-byte aligned");
+  if (dsink) {
+    if (!sink) return fail(HS_ERR_INVALID_ARG, "dsink is set but there is no sink");
+    if ((st = check_ptr(dsink, "dsink", 4))) return st;
+  }
+  if (op == HS_OP_SPARSE_GATHER) {
+    if ((st = check_ptr(block_idx, "block_idx", 4))) return st;
+    if (top_k < 1) return fail(HS_ERR_INVALID_ARG, "top_k must be >= 1 (got %d)", top_k);
+    if (top_k > 64) return fail(HS_ERR_UNSUPPORTED, "top_k %d exceeds 64", top_k);
+    if ((long)g.B * g.Sq * top_k > 0x7fffffffL)
+      return fail(HS_ERR_UNSUPPORTED, "batch * seqlen_q * top_k exceeds 2^31 - 1");
+    if (g.NB > 4096) return fail(HS_ERR_UNSUPPORTED, "%d blocks exceed 4096", g.NB);
+  }
+  if (op == HS_OP_SWA && window < 1)
+    return fail(HS_ERR_INVALID_ARG, "window must be >= 1 (got %d)", window);
+  const bool bf16 = p->dtype == HS_BF16;
+  const int kop = op == HS_OP_SWA ? hs::kSwa : op == HS_OP_SPARSE_GATHER ? hs::kGather : hs::kScore;
+  const hs::BwdLayout L = hs::bwd_layout(g, kop, top_k, window, bf16);
+  if (!ws || ws_bytes < L.total)
+    return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", L.total,
+                ws ? ws_bytes : (size_t)0);
+  if (reinterpret_cast<uintptr_t>(ws) % 16 != 0)
+    return fail(HS_ERR_WORKSPACE, "workspace is not 16-byte aligned");
+  char* w = static_cast<char*>(ws);
+  hs::BwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.kv = kv;
+  a.sink = sink;
+  a.out = out;
+  a.lse = lse;
+  a.dout = dout;
+  a.block_idx = block_idx;
+  a.top_k = top_k;
+  a.window = window;
+  a.dq = dq;
+  a.dkv = dkv;
+  a.dsink = dsink;
+  a.dsum = reinterpret_cast<float*>(w + L.dsum);
+  a.sink_part = reinterpret_cast<float*>(w + L.sink_part);
+  a.n_pre = L.n_pre;
+  a.rows_per_pre = L.rows_per_pre;
+  if (bf16) {
+    a.plan_first = reinterpret_cast<int*>(w + L.first);
+    a.plan_nrows = reinterpret_cast<int*>(w + L.nrows);
+    a.plan_pre = reinterpret_cast<int*>(w + L.pre);
+    if (kop == hs::kGather) {
+      a.g_cnt = reinterpret_cast<int*>(w + L.cnt);
+      a.g_rows = reinterpret_cast<int*>(w + L.rows);
+    }
+    a.part = reinterpret_cast<float*>(w + L.part);
+    a.chunk_rows = L.chunk_rows;
+    a.items = L.items;
+    a.row_tiles = L.row_tiles;
+  }
+  a.g = g;
+  return hip_status(hs::bwd_launch(kop, a, bf16, static_cast<hipStream_t>(stream)),
+                    "gradient launch");
+}
+
 }  // namespace
 
 extern "C" {
 
-int32_t hs_version(void) { return 102; }
+int32_t hs_version(void) { return 103; }
 
 const char* hs_status_string(int32_t status) {
   switch (status) {
@@ -326,7 +402,17 @@ hs_status hs_workspace_size(const hs_problem* p, int32_t op, int32_t top_k, int3
   hs_status st = prepare(p, g);
   if (st != HS_OK) return st;
   if (!bytes) return fail(HS_ERR_INVALID_ARG, "bytes is NULL");
-  if (op < HS_OP_BLOCK_SCORE || op > HS_OP_SWA) return fail(HS_ERR_INVALID_ARG, "unknown op %d", op);
+  if (op < HS_OP_BLOCK_SCORE || op > HS_OP_SWA_BWD) return fail(HS_ERR_INVALID_ARG, "unknown op %d", op);
+  if (op >= HS_OP_BLOCK_SCORE_BWD) {
+    const int kop = op == HS_OP_SWA_BWD ? hs::kSwa : op == HS_OP_SPARSE_GATHER_BWD ? hs::kGather
+                                                                                  : hs::kScore;
+    if (kop == hs::kGather && (top_k < 1 || top_k > 64))
+      return fail(HS_ERR_INVALID_ARG, "top_k must be in 1..64 (got %d)", top_k);
+    if (kop == hs::kSwa && window < 1)
+      return fail(HS_ERR_INVALID_ARG, "window must be >= 1 (got %d)", window);
+    *bytes = hs::bwd_layout(g, kop, top_k, window, p->dtype == HS_BF16).total;
+    return HS_OK;
+  }
   *bytes = p->dtype == HS_BF16 ? split_ws_bytes(g, plan_split(g, op, top_k, window).nsplit) : 0;
   return HS_OK;
 }
@@ -377,6 +463,30 @@ hs_status hs_topk_blocks(const hs_problem* p, const float* block_logit, int32_t 
   a.top_k = top_k;
   a.g = g;
   return hip_status(hs::topk_launch(a, static_cast<hipStream_t>(stream)), "top-k launch");
+}
+
+hs_status hs_block_score_bwd(const hs_problem* p, const void* q, const void* kv, const float* sink,
+                             const void* out, const float* lse, const void* dout, float* dq,
+                             float* dkv, float* dsink, void* ws, size_t ws_bytes, void* stream) {
+  return launch_bwd(HS_OP_BLOCK_SCORE, p, q, kv, sink, nullptr, 0, 0, out, lse, dout, dq, dkv,
+                    dsink, ws, ws_bytes, stream);
+}
+
+hs_status hs_sparse_gather_bwd(const hs_problem* p, const void* q, const void* kv,
+                               const float* sink, const int32_t* block_idx, int32_t top_k,
+                               const void* out, const float* lse, const void* dout, float* dq,
+                               float* dkv, float* dsink, void* ws, size_t ws_bytes,
+                               void* stream) {
+  return launch_bwd(HS_OP_SPARSE_GATHER, p, q, kv, sink, block_idx, top_k, 0, out, lse, dout, dq,
+                    dkv, dsink, ws, ws_bytes, stream);
+}
+
+hs_status hs_swa_bwd(const hs_problem* p, const void* q, const void* kv, const float* sink,
+                     int32_t window, const void* out, const float* lse, const void* dout,
+                     float* dq, float* dkv, float* dsink, void* ws, size_t ws_bytes,
+                     void* stream) {
+  return launch_bwd(HS_OP_SWA, p, q, kv, sink, nullptr, 0, window, out, lse, dout, dq, dkv, dsink,
+                    ws, ws_bytes, stream);
 }
 
 }  // extern "C"

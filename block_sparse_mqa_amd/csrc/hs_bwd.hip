@@ -1,0 +1,936 @@
+// Gradients of the three attention operations of the HySparse MQA path:
+// causal attention (the attention half of the block-score operation),
+// block-sparse gather attention and sliding-window attention, each with the
+// optional learnable per-head sink (page "HySparse MQA sparse attention (FA4
+// block scoring + SWA MQA + block-sparse DSA gather)", section "Core": block
+// scoring with gradients routed through the autograd layer, the analytic
+// gradient of the sink; per-file table rows for windowed_mqa_attn*.py and
+// block_sparse_mqa_dsa.py). The block scores take no gradient (review of
+// PaddleFleet PR 1453, block-score PyLayer comments: the backward returns
+// gradients for q, k and v only).
+//
+// For one row and head, with P_i = exp(s_i - lse) and Dsum = dout . out:
+//   dS_i = P_i (dout . v_i - Dsum),           dq = scale sum_i dS_i k_i,
+//   dkv_i += scale dS_i q + [P_i dout, 0],    dsink = -sum_rows exp(sigma - lse) Dsum
+// (the latent row is both key and value: its key and value gradients add).
+//
+// Launch sequence (one stream):
+//   pre     : Dsum per (row, head) and per-workgroup sink partials
+//   sink    : fixed-order sum of the partials (when a sink gradient is asked)
+//   plan    : rows reaching each key block, split into work items (the gather
+//             first counts and lists, per block, the rows that selected it)
+//   dq      : one workgroup per query row, walking the row's key tiles
+//   dkv     : one workgroup per (key block, chunk of rows): partial gradients
+//   reduce  : fixed-order sum of each block's partials into dkv
+// Every workspace word is written before it is read (no memset), and every
+// sum runs in a fixed order, so results are reproducible bit for bit.
+//
+// bf16 MFMA kernels (absorbed-MLA shape H = 64, Dk = 576, Dv = 512; page
+// above, section "FlashMLA sparse kernel constraints"). The 16x16x32 bf16
+// MFMA contracts 32 along k; lane l holds A[l%16][8(l/16)..+8],
+// B[8(l/16)..+8][l%16] and D[4(l/16)..+4][l%16].
+//   dq kernel (wave w owns heads 16w..16w+15, Q and dout rows in registers):
+//     S^T[key, head]  = K_tile . Q^T    (A = K from LDS, B = Q)
+//     dP^T[key, head] = V_tile . dout^T (the same K fragments: V is the
+//                       leading 512 columns of the latent row)
+//     dQ^T[dim, head] += K^T . dS^T     (A = K^T by LDS transpose reads,
+//                       B = dS^T straight from the S^T registers; inside each
+//                       32-key k-step both operands use one key permutation)
+//   dkv kernel (wave w owns keys 16w..16w+15 of the block, K in registers):
+//     per query row, two stages of 32 heads each: (Q, dout) half rows are
+//     staged in LDS, double-buffered;
+//     S[head, key]  = Q . K^T,   dP[head, key] = dout . V^T  (B = K registers)
+//     dKV^T[dim, key] += Q^T . dS + [dout^T . P, 0]         (A by transpose reads)
+// LDS tiles use the swizzled 64-column-group layout of the forward engine:
+// row k's 16-byte chunk c sits in slot c ^ sw(k), sw(k) = 3 bit2(k) + 4 bit1(k).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+
+#include "hs_common.h"
+#include "hs_kernels.h"
+
+namespace hs {
+
+namespace {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define HS_LDS __attribute__((address_space(3)))
+
+namespace bw {
+constexpr int H = 64, DK = 576, DV = 512, BS = 64, NT = 256;
+constexpr int KSTEPS = DK / 32;     // 18
+constexpr int VSTEPS = DV / 32;     // 16
+constexpr int DBK = DK / 16;        // 36 column blocks of a latent row
+constexpr int DBV = DV / 16;        // 32 column blocks of a value row
+constexpr int GR = BS * 128;        // column group of a 64-row tile
+constexpr int TILE = 9 * GR;        // 73728
+constexpr int HGR = 32 * 128;       // column group of a 32-row half tile
+constexpr int QH = 9 * HGR;         // 36864: 32 Q rows
+constexpr int STAGE = QH + 8 * HGR; // + 32 dout rows = 69632
+}  // namespace bw
+
+constexpr int kMaxHeads = 64;
+
+__device__ __forceinline__ int swz(int k) { return 3 * ((k >> 2) & 1) + 4 * ((k >> 1) & 1); }
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// One LDS DMA instruction: lane l copies 16 B from src to LDS byte lds + 16 l
+// (base in M0; one wait state separates the M0 write from the DMA). Counted
+// by vmcnt only; callers wait with s_waitcnt vmcnt(0) and a barrier.
+__device__ __forceinline__ void dma16(const char* src, char* lds) {
+  const unsigned m = (unsigned)(uintptr_t)(HS_LDS char*)lds;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m) : "memory");
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Host-and-device forms of the block helpers of hs_common.h (the workspace
+// plan runs the same arithmetic on the host).
+__host__ __device__ inline int blocks_of_entry(const Geom& g, int b) {
+  if (g.n_docs == 0) return (g.kv_len[b] + g.BS - 1) / g.BS;
+  return g.doc_blk0[g.n_docs];
+}
+
+__host__ __device__ inline Blk block_span(const Geom& g, int b, int j) {
+  int s, e;
+  if (g.n_docs == 0) {
+    s = j * g.BS;
+    e = g.kv_len[b];
+  } else {
+    int lo = 0, hi = g.n_docs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (g.doc_blk0[mid] <= j) lo = mid; else hi = mid - 1;
+    }
+    s = g.doc_start[lo] + (j - g.doc_blk0[lo]) * g.BS;
+    e = g.doc_end[lo];
+  }
+  return Blk{s, e - s < g.BS ? e - s : g.BS};
+}
+
+// Whether row rr of entry b gathers block j (the forward's tile rule: a valid
+// id whose block meets the row's allowed key range).
+__host__ __device__ inline bool gather_hit(const Geom& g, int b, int nb_b, const RowRange& rr,
+                                           int j) {
+  if (j < 0 || j >= nb_b) return false;
+  const Blk bk = block_span(g, b, j);
+  return !(bk.start > rr.hi || bk.start + bk.len - 1 < rr.lo);
+}
+
+// Rows of entry b whose allowed keys meet block j, for the causal and window
+// operations: a contiguous range [*first, *first + n) of row indices.
+__host__ __device__ inline int block_row_range(const Geom& g, int op, int b, int j, int window,
+                                               int* first) {
+  *first = 0;
+  if (j >= blocks_of_entry(g, b)) return 0;
+  const int L = g.kv_len[b];
+  const Blk blk = block_span(g, b, j);
+  const Doc d = doc_of_pos(g, b, blk.start);
+  const int p_lo = blk.start > L - g.Sq ? blk.start : L - g.Sq;
+  int p_hi = d.end - 1;
+  if (op == kSwa) {
+    const long reach = (long)blk.start + blk.len - 1 + window - 1;
+    if (reach < p_hi) p_hi = (int)reach;
+  }
+  if (p_hi < p_lo) return 0;
+  *first = p_lo - (L - g.Sq);
+  return p_hi - p_lo + 1;
+}
+
+// ---------------------------------------------------------------------------
+// Dsum and the sink-gradient partials.
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ float dot_row(const T* x, const T* y, int n, int lane);
+
+template <>
+__device__ __forceinline__ float dot_row<bf16>(const bf16* x, const bf16* y, int n, int lane) {
+  float s = 0.f;
+  for (int d = 8 * lane; d < n; d += 512) {
+    const bf16x8 a = *(const bf16x8*)(x + d);
+    const bf16x8 b = *(const bf16x8*)(y + d);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = fmaf((float)a[e], (float)b[e], s);
+  }
+  return s;
+}
+
+template <>
+__device__ __forceinline__ float dot_row<float>(const float* x, const float* y, int n, int lane) {
+  float s = 0.f;
+  for (int d = lane; d < n; d += 64) s = fmaf(x[d], y[d], s);
+  return s;
+}
+
+// Workgroup w handles rows [w R, w R + R); each wave takes (row, head) pairs
+// in turn and reduces one dot product across its lanes.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
+  __shared__ float sacc[4][kMaxHeads];
+  const Geom& g = a.g;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int H = g.H, Dv = g.Dv;
+  const size_t rows = (size_t)g.B * g.Sq;
+  const size_t r0 = (size_t)blockIdx.x * a.rows_per_pre;
+  if (lane < H) sacc[wave][lane] = 0.f;
+  const T* out = static_cast<const T*>(a.out);
+  const T* dout = static_cast<const T*>(a.dout);
+  for (int p = wave; p < a.rows_per_pre * H; p += 4) {
+    const size_t row = r0 + p / H;
+    const int h = p % H;
+    if (row >= rows) break;
+    const size_t off = (row * H + h) * (size_t)Dv;
+    const float d = wave_sum(dot_row<T>(out + off, dout + off, Dv, lane));
+    if (lane == 0) {
+      a.dsum[row * H + h] = d;
+      if (a.sink != nullptr) {
+        const float lse = a.lse[row * H + h];
+        if (lse > -INFINITY) sacc[wave][h] -= __builtin_amdgcn_exp2f((a.sink[h] - lse) * kLog2e) * d;
+      }
+    }
+  }
+  __syncthreads();
+  if (a.dsink != nullptr && threadIdx.x < (unsigned)H) {
+    const int h = threadIdx.x;
+    a.sink_part[(size_t)blockIdx.x * H + h] = ((sacc[0][h] + sacc[1][h]) + sacc[2][h]) + sacc[3][h];
+  }
+}
+
+__global__ __launch_bounds__(64) void bwd_sink_kernel(BwdArgs a) {
+  const int h = threadIdx.x;
+  if (h >= a.g.H) return;
+  float s = 0.f;
+  for (int w = 0; w < a.n_pre; ++w) s += a.sink_part[(size_t)w * a.g.H + h];
+  a.dsink[h] = s;
+}
+
+// ---------------------------------------------------------------------------
+// Work plan of the key-block gradient.
+// ---------------------------------------------------------------------------
+// Gather: counts of each block's selecting rows per tile of 64 rows.
+__global__ __launch_bounds__(256) void bwd_gcount_kernel(BwdArgs a) {
+  __shared__ int hist[4096];
+  const Geom& g = a.g;
+  const int T = a.row_tiles;
+  const int b = blockIdx.x / T, tile = blockIdx.x % T;
+  for (int j = threadIdx.x; j < g.NB; j += 256) hist[j] = 0;
+  __syncthreads();
+  const int nb_b = nb_of_entry(g, b);
+  const int K = a.top_k;
+  for (int e = threadIdx.x; e < 64 * K; e += 256) {
+    const int r = tile * 64 + e / K;
+    if (r >= g.Sq) continue;
+    const int j = a.block_idx[((size_t)b * g.Sq + r) * K + e % K];
+    const RowRange rr = row_range(g, kGather, b, r, 0);
+    if (gather_hit(g, b, nb_b, rr, j)) atomicAdd(&hist[j], 1);
+  }
+  __syncthreads();
+  int* cnt = a.g_cnt + ((size_t)b * T + tile) * g.NB;
+  for (int j = threadIdx.x; j < g.NB; j += 256) cnt[j] = hist[j];
+}
+
+// Gather: per block, exclusive prefix of the tile counts (in place) and the
+// block's total.
+__global__ __launch_bounds__(256) void bwd_gscan_kernel(BwdArgs a) {
+  const Geom& g = a.g;
+  const int f = blockIdx.x * 256 + threadIdx.x;
+  if (f >= g.B * g.NB) return;
+  const int b = f / g.NB, j = f % g.NB;
+  int run = 0;
+  for (int t = 0; t < a.row_tiles; ++t) {
+    int* c = a.g_cnt + ((size_t)b * a.row_tiles + t) * g.NB + j;
+    const int v = *c;
+    *c = run;
+    run += v;
+  }
+  a.plan_nrows[f] = run;
+}
+
+// Rows per block, list offsets (gather) and the first work item of each
+// block: one workgroup, each thread a contiguous segment of blocks.
+__global__ __launch_bounds__(256) void bwd_plan_kernel(BwdArgs a, int op) {
+  __shared__ int seg_rows[256], seg_items[256];
+  const Geom& g = a.g;
+  const int F = g.B * g.NB;
+  const int per = (F + 255) / 256;
+  const int f0 = min(F, (int)threadIdx.x * per), f1 = min(F, f0 + per);
+  const int R = a.chunk_rows;
+  int rows = 0, items = 0;
+  for (int f = f0; f < f1; ++f) {
+    int n;
+    if (op == kGather) {
+      n = a.plan_nrows[f];
+    } else {
+      int first;
+      n = block_row_range(g, op, f / g.NB, f % g.NB, a.window, &first);
+      a.plan_first[f] = first;
+      a.plan_nrows[f] = n;
+    }
+    rows += n;
+    items += (n + R - 1) / R;
+  }
+  seg_rows[threadIdx.x] = rows;
+  seg_items[threadIdx.x] = items;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int r = 0, it = 0;
+    for (int t = 0; t < 256; ++t) {
+      const int vr = seg_rows[t], vi = seg_items[t];
+      seg_rows[t] = r;
+      seg_items[t] = it;
+      r += vr;
+      it += vi;
+    }
+    a.plan_pre[F] = min(it, a.items);
+  }
+  __syncthreads();
+  rows = seg_rows[threadIdx.x];
+  items = seg_items[threadIdx.x];
+  for (int f = f0; f < f1; ++f) {
+    const int n = a.plan_nrows[f];
+    if (op == kGather) a.plan_first[f] = rows;
+    a.plan_pre[f] = min(items, a.items);
+    rows += n;
+    items += (n + R - 1) / R;
+  }
+}
+
+// Gather: row lists, each block's rows in ascending order. One wave walks
+// the tile's rows in order; a row's entries are distinct blocks, and the
+// LDS counter makes repeated entries land in distinct slots regardless.
+__global__ __launch_bounds__(256) void bwd_gfill_kernel(BwdArgs a) {
+  __shared__ int next[4096];
+  const Geom& g = a.g;
+  const int T = a.row_tiles;
+  const int b = blockIdx.x / T, tile = blockIdx.x % T;
+  const int* cnt = a.g_cnt + ((size_t)b * T + tile) * g.NB;
+  for (int j = threadIdx.x; j < g.NB; j += 256) next[j] = a.plan_first[b * g.NB + j] + cnt[j];
+  __syncthreads();
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  const int nb_b = nb_of_entry(g, b);
+  for (int rl = 0; rl < 64; ++rl) {
+    const int r = tile * 64 + rl;
+    if (r >= g.Sq) break;
+    if (lane < a.top_k) {
+      const int j = a.block_idx[((size_t)b * g.Sq + r) * a.top_k + lane];
+      const RowRange rr = row_range(g, kGather, b, r, 0);
+      if (gather_hit(g, b, nb_b, rr, j)) a.g_rows[atomicAdd(&next[j], 1)] = r;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA kernels.
+// ---------------------------------------------------------------------------
+// Copy a 64-row KV tile (rows start .. start+len-1, clamped) into LDS: DMA
+// instruction (G, kq) fills rows 8kq .. 8kq+7 of column group G; wave w
+// issues kq = w and w + 4.
+__device__ __forceinline__ void stage_kv_tile(char* buf, const bf16* base, int start, int len,
+                                              int wave, int lane) {
+  using namespace bw;
+  const int kl = lane >> 3;
+  const int c8 = (lane & 7) ^ swz(8 * wave + kl);
+  const int ka = min(8 * wave + kl, len - 1);
+  const int kb = min(8 * (wave + 4) + kl, len - 1);
+  const char* src_a = (const char*)(base + (size_t)(start + ka) * DK) + 16 * c8;
+  const char* src_b = (const char*)(base + (size_t)(start + kb) * DK) + 16 * c8;
+  char* dst = buf + wave * 1024;
+#pragma unroll
+  for (int G = 0; G < 9; ++G) {
+    dma16(src_a + 128 * G, dst + G * GR);
+    dma16(src_b + 128 * G, dst + G * GR + 4096);
+  }
+}
+
+// Copy 32 head rows of Q (576 wide) and of dout (512 wide) into a stage
+// buffer: wave w fills rows 8w .. 8w+7 of every column group.
+__device__ __forceinline__ void stage_half_rows(char* st, const bf16* qrows, const bf16* drows,
+                                                int wave, int lane) {
+  using namespace bw;
+  const int hr = 8 * wave + (lane >> 3);
+  const int c8 = (lane & 7) ^ swz(hr);
+  const char* sq = (const char*)(qrows + (size_t)hr * DK) + 16 * c8;
+  const char* sd = (const char*)(drows + (size_t)hr * DV) + 16 * c8;
+  char* dst = st + wave * 1024;
+#pragma unroll
+  for (int G = 0; G < 9; ++G) dma16(sq + 128 * G, dst + G * HGR);
+#pragma unroll
+  for (int G = 0; G < 8; ++G) dma16(sd + 128 * G, dst + QH + G * HGR);
+}
+
+// A fragment rows 16 rb + l16, k-step ks, from a tile with group stride gs.
+__device__ __forceinline__ bf16x8 frag(const char* base, int gs, int ks, int rb, int l16, int grp) {
+  const int slot = (4 * (ks & 1) + grp) ^ swz(l16);
+  return *(const HS_LDS bf16x8*)(const HS_LDS char*)(base + (ks >> 1) * gs + (16 * rb + l16) * 128 +
+                                                     16 * slot);
+}
+
+// Transposed A fragment: A[m = column 16 db + l16][k-slot 8 grp + e] =
+// tile[row 32 kk + 16 (e >> 2) + 4 grp + (e & 3)][column], by two transpose
+// reads (rows 4 grp .. +3 and 16 + 4 grp .. +3 of the 32-row k-step).
+__device__ __forceinline__ bf16x8 frag_t(const char* base, int gs, int kk, int db, int l16, int grp) {
+  const int kloc = 4 * grp + (l16 >> 2);
+  const int tv = ((l16 >> 1) & 1) ^ swz(kloc);
+  const char* p = base + kloc * 128 + 8 * (l16 & 1) + 16 * ((2 * (db & 3)) ^ tv) + (db >> 2) * gs +
+                  (32 * kk) * 128;
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((HS_LDS bf16x4*)(HS_LDS char*)p);
+  const bf16x4 hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4bf16((HS_LDS bf16x4*)(HS_LDS char*)(p + 16 * 128));
+  bf16x8 v;
+  v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+  v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+  return v;
+}
+
+template <int OP>
+__global__ __launch_bounds__(bw::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dq_bf16_kernel(BwdArgs a) {
+  using namespace bw;
+  __shared__ __attribute__((aligned(16))) char buf[2][TILE];
+  __shared__ int tile_list[64];
+  __shared__ int tile_count;
+
+  const Geom& g = a.g;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = lane >> 4, l16 = lane & 15;
+  const int head = 16 * wave + l16;
+  const int w = blockIdx.x;
+  const int b = w / g.Sq;
+  const int r = g.Sq - 1 - (w % g.Sq);  // heaviest rows first
+  const size_t row = (size_t)b * g.Sq + r;
+  const RowRange rr = row_range(g, OP, b, r, a.window);
+  const int nb_b = nb_of_entry(g, b);
+
+  int ntiles;
+  if (OP == kGather) {
+    if (wave == 0) {
+      int j = -1;
+      bool ok = false;
+      if (lane < a.top_k) {
+        j = a.block_idx[row * a.top_k + lane];
+        ok = gather_hit(g, b, nb_b, rr, j);
+      }
+      const unsigned long long m = __ballot(ok);
+      if (ok) tile_list[__popcll(m & ((1ull << lane) - 1ull))] = j;
+      if (lane == 0) tile_count = __popcll(m);
+    }
+    __syncthreads();
+    ntiles = tile_count;
+  } else {
+    ntiles = rr.j_last - rr.j_first + 1;
+  }
+  auto tile_block = [&](int t) -> int { return OP == kGather ? tile_list[t] : rr.j_first + t; };
+
+  const bf16* kv_entry = static_cast<const bf16*>(a.kv) + (size_t)b * g.Skv * DK;
+  if (ntiles > 0) {
+    const Blk b0 = block_rows(g, b, tile_block(0));
+    stage_kv_tile(buf[0], kv_entry, b0.start, b0.len, wave, lane);
+  }
+
+  bf16x8 qreg[KSTEPS], dreg[VSTEPS];
+  {
+    const bf16* qp = static_cast<const bf16*>(a.q) + (row * H + head) * DK + 8 * grp;
+    const bf16* dp = static_cast<const bf16*>(a.dout) + (row * H + head) * DV + 8 * grp;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) qreg[ks] = *(const bf16x8*)(qp + 32 * ks);
+#pragma unroll
+    for (int ks = 0; ks < VSTEPS; ++ks) dreg[ks] = *(const bf16x8*)(dp + 32 * ks);
+  }
+  const float lse2 = a.lse[row * H + head] * kLog2e;
+  const float dsum = a.dsum[row * H + head];
+  const float sl2 = g.scale_log2;
+  const float scale = g.scale_log2 * kLn2;
+
+  f32x4 acc[DBK];
+#pragma unroll
+  for (int db = 0; db < DBK; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int t = 0; t < ntiles; ++t) {
+    char* cur = buf[t & 1];
+    const int j = tile_block(t);
+    const Blk blk = block_rows(g, b, j);
+    const int klo = rr.lo - blk.start, khi = min(rr.hi - blk.start, blk.len - 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // tile t resident; tile t-1 consumed by every wave
+    if (t + 1 < ntiles) {
+      const Blk nb = block_rows(g, b, tile_block(t + 1));
+      stage_kv_tile(buf[(t + 1) & 1], kv_entry, nb.start, nb.len, wave, lane);
+    }
+
+    f32x4 s[4], dp[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dp[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8 kf = frag(cur, GR, ks, kb, l16, grp);
+        s[kb] = mfma(kf, qreg[ks], s[kb]);
+        if (ks < VSTEPS) dp[kb] = mfma(kf, dreg[ks], dp[kb]);
+      }
+    }
+    // s[kb][i], dp[kb][i]: key 16 kb + 4 grp + i of the tile, head l16.
+    bf16x8 dsb[2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k = 16 * kb + 4 * grp + i;
+        const float p =
+            (k >= klo && k <= khi) ? __builtin_amdgcn_exp2f(s[kb][i] * sl2 - lse2) : 0.f;
+        dsb[kb >> 1][4 * (kb & 1) + i] = (bf16)(p * (dp[kb][i] - dsum) * scale);
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < DBK; ++db) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) acc[db] = mfma(frag_t(cur, GR, kk, db, l16, grp), dsb[kk], acc[db]);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // acc[db][i] = dq[head][16 db + 4 grp + i]
+  float* out = a.dq + (row * H + head) * DK + 4 * grp;
+#pragma unroll
+  for (int db = 0; db < DBK; ++db) *(f32x4*)(out + 16 * db) = acc[db];
+}
+
+template <int OP>
+__global__ __launch_bounds__(bw::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkv_bf16_kernel(BwdArgs a) {
+  using namespace bw;
+  __shared__ __attribute__((aligned(16))) char stg[2][STAGE];
+
+  const Geom& g = a.g;
+  const int F = g.B * g.NB;
+  const int item = blockIdx.x;
+  if (item >= a.plan_pre[F]) return;
+  int lo = 0, hi = F - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.plan_pre[mid] <= item) lo = mid; else hi = mid - 1;
+  }
+  const int f = lo;
+  const int b = f / g.NB, j = f % g.NB;
+  const int i0 = (item - a.plan_pre[f]) * a.chunk_rows;
+  const int n = min(a.chunk_rows, a.plan_nrows[f] - i0);
+  const int base_i = a.plan_first[f] + i0;
+  auto row_at = [&](int i) -> int {
+    const int rr = OP == kGather ? a.g_rows[base_i + i] : base_i + i;
+    return min(max(rr, 0), g.Sq - 1);
+  };
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = lane >> 4, l16 = lane & 15;
+  const int kloc = 16 * wave + l16;  // this lane's key inside the block
+  const Blk blk = block_rows(g, b, j);
+  const int key = blk.start + kloc;
+
+  const bf16* q = static_cast<const bf16*>(a.q);
+  const bf16* dout = static_cast<const bf16*>(a.dout);
+  auto stage = [&](int s) {
+    const size_t rw = (size_t)b * g.Sq + row_at(s >> 1);
+    const int h0 = 32 * (s & 1);
+    stage_half_rows(stg[s & 1], q + (rw * H + h0) * DK, dout + (rw * H + h0) * DV, wave, lane);
+  };
+  if (n > 0) stage(0);
+
+  bf16x8 kreg[KSTEPS];
+  {
+    const int kr = blk.start + min(kloc, blk.len - 1);
+    const bf16* kp = static_cast<const bf16*>(a.kv) + ((size_t)b * g.Skv + kr) * DK + 8 * grp;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) kreg[ks] = *(const bf16x8*)(kp + 32 * ks);
+  }
+  const float sl2 = g.scale_log2;
+  const float scale = g.scale_log2 * kLn2;
+
+  f32x4 acc[DBK];
+#pragma unroll
+  for (int db = 0; db < DBK; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int s = 0; s < 2 * n; ++s) {
+    const char* cur = stg[s & 1];
+    const int r = row_at(s >> 1);
+    const size_t rw = (size_t)b * g.Sq + r;
+    const int h0 = 32 * (s & 1);
+    const RowRange rr = row_range(g, OP, b, r, a.window);
+    const bool valid = kloc < blk.len && key >= rr.lo && key <= rr.hi;
+    // heads h0 + 16 hb + 4 grp + i of this lane
+    float lse2[2][4], ds[2][4];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = h0 + 16 * hb + 4 * grp + i;
+        lse2[hb][i] = a.lse[rw * H + h] * kLog2e;
+        ds[hb][i] = a.dsum[rw * H + h];
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // stage s resident; stage s-1 consumed by every wave
+    if (s + 1 < 2 * n) stage(s + 1);
+
+    f32x4 sc[2], dp[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      sc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dp[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        sc[hb] = mfma(frag(cur, HGR, ks, hb, l16, grp), kreg[ks], sc[hb]);
+        if (ks < VSTEPS) dp[hb] = mfma(frag(cur + QH, HGR, ks, hb, l16, grp), kreg[ks], dp[hb]);
+      }
+    }
+    // sc[hb][i], dp[hb][i]: head h0 + 16 hb + 4 grp + i, key kloc.
+    bf16x8 pb, dsb;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = valid ? __builtin_amdgcn_exp2f(sc[hb][i] * sl2 - lse2[hb][i]) : 0.f;
+        pb[4 * hb + i] = (bf16)p;
+        dsb[4 * hb + i] = (bf16)(p * (dp[hb][i] - ds[hb][i]) * scale);
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < DBK; ++db) acc[db] = mfma(frag_t(cur, HGR, 0, db, l16, grp), dsb, acc[db]);
+#pragma unroll
+    for (int db = 0; db < DBV; ++db)
+      acc[db] = mfma(frag_t(cur + QH, HGR, 0, db, l16, grp), pb, acc[db]);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // acc[db][i] = dkv[key kloc][16 db + 4 grp + i]
+  float* out = a.part + ((size_t)item * BS + kloc) * DK + 4 * grp;
+#pragma unroll
+  for (int db = 0; db < DBK; ++db) *(f32x4*)(out + 16 * db) = acc[db];
+}
+
+// dkv rows of entry b, 64 at a time: each row sums its block's partials in
+// item order; rows past the entry's valid length are zero.
+__global__ __launch_bounds__(256) void bwd_reduce_bf16_kernel(BwdArgs a) {
+  using namespace bw;
+  const Geom& g = a.g;
+  const int chunks = (g.Skv + 63) / 64;
+  const int b = blockIdx.x / chunks, c = blockIdx.x % chunks;
+  const int L = kv_len_of(g, b);
+  constexpr int V4 = DK / 4;  // 144 float4 per row
+  for (int e = threadIdx.x; e < 64 * V4; e += 256) {
+    const int i = 64 * c + e / V4, c4 = e % V4;
+    if (i >= g.Skv) break;
+    f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (i < L) {
+      const Doc d = doc_of_pos(g, b, i);
+      const int j = block_of_pos(g, d, i);
+      const int k = i - (d.start + (j - d.blk0) * g.BS);
+      const int f = b * g.NB + j;
+      const int s0 = a.plan_pre[f], s1 = a.plan_pre[f + 1];
+      for (int s = s0; s < s1; ++s) v += *(const f32x4*)(a.part + ((size_t)s * BS + k) * DK + 4 * c4);
+    }
+    *(f32x4*)(a.dkv + ((size_t)b * g.Skv + i) * DK + 4 * c4) = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernels (H <= 16, Dk <= 128): plain FMAs over LDS-staged rows.
+// ---------------------------------------------------------------------------
+namespace f32b {
+constexpr int MAXH = 16, MAXD = 128, BS = 64, NT = 256, KS = MAXD + 1;
+constexpr int MAXQ = (MAXH * MAXD + NT - 1) / NT;  // dq elements per thread
+constexpr int MAXK = (BS * MAXD + NT - 1) / NT;    // dkv elements per thread
+}  // namespace f32b
+
+template <int OP>
+__global__ __launch_bounds__(f32b::NT) void bwd_dq_f32_kernel(BwdArgs a) {
+  using namespace f32b;
+  __shared__ float qs[MAXH * MAXD], dos[MAXH * MAXD], ks[BS * KS], dss[MAXH * BS];
+  __shared__ float lse2[MAXH], dsum[MAXH];
+  __shared__ int tile_list[64];
+  __shared__ int tile_count;
+  const Geom& g = a.g;
+  const int H = g.H, Dk = g.Dk, Dv = g.Dv, tid = threadIdx.x;
+  const int w = blockIdx.x;
+  const int b = w / g.Sq, r = g.Sq - 1 - (w % g.Sq);
+  const size_t row = (size_t)b * g.Sq + r;
+  const RowRange rr = row_range(g, OP, b, r, a.window);
+  const int nb_b = nb_of_entry(g, b);
+  const float* q = static_cast<const float*>(a.q);
+  const float* kv = static_cast<const float*>(a.kv);
+  const float* dout = static_cast<const float*>(a.dout);
+  if (tid == 0) {
+    int n = 0;
+    if (OP == kGather) {
+      for (int k = 0; k < a.top_k; ++k) {
+        const int j = a.block_idx[row * a.top_k + k];
+        if (gather_hit(g, b, nb_b, rr, j)) tile_list[n++] = j;
+      }
+    } else {
+      n = rr.j_last - rr.j_first + 1;
+    }
+    tile_count = n;
+  }
+  for (int i = tid; i < H * Dk; i += NT) qs[(i / Dk) * MAXD + i % Dk] = q[row * H * Dk + i];
+  for (int i = tid; i < H * Dv; i += NT) dos[(i / Dv) * MAXD + i % Dv] = dout[row * H * Dv + i];
+  if (tid < H) {
+    lse2[tid] = a.lse[row * H + tid] * kLog2e;
+    dsum[tid] = a.dsum[row * H + tid];
+  }
+  __syncthreads();
+  const int ntiles = tile_count;
+  const float sl2 = g.scale_log2, scale = g.scale_log2 * kLn2;
+  float acc[MAXQ];
+#pragma unroll
+  for (int m = 0; m < MAXQ; ++m) acc[m] = 0.f;
+  const float* kv_entry = kv + (size_t)b * g.Skv * Dk;
+  for (int t = 0; t < ntiles; ++t) {
+    const int j = OP == kGather ? tile_list[t] : rr.j_first + t;
+    const Blk blk = block_rows(g, b, j);
+    for (int i = tid; i < BS * Dk; i += NT) {
+      const int k = i / Dk, d = i % Dk;
+      ks[k * KS + d] = kv_entry[(size_t)(blk.start + min(k, blk.len - 1)) * Dk + d];
+    }
+    __syncthreads();
+    for (int i = tid; i < H * BS; i += NT) {
+      const int h = i / BS, k = i % BS;
+      float s = 0.f, dp = 0.f;
+      for (int d = 0; d < Dk; ++d) s = fmaf(qs[h * MAXD + d], ks[k * KS + d], s);
+      for (int d = 0; d < Dv; ++d) dp = fmaf(dos[h * MAXD + d], ks[k * KS + d], dp);
+      const int key = blk.start + k;
+      const bool ok = k < blk.len && key >= rr.lo && key <= rr.hi;
+      const float p = ok ? exp2f(s * sl2 - lse2[h]) : 0.f;
+      dss[i] = p * (dp - dsum[h]) * scale;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < MAXQ; ++m) {
+      const int e = tid + NT * m;
+      if (e < H * Dk) {
+        const int h = e / Dk, d = e % Dk;
+        float v = acc[m];
+        for (int k = 0; k < BS; ++k) v = fmaf(dss[h * BS + k], ks[k * KS + d], v);
+        acc[m] = v;
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int m = 0; m < MAXQ; ++m) {
+    const int e = tid + NT * m;
+    if (e < H * Dk) a.dq[row * H * Dk + e] = acc[m];
+  }
+}
+
+// One workgroup per (entry, key block); the last B workgroups zero the rows
+// past each entry's valid length.
+template <int OP>
+__global__ __launch_bounds__(f32b::NT) void bwd_dkv_f32_kernel(BwdArgs a) {
+  using namespace f32b;
+  __shared__ float ks[BS * KS], qs[MAXH * MAXD], dos[MAXH * MAXD], ps[MAXH * BS], dss[MAXH * BS];
+  __shared__ float lse2[MAXH], dsum[MAXH];
+  __shared__ int take;
+  const Geom& g = a.g;
+  const int H = g.H, Dk = g.Dk, Dv = g.Dv, tid = threadIdx.x;
+  const float* q = static_cast<const float*>(a.q);
+  const float* kv = static_cast<const float*>(a.kv);
+  const float* dout = static_cast<const float*>(a.dout);
+  if ((int)blockIdx.x >= g.B * g.NB) {
+    const int b = blockIdx.x - g.B * g.NB;
+    const int L = kv_len_of(g, b);
+    for (size_t i = (size_t)L * Dk + tid; i < (size_t)g.Skv * Dk; i += NT)
+      a.dkv[(size_t)b * g.Skv * Dk + i] = 0.f;
+    return;
+  }
+  const int b = blockIdx.x / g.NB, j = blockIdx.x % g.NB;
+  const int nb_b = nb_of_entry(g, b);
+  if (j >= nb_b) return;
+  const Blk blk = block_rows(g, b, j);
+  const float* kv_entry = kv + (size_t)b * g.Skv * Dk;
+  for (int i = tid; i < BS * Dk; i += NT) {
+    const int k = i / Dk, d = i % Dk;
+    ks[k * KS + d] = kv_entry[(size_t)(blk.start + min(k, blk.len - 1)) * Dk + d];
+  }
+  // Candidate rows: the causal range of the block (the window and gather
+  // sets lie inside it).
+  int first;
+  const int n = block_row_range(g, OP == kSwa ? kSwa : kScore, b, j, a.window, &first);
+  const float sl2 = g.scale_log2, scale = g.scale_log2 * kLn2;
+  float acc[MAXK];
+#pragma unroll
+  for (int m = 0; m < MAXK; ++m) acc[m] = 0.f;
+  for (int ri = 0; ri < n; ++ri) {
+    const int r = first + ri;
+    const size_t row = (size_t)b * g.Sq + r;
+    const RowRange rr = row_range(g, OP, b, r, a.window);
+    __syncthreads();
+    if (tid == 0) {
+      bool hit = true;
+      if (OP == kGather) {
+        hit = false;
+        for (int k = 0; k < a.top_k; ++k)
+          if (a.block_idx[row * a.top_k + k] == j && gather_hit(g, b, nb_b, rr, j)) hit = true;
+      }
+      take = hit;
+    }
+    for (int i = tid; i < H * Dk; i += NT) qs[(i / Dk) * MAXD + i % Dk] = q[row * H * Dk + i];
+    for (int i = tid; i < H * Dv; i += NT) dos[(i / Dv) * MAXD + i % Dv] = dout[row * H * Dv + i];
+    if (tid < H) {
+      lse2[tid] = a.lse[row * H + tid] * kLog2e;
+      dsum[tid] = a.dsum[row * H + tid];
+    }
+    __syncthreads();
+    if (!take) continue;
+    for (int i = tid; i < H * BS; i += NT) {
+      const int h = i / BS, k = i % BS;
+      float s = 0.f, dp = 0.f;
+      for (int d = 0; d < Dk; ++d) s = fmaf(qs[h * MAXD + d], ks[k * KS + d], s);
+      for (int d = 0; d < Dv; ++d) dp = fmaf(dos[h * MAXD + d], ks[k * KS + d], dp);
+      const int key = blk.start + k;
+      const bool ok = k < blk.len && key >= rr.lo && key <= rr.hi;
+      const float p = ok ? exp2f(s * sl2 - lse2[h]) : 0.f;
+      ps[i] = p;
+      dss[i] = p * (dp - dsum[h]) * scale;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < MAXK; ++m) {
+      const int e = tid + NT * m;
+      if (e < BS * Dk) {
+        const int k = e / Dk, d = e % Dk;
+        float v = acc[m];
+        for (int h = 0; h < H; ++h) v = fmaf(dss[h * BS + k], qs[h * MAXD + d], v);
+        if (d < Dv)
+          for (int h = 0; h < H; ++h) v = fmaf(ps[h * BS + k], dos[h * MAXD + d], v);
+        acc[m] = v;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MAXK; ++m) {
+    const int e = tid + NT * m;
+    if (e < blk.len * Dk) a.dkv[((size_t)b * g.Skv + blk.start) * Dk + e] = acc[m];
+  }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+template <int OP>
+void launch_bf16(const BwdArgs& a, hipStream_t s) {
+  const Geom& g = a.g;
+  const unsigned F = (unsigned)(g.B * g.NB);
+  if (OP == kGather) {
+    hipLaunchKernelGGL(bwd_gcount_kernel, dim3(g.B * a.row_tiles), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(bwd_gscan_kernel, dim3((F + 255) / 256), dim3(256), 0, s, a);
+  }
+  hipLaunchKernelGGL(bwd_plan_kernel, dim3(1), dim3(256), 0, s, a, OP);
+  if (OP == kGather)
+    hipLaunchKernelGGL(bwd_gfill_kernel, dim3(g.B * a.row_tiles), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(bwd_dq_bf16_kernel<OP>, dim3(g.B * g.Sq), dim3(bw::NT), 0, s, a);
+  if (a.items > 0)
+    hipLaunchKernelGGL(bwd_dkv_bf16_kernel<OP>, dim3(a.items), dim3(bw::NT), 0, s, a);
+  hipLaunchKernelGGL(bwd_reduce_bf16_kernel, dim3(g.B * ((g.Skv + 63) / 64)), dim3(256), 0, s, a);
+}
+
+template <int OP>
+void launch_f32(const BwdArgs& a, hipStream_t s) {
+  const Geom& g = a.g;
+  hipLaunchKernelGGL(bwd_dq_f32_kernel<OP>, dim3(g.B * g.Sq), dim3(f32b::NT), 0, s, a);
+  hipLaunchKernelGGL(bwd_dkv_f32_kernel<OP>, dim3(g.B * g.NB + g.B), dim3(f32b::NT), 0, s, a);
+}
+
+}  // namespace
+
+BwdLayout bwd_layout(const Geom& g, int op, int top_k, int window, bool is_bf16) {
+  BwdLayout L;
+  std::memset(&L, 0, sizeof(L));
+  const size_t rows = (size_t)g.B * g.Sq;
+  L.rows_per_pre = (int)std::max<size_t>(8, (rows + 2047) / 2048);
+  L.n_pre = (int)((rows + L.rows_per_pre - 1) / L.rows_per_pre);
+  size_t off = 0;
+  L.dsum = off;
+  off = align256(off + rows * g.H * sizeof(float));
+  L.sink_part = off;
+  off = align256(off + (size_t)L.n_pre * g.H * sizeof(float));
+  if (is_bf16) {
+    const size_t F = (size_t)g.B * g.NB;
+    L.row_tiles = (g.Sq + 63) / 64;
+    L.first = off;
+    off = align256(off + F * sizeof(int));
+    L.nrows = off;
+    off = align256(off + F * sizeof(int));
+    L.pre = off;
+    off = align256(off + (F + 1) * sizeof(int));
+    // Rows per work item: the largest power of two from 4096 down to 64 that
+    // still gives about 2048 items (eight per compute unit).
+    auto items_for = [&](int R, long* pairs) -> long {
+      long it = 0, pr = 0;
+      if (op == kGather) {
+        pr = (long)g.B * g.Sq * std::min(top_k, g.NB);
+        it = (pr + R - 1) / R + std::min<long>((long)F, pr);
+      } else {
+        for (int b = 0; b < g.B; ++b)
+          for (int j = 0; j < g.NB; ++j) {
+            int first;
+            const int n = block_row_range(g, op, b, j, window, &first);
+            pr += n;
+            it += (n + R - 1) / R;
+          }
+      }
+      if (pairs) *pairs = pr;
+      return it;
+    };
+    int R = 4096;
+    while (R > 64 && items_for(R, nullptr) < 2048) R >>= 1;
+    L.chunk_rows = R;
+    L.items = (int)items_for(R, nullptr);
+    if (op == kGather) {
+      L.cnt = off;
+      off = align256(off + (size_t)g.B * L.row_tiles * g.NB * sizeof(int));
+      L.rows = off;
+      off = align256(off + rows * std::max(top_k, 1) * sizeof(int));
+    }
+    L.part = off;
+    off = align256(off + (size_t)L.items * 64 * g.Dk * sizeof(float));
+  }
+  L.total = off;
+  return L;
+}
+
+int bwd_launch(int op, const BwdArgs& a, bool is_bf16, hipStream_t s) {
+  if (is_bf16) hipLaunchKernelGGL(bwd_pre_kernel<bf16>, dim3(a.n_pre), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(bwd_pre_kernel<float>, dim3(a.n_pre), dim3(256), 0, s, a);
+  if (a.dsink != nullptr) hipLaunchKernelGGL(bwd_sink_kernel, dim3(1), dim3(64), 0, s, a);
+  if (is_bf16) {
+    if (op == kScore) launch_bf16<kScore>(a, s);
+    else if (op == kGather) launch_bf16<kGather>(a, s);
+    else launch_bf16<kSwa>(a, s);
+  } else {
+    if (op == kScore) launch_f32<kScore>(a, s);
+    else if (op == kGather) launch_f32<kGather>(a, s);
+    else launch_f32<kSwa>(a, s);
+  }
+  return (int)hipGetLastError();
+}
+
+}  // namespace hs

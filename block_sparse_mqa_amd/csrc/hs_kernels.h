@@ -50,6 +50,47 @@ struct TopkArgs {
   Geom g;
 };
 
+// Arguments of the gradient kernels (both dtypes). The workspace pieces are
+// laid out by bwd_layout().
+struct BwdArgs {
+  const void* q;             // [B, Sq, H, Dk] dtype
+  const void* kv;            // [B, Skv, Dk] dtype
+  const float* sink;         // [H] or nullptr
+  const void* out;           // [B, Sq, H, Dv] dtype (forward output)
+  const float* lse;          // [B, Sq, H] (forward output, natural log)
+  const void* dout;          // [B, Sq, H, Dv] dtype
+  const int* block_idx;      // gather: [B, Sq, top_k]
+  int top_k;
+  int window;
+  float* dq;                 // [B, Sq, H, Dk]
+  float* dkv;                // [B, Skv, Dk]
+  float* dsink;              // [H] or nullptr
+  // workspace
+  float* dsum;               // [B * Sq * H] dout . out per row and head
+  float* sink_part;          // [n_pre, H] per-workgroup sink-gradient partials
+  int n_pre, rows_per_pre;
+  int* plan_first;           // [B * NB] first row (range) or list offset (gather)
+  int* plan_nrows;           // [B * NB] rows that reach the block
+  int* plan_pre;             // [B * NB + 1] first work item of each block
+  int* g_cnt;                // gather: [B, T, NB] per-row-tile counts, then offsets
+  int* g_rows;               // gather: row lists of all blocks
+  float* part;               // [items, 64, Dk] per-item key-block gradient partials
+  int chunk_rows;            // rows per work item
+  int items;                 // work items launched (exact or an upper bound)
+  int row_tiles;             // T = ceil(Sq / 64)
+  Geom g;
+};
+
+// Workspace layout of one gradient call: byte offsets of each piece and the
+// total, plus the work split of the key-block gradient.
+struct BwdLayout {
+  size_t dsum, sink_part, first, nrows, pre, cnt, rows, part, total;
+  int n_pre, rows_per_pre, chunk_rows, items, row_tiles;
+};
+
+BwdLayout bwd_layout(const Geom& g, int op, int top_k, int window, bool bf16);
+int bwd_launch(int op, const BwdArgs& a, bool bf16, hipStream_t stream);
+
 int attn_bf16_launch(int op, const AttnArgs& a, hipStream_t stream);
 int attn_f32_launch(int op, const AttnF32Args& a, hipStream_t stream);
 int topk_launch(const TopkArgs& a, hipStream_t stream);

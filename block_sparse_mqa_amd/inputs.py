@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the HySparse MQA forward path.
+"""Seeded synthetic inputs for the HySparse MQA path (forward and gradients).
 
 This module only draws random tensors and describes problem shapes. It holds
 none of the method's arithmetic: no scores, no softmax, no block scoring, no
@@ -26,6 +26,10 @@ to the storage dtype with round-to-nearest-even. q ~ N(0, 1). kv ~ N(0, 1) for
 config 1 and N(0, 1) * 4 / sqrt(576) for the others. sink ~ N(0, 1), stored
 fp32. KV rows past a sequence's valid length are filled with NaN so that any
 read of them shows up in the outputs.
+
+Upstream gradients for the gradient calls (``make_dout``): dout ~ N(0, 1) of
+the output's shape [B, Sq, H, Dv], drawn from its own generator seeded with
+the given seed, in fp32 chunks of 1024 rows, cast to the storage dtype.
 """
 from __future__ import annotations
 
@@ -194,3 +198,10 @@ def _make_decode_with_generator(g, lens) -> Problem:
     return Problem(name="decode_B32_L16k-64k", dtype="bf16", B=B, Sq=1, Skv=Skv, H=H, Dk=Dk,
                    Dv=Dv, block_size=64, top_k=32, window=1024, scale=1.0 / math.sqrt(Dk),
                    kv_lens=list(lens), q=q, kv=kv, sink=sink)
+
+
+def make_dout(p: Problem, seed: int) -> torch.Tensor:
+    """Seeded upstream gradient of the attention output: [B, Sq, H, Dv]."""
+    g = torch.Generator().manual_seed(seed)
+    d = _draw_rows(g, p.B * p.Sq, (p.H, p.Dv), 1.0, p.dtype)
+    return d.view(p.B, p.Sq, p.H, p.Dv)

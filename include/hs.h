@@ -90,7 +90,14 @@ typedef enum {
 
 typedef enum { HS_BF16 = 0, HS_F32 = 1 } hs_dtype;
 
-typedef enum { HS_OP_BLOCK_SCORE = 0, HS_OP_SPARSE_GATHER = 1, HS_OP_SWA = 2 } hs_op;
+typedef enum {
+  HS_OP_BLOCK_SCORE = 0,
+  HS_OP_SPARSE_GATHER = 1,
+  HS_OP_SWA = 2,
+  HS_OP_BLOCK_SCORE_BWD = 3,    /* workspace of hs_block_score_bwd   */
+  HS_OP_SPARSE_GATHER_BWD = 4,  /* workspace of hs_sparse_gather_bwd */
+  HS_OP_SWA_BWD = 5             /* workspace of hs_swa_bwd           */
+} hs_op;
 
 typedef struct {
   int32_t batch;          /* B                                                   */
@@ -120,8 +127,9 @@ int32_t hs_num_blocks(const hs_problem* p);
 
 /* Workspace bytes the given operation needs for this problem (0 when it
  * needs none; single-token decode splits the key range across workgroups and
- * merges partial results through the workspace). top_k and window are the
- * values the operation will be called with (ignored where irrelevant). */
+ * merges partial results through the workspace; the gradient operations
+ * always need one). top_k and window are the values the operation will be
+ * called with (ignored where irrelevant). */
 hs_status hs_workspace_size(const hs_problem* p, int32_t op, int32_t top_k, int32_t window,
                             size_t* bytes);
 
@@ -180,6 +188,46 @@ hs_status hs_sparse_gather_fwd(const hs_problem* p, const void* q, const void* k
  * token itself). window >= 1. */
 hs_status hs_swa_fwd(const hs_problem* p, const void* q, const void* kv, const float* sink,
                      int32_t window, void* out, float* lse, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Gradients (page "HySparse MQA sparse attention ...", section "Core": block
+ * scoring trained through its autograd layer and the analytic gradient of
+ * the learnable per-head sink; per-file table rows for windowed_mqa_attn*.py
+ * and block_sparse_mqa_dsa.py, forward and backward kernels). For the loss
+ * L = sum(dout * out) of the forward output out:
+ *   dq  [B, Sq, H, Dk]  float32 = dL/dq;
+ *   dkv [B, Skv, Dk]    float32 = dL/dkv, the key and value gradients added
+ *                       (the latent row is both); rows past an entry's valid
+ *                       length are zero; every row is written;
+ *   dsink [H] float32   = dL/dsink = -sum over rows of exp(sink - lse) *
+ *                       (dout . out); NULL skips it; needs a sink.
+ * out and lse are the forward's outputs for the same inputs (out: dtype,
+ * [B, Sq, H, Dv]; lse: [B, Sq, H]); dout has out's layout and dtype. lse is
+ * a saved statistic and takes no gradient; the block scores take none either
+ * (review of PaddleFleet PR 1453, block-score PyLayer comments: the backward
+ * returns gradients for q, k and v only). The workspace is mandatory:
+ * hs_workspace_size with HS_OP_*_BWD and the same top_k / window, 16-byte
+ * aligned. Results are deterministic (fixed summation order). Paged KV and
+ * device-resident lengths are rejected (HS_ERR_UNSUPPORTED).
+ * hs_block_score_bwd: the causal attention of hs_block_score_fwd. */
+hs_status hs_block_score_bwd(const hs_problem* p, const void* q, const void* kv, const float* sink,
+                             const void* out, const float* lse, const void* dout, float* dq,
+                             float* dkv, float* dsink, void* ws, size_t ws_bytes, void* stream);
+
+/* Gradients of hs_sparse_gather_fwd for the given selection (block_idx and
+ * top_k as in the forward; the selection itself takes no gradient). At most
+ * 4096 blocks. */
+hs_status hs_sparse_gather_bwd(const hs_problem* p, const void* q, const void* kv,
+                               const float* sink, const int32_t* block_idx, int32_t top_k,
+                               const void* out, const float* lse, const void* dout, float* dq,
+                               float* dkv, float* dsink, void* ws, size_t ws_bytes, void* stream);
+
+/* Gradients of hs_swa_fwd (review of PaddleFleet PR 1453, the windowed
+ * backward comments: a sequence length that is not a multiple of the tile
+ * must read no row past its end; here every row index is bounded by Sq). */
+hs_status hs_swa_bwd(const hs_problem* p, const void* q, const void* kv, const float* sink,
+                     int32_t window, const void* out, const float* lse, const void* dout,
+                     float* dq, float* dkv, float* dsink, void* ws, size_t ws_bytes,
                      void* stream);
 
 /* Static description of a status code. */

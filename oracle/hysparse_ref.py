@@ -317,7 +317,7 @@ def sparse_gather(q, kv, sink, Dv, scale, block_idx, block_size=64, kv_lens=None
 # Gradients of the three attention operations.
 # ---------------------------------------------------------------------------
 def _op_bwd(kind, q, kv, sink, Dv, scale, dout, block_size, kv_lens=None, doc_start=None,
-            doc_end=None, window=None, block_idx=None, chunk=None):
+            doc_end=None, window=None, block_idx=None, chunk=None, rows=None):
     """Gradients of L = sum(dout * out) for one attention operation.
 
     The pages train through these kernels: page "HySparse MQA sparse attention
@@ -340,15 +340,20 @@ def _op_bwd(kind, q, kv, sink, Dv, scale, dout, block_size, kv_lens=None, doc_st
     columns), so dkv_i = dk_i + [dv_i, 0]. Reading: lse receives no incoming
     gradient (it is a saved statistic of the forward). Returns dq [B,Sq,H,Dk],
     dkv [B,Skv,Dk] (zero past each entry's valid length) and dsink [H]
-    (None without a sink)."""
+    (None without a sink).
+
+    rows: optionally only these query rows (dout is then [B, len(rows), H,
+    Dv]): dq [B, len(rows), H, Dk] for them, and the dkv and dsink
+    contributions of these rows alone (complete for a key that no other row
+    attends to)."""
     q, kv, sk = _prepare(q, kv, sink, Dv)
     B, Sq, H, Dk = q.shape
     Skv = kv.shape[1]
     g_all = dout
-    dq = np.zeros((B, Sq, H, Dk))
+    rows_sel = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
+    dq = np.zeros((B, len(rows_sel), H, Dk))
     dkv = np.zeros((B, Skv, Dk))
     dsink = None if sk is None else np.zeros(H)
-    rows_sel = np.arange(Sq)
     k_entry, k_b = None, -1
     for b, rr, L, kmin, kmax, allowed, _ in _chunk_masks(
             kind, B, Sq, Skv, H, block_size, kv_lens, doc_start, doc_end, window, block_idx,
@@ -357,7 +362,7 @@ def _op_bwd(kind, q, kv, sink, Dv, scale, dout, block_size, kv_lens=None, doc_st
             k_entry, k_b = _to64(kv[b, :L]), b
         k = k_entry[kmin:kmax]
         v = k[:, :Dv]
-        qr = _to64(q[b, rr])                                  # [r, H, Dk]
+        qr = _to64(q[b, rows_sel[rr]])                        # [r, H, Dk]
         g = _to64(g_all[b, rr])                               # [r, H, Dv]
         s = _scores(qr, k, scale)                             # [r, H, n]
         out, lse = _attend_masked(s, allowed, v, sk)
@@ -377,26 +382,26 @@ def _op_bwd(kind, q, kv, sink, Dv, scale, dout, block_size, kv_lens=None, doc_st
 
 
 def block_score_bwd(q, kv, sink, Dv, scale, dout, block_size=64, kv_lens=None,
-                    doc_start=None, doc_end=None, chunk=None):
+                    doc_start=None, doc_end=None, chunk=None, rows=None):
     """Gradients of the causal attention of block_score (block_logit has none)."""
     return _op_bwd("score", q, kv, sink, Dv, scale, dout, block_size, kv_lens, doc_start,
-                   doc_end, chunk=chunk)
+                   doc_end, chunk=chunk, rows=rows)
 
 
 def swa_bwd(q, kv, sink, Dv, scale, window, dout, block_size=64, kv_lens=None,
-            doc_start=None, doc_end=None, chunk=None):
+            doc_start=None, doc_end=None, chunk=None, rows=None):
     """Gradients of the sliding-window attention."""
     return _op_bwd("swa", q, kv, sink, Dv, scale, dout, block_size, kv_lens, doc_start,
-                   doc_end, window=window, chunk=chunk)
+                   doc_end, window=window, chunk=chunk, rows=rows)
 
 
 def sparse_gather_bwd(q, kv, sink, Dv, scale, block_idx, dout, block_size=64, kv_lens=None,
-                      doc_start=None, doc_end=None, chunk=None):
+                      doc_start=None, doc_end=None, chunk=None, rows=None):
     """Gradients of the block-sparse gather attention for a fixed selection."""
     bi = np.asarray(block_idx.cpu() if hasattr(block_idx, "cpu") else block_idx,
                     dtype=np.int64)
     return _op_bwd("gather", q, kv, sink, Dv, scale, dout, block_size, kv_lens, doc_start,
-                   doc_end, block_idx=bi, chunk=chunk)
+                   doc_end, block_idx=bi, chunk=chunk, rows=rows)
 
 
 def own_blocks(B, Sq, Skv, block_size, kv_lens=None, doc_start=None, doc_end=None,

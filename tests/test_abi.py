@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(hs.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.hs_version() == 102
+    assert lib.hs_version() == 103
 
 
 def _mla(**kw):
@@ -103,6 +103,52 @@ def test_fused_score_topk_rejects_before_launch():
     # split decode without its workspace
     d = _mla(B=2, Sq=1, Skv=4096, kv_lens=[4096, 2000])
     assert call(4, fake, d) == hs.HS_ERR_WORKSPACE
+
+
+def test_gradient_calls_reject_before_launch():
+    lib = hs.load_library()
+    p = _mla()
+    f = ctypes.c_void_p(4096)
+    n = hs.hs_workspace_size(p, hs.HS_OP_BLOCK_SCORE_BWD)
+    assert n > 0
+    big = ctypes.c_size_t(n)
+
+    def score(prob=p, q=f, sink=None, dout=f, dsink=None, ws=f, nbytes=big):
+        return lib.hs_block_score_bwd(prob.ref, q, f, sink, f, f, dout, f, f, dsink, ws, nbytes,
+                                      None)
+    assert score(q=None) == hs.HS_ERR_INVALID_ARG and b"q is NULL" in lib.hs_last_error()
+    assert score(dout=ctypes.c_void_p(4100)) == hs.HS_ERR_INVALID_ARG
+    assert score(dsink=f) == hs.HS_ERR_INVALID_ARG and b"no sink" in lib.hs_last_error()
+    assert score(ws=None) == hs.HS_ERR_WORKSPACE
+    assert score(nbytes=ctypes.c_size_t(n - 1)) == hs.HS_ERR_WORKSPACE
+    assert score(ws=ctypes.c_void_p(4104)) == hs.HS_ERR_WORKSPACE
+    # paged KV has no gradient path
+    paged = _raw_problem()
+    st = lib.hs_block_score_bwd(ctypes.byref(paged), f, f, None, f, f, f, f, f, None, f, big, None)
+    assert st == hs.HS_ERR_UNSUPPORTED and b"paged" in lib.hs_last_error()
+    # window and top_k
+    st = lib.hs_swa_bwd(p.ref, f, f, None, 0, f, f, f, f, f, None, f, big, None)
+    assert st == hs.HS_ERR_INVALID_ARG and b"window" in lib.hs_last_error()
+    st = lib.hs_sparse_gather_bwd(p.ref, f, f, None, f, 65, f, f, f, f, f, None, f, big, None)
+    assert st == hs.HS_ERR_UNSUPPORTED
+    st = lib.hs_sparse_gather_bwd(p.ref, f, f, None, None, 4, f, f, f, f, f, None, f, big, None)
+    assert st == hs.HS_ERR_INVALID_ARG and b"block_idx" in lib.hs_last_error()
+    with pytest.raises(ValueError):
+        hs.hs_workspace_size(p, hs.HS_OP_SWA_BWD, window=0)
+
+
+def test_gradient_workspace_sizes():
+    """Gradients always need a workspace; it grows with the work items of the
+    key-block gradient and covers the gather's row lists."""
+    small = _mla(Sq=128, Skv=128)
+    big = _mla(Sq=4096, Skv=4096)
+    for op, kw in ((hs.HS_OP_BLOCK_SCORE_BWD, {}), (hs.HS_OP_SPARSE_GATHER_BWD, {"top_k": 8}),
+                   (hs.HS_OP_SWA_BWD, {"window": 256})):
+        a = hs.hs_workspace_size(small, op, **kw)
+        b = hs.hs_workspace_size(big, op, **kw)
+        assert 0 < a < b
+    f32 = _mla(dtype="f32", H=8, Dk=96, Dv=64)
+    assert hs.hs_workspace_size(f32, hs.HS_OP_BLOCK_SCORE_BWD) >= 128 * 8 * 4
 
 
 @pytest.mark.parametrize("case", [

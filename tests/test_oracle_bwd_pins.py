@@ -188,3 +188,18 @@ def test_empty_selection_gives_zero_gradients():
     assert not np.any(dq[0, rows])
     assert not np.any(dkv[0, :4]) and not np.any(dkv[0, 5:])
     assert np.any(dkv[0, 4:5])
+
+
+def test_row_subset_matches_full_run():
+    """Restricting the gradient to a set of rows gives those rows' dq exactly,
+    and dkv / dsink summed over a partition of the rows equal the full run."""
+    rng, q, kv, sink, dout = _problem(21, 1, 37, 37, 2, 5, 4, True)
+    full = ref.swa_bwd(q, kv, sink, 4, 0.6, 9, dout, block_size=4)
+    a = np.arange(0, 37, 3)
+    b = np.setdiff1d(np.arange(37), a)
+    pa = ref.swa_bwd(q, kv, sink, 4, 0.6, 9, dout[:, a], block_size=4, rows=a)
+    pb = ref.swa_bwd(q, kv, sink, 4, 0.6, 9, dout[:, b], block_size=4, rows=b)
+    assert np.allclose(pa[0], full[0][:, a], atol=1e-14)
+    assert np.allclose(pb[0], full[0][:, b], atol=1e-14)
+    assert np.allclose(pa[1] + pb[1], full[1], atol=1e-12)
+    assert np.allclose(pa[2] + pb[2], full[2], atol=1e-12)
