@@ -359,10 +359,13 @@ hs_status launch_bwd(int op, const hs_problem* p, const void* q, const void* kv,
     a.plan_pre = reinterpret_cast<int*>(w + L.pre);
     if (kop == hs::kGather) {
       a.g_cnt = reinterpret_cast<int*>(w + L.cnt);
+      a.g_total = reinterpret_cast<int*>(w + L.total_g);
+      a.g_off = reinterpret_cast<int*>(w + L.off_g);
       a.g_rows = reinterpret_cast<int*>(w + L.rows);
     }
     a.part = reinterpret_cast<float*>(w + L.part);
     a.chunk_rows = L.chunk_rows;
+    a.n_chunks = L.n_chunks;
     a.items = L.items;
     a.row_tiles = L.row_tiles;
   }

@@ -47,6 +47,7 @@
 
 #include <algorithm>
 #include <cstring>
+#include <utility>
 
 #include "hs_common.h"
 #include "hs_kernels.h"
@@ -81,6 +82,39 @@ __device__ __forceinline__ int swz(int k) { return 3 * ((k >> 2) & 1) + 4 * ((k 
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <typename Fn, int... Is>
+__device__ __forceinline__ void static_for_impl(Fn&& fn, std::integer_sequence<int, Is...>) {
+  (fn(std::integral_constant<int, Is>{}), ...);
+}
+// fn(std::integral_constant<int, i>) for i = 0 .. N-1, with i a constant.
+template <int N, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& fn) {
+  static_for_impl(fn, std::make_integer_sequence<int, N>{});
+}
+
+// Operand stream: NF LDS fragments consumed in order, each requested LA
+// places ahead of its use into its own ring register, so that LA reads are in
+// flight while the MFMAs run (LDS reads complete in order; the compiler's
+// wait for fragment i then leaves the later ones pending). pre(i) runs before
+// fragment i is used; the scheduling barrier keeps this order.
+template <int NF, int LA, typename Load, typename Use, typename Pre>
+__device__ __forceinline__ void operand_stream(Load&& load, Use&& use, Pre&& pre) {
+  constexpr int RB = LA + 1;
+  bf16x8 fr[RB];
+  static_for<LA>([&](auto F) __attribute__((always_inline)) {
+    constexpr int f = decltype(F)::value;
+    fr[f % RB] = load(F);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  static_for<NF>([&](auto I) __attribute__((always_inline)) {
+    constexpr int i = decltype(I)::value;
+    pre(I);
+    use(I, fr[i % RB]);
+    if constexpr (i + LA < NF) fr[(i + LA) % RB] = load(std::integral_constant<int, i + LA>{});
+    __builtin_amdgcn_sched_barrier(0);
+  });
 }
 
 // One LDS DMA instruction: lane l copies 16 B from src to LDS byte lds + 16 l
@@ -255,56 +289,84 @@ __global__ __launch_bounds__(256) void bwd_gscan_kernel(BwdArgs a) {
     *c = run;
     run += v;
   }
-  a.plan_nrows[f] = run;
+  a.g_total[f] = run;
 }
 
-// Rows per block, list offsets (gather) and the first work item of each
-// block: one workgroup, each thread a contiguous segment of blocks.
+// Rows of work item (b, c, j): a range [*first, *first + n) of row indices,
+// or (gather) a range of positions in block j's row list.
+__host__ __device__ inline int item_rows(const Geom& g, int op, int b, int c, int j, int window,
+                                         int R, int T, const int* g_cnt, const int* g_total,
+                                         const int* g_off, int* first) {
+  if (op == kGather) {
+    const int f = b * g.NB + j;
+    const int t0 = c * (R / 64), t1 = (c + 1) * (R / 64);
+    const int s0 = g_cnt[((size_t)b * T + t0) * g.NB + j];
+    const int s1 = t1 < T ? g_cnt[((size_t)b * T + t1) * g.NB + j] : g_total[f];
+    *first = g_off[f] + s0;
+    return s1 - s0;
+  }
+  int bf;
+  const int n = block_row_range(g, op, b, j, window, &bf);
+  const int lo = bf > c * R ? bf : c * R;
+  const int hi = bf + n < (c + 1) * R ? bf + n : (c + 1) * R;
+  *first = lo;
+  return hi > lo ? hi - lo : 0;
+}
+
+// Work items of the key-block gradient (one workgroup): the gather's list
+// offsets first, then the rows of every (b, c, j) and the item prefix. Each
+// thread takes a contiguous segment; the segment totals are scanned in LDS.
 __global__ __launch_bounds__(256) void bwd_plan_kernel(BwdArgs a, int op) {
-  __shared__ int seg_rows[256], seg_items[256];
+  __shared__ int seg[256];
   const Geom& g = a.g;
-  const int F = g.B * g.NB;
-  const int per = (F + 255) / 256;
-  const int f0 = min(F, (int)threadIdx.x * per), f1 = min(F, f0 + per);
-  const int R = a.chunk_rows;
-  int rows = 0, items = 0;
-  for (int f = f0; f < f1; ++f) {
-    int n;
-    if (op == kGather) {
-      n = a.plan_nrows[f];
-    } else {
-      int first;
-      n = block_row_range(g, op, f / g.NB, f % g.NB, a.window, &first);
-      a.plan_first[f] = first;
-      a.plan_nrows[f] = n;
+  const int tid = threadIdx.x;
+  auto seg_scan = [&](int v) -> int {  // exclusive prefix of v over threads
+    seg[tid] = v;
+    __syncthreads();
+    if (tid == 0) {
+      int r = 0;
+      for (int t = 0; t < 256; ++t) {
+        const int x = seg[t];
+        seg[t] = r;
+        r += x;
+      }
     }
-    rows += n;
-    items += (n + R - 1) / R;
-  }
-  seg_rows[threadIdx.x] = rows;
-  seg_items[threadIdx.x] = items;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int r = 0, it = 0;
-    for (int t = 0; t < 256; ++t) {
-      const int vr = seg_rows[t], vi = seg_items[t];
-      seg_rows[t] = r;
-      seg_items[t] = it;
-      r += vr;
-      it += vi;
+    __syncthreads();
+    const int out = seg[tid];
+    __syncthreads();
+    return out;
+  };
+  if (op == kGather) {
+    const int FB = g.B * g.NB, per = (FB + 255) / 256;
+    const int f0 = min(FB, tid * per), f1 = min(FB, f0 + per);
+    int sum = 0;
+    for (int f = f0; f < f1; ++f) sum += a.g_total[f];
+    int run = seg_scan(sum);
+    for (int f = f0; f < f1; ++f) {
+      a.g_off[f] = run;
+      run += a.g_total[f];
     }
-    a.plan_pre[F] = min(it, a.items);
+    __syncthreads();
   }
-  __syncthreads();
-  rows = seg_rows[threadIdx.x];
-  items = seg_items[threadIdx.x];
+  const int C = a.n_chunks;
+  const int F = g.B * C * g.NB, per = (F + 255) / 256;
+  const int f0 = min(F, tid * per), f1 = min(F, f0 + per);
+  int cnt = 0;
   for (int f = f0; f < f1; ++f) {
-    const int n = a.plan_nrows[f];
-    if (op == kGather) a.plan_first[f] = rows;
-    a.plan_pre[f] = min(items, a.items);
-    rows += n;
-    items += (n + R - 1) / R;
+    const int j = f % g.NB, c = (f / g.NB) % C, b = f / (g.NB * C);
+    int first;
+    const int n = item_rows(g, op, b, c, j, a.window, a.chunk_rows, a.row_tiles, a.g_cnt,
+                            a.g_total, a.g_off, &first);
+    a.plan_first[f] = first;
+    a.plan_nrows[f] = n;
+    cnt += n > 0;
   }
+  int run = seg_scan(cnt);
+  for (int f = f0; f < f1; ++f) {
+    a.plan_pre[f] = min(run, a.items);
+    run += a.plan_nrows[f] > 0;
+  }
+  if (tid == 255) a.plan_pre[F] = min(run, a.items);
 }
 
 // Gather: row lists, each block's rows in ascending order. One wave walks
@@ -316,7 +378,7 @@ __global__ __launch_bounds__(256) void bwd_gfill_kernel(BwdArgs a) {
   const int T = a.row_tiles;
   const int b = blockIdx.x / T, tile = blockIdx.x % T;
   const int* cnt = a.g_cnt + ((size_t)b * T + tile) * g.NB;
-  for (int j = threadIdx.x; j < g.NB; j += 256) next[j] = a.plan_first[b * g.NB + j] + cnt[j];
+  for (int j = threadIdx.x; j < g.NB; j += 256) next[j] = a.g_off[b * g.NB + j] + cnt[j];
   __syncthreads();
   if (threadIdx.x >= 64) return;
   const int lane = threadIdx.x;
@@ -471,38 +533,46 @@ void bwd_dq_bf16_kernel(BwdArgs a) {
       stage_kv_tile(buf[(t + 1) & 1], kv_entry, nb.start, nb.len, wave, lane);
     }
 
+    // Stream: 72 K fragments (k-step ks, key block kb), each feeding the
+    // score MFMA and, for ks < 16, the dP MFMA; then 72 K^T fragments (k-step
+    // kk major, column block db) for dQ. P and dS are formed between the two.
+    constexpr int NP1 = 4 * KSTEPS, NF = NP1 + 2 * DBK;
     f32x4 s[4], dp[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dp[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const bf16x8 kf = frag(cur, GR, ks, kb, l16, grp);
-        s[kb] = mfma(kf, qreg[ks], s[kb]);
-        if (ks < VSTEPS) dp[kb] = mfma(kf, dreg[ks], dp[kb]);
-      }
-    }
-    // s[kb][i], dp[kb][i]: key 16 kb + 4 grp + i of the tile, head l16.
     bf16x8 dsb[2];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int k = 16 * kb + 4 * grp + i;
-        const float p =
-            (k >= klo && k <= khi) ? __builtin_amdgcn_exp2f(s[kb][i] * sl2 - lse2) : 0.f;
-        dsb[kb >> 1][4 * (kb & 1) + i] = (bf16)(p * (dp[kb][i] - dsum) * scale);
+    auto load = [&](auto F) __attribute__((always_inline)) -> bf16x8 {
+      constexpr int f = decltype(F)::value;
+      if constexpr (f < NP1) return frag(cur, GR, f / 4, f % 4, l16, grp);
+      else return frag_t(cur, GR, (f - NP1) / DBK, (f - NP1) % DBK, l16, grp);
+    };
+    auto use = [&](auto I, bf16x8 fr) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      if constexpr (i < NP1) {
+        constexpr int ks = i / 4, kb = i % 4;
+        s[kb] = mfma(fr, qreg[ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[kb]);
+        if constexpr (ks < VSTEPS)
+          dp[kb] = mfma(fr, dreg[ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : dp[kb]);
+      } else {
+        constexpr int kk = (i - NP1) / DBK, db = (i - NP1) % DBK;
+        acc[db] = mfma(fr, dsb[kk], acc[db]);
       }
-    }
+    };
+    auto pre = [&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      if constexpr (i == NP1) {
+        // s[kb][i], dp[kb][i]: key 16 kb + 4 grp + i of the tile, head l16.
 #pragma unroll
-    for (int db = 0; db < DBK; ++db) {
+        for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) acc[db] = mfma(frag_t(cur, GR, kk, db, l16, grp), dsb[kk], acc[db]);
-    }
+          for (int e = 0; e < 4; ++e) {
+            const int k = 16 * kb + 4 * grp + e;
+            const float p =
+                (k >= klo && k <= khi) ? __builtin_amdgcn_exp2f(s[kb][e] * sl2 - lse2) : 0.f;
+            dsb[kb >> 1][4 * (kb & 1) + e] = (bf16)(p * (dp[kb][e] - dsum) * scale);
+          }
+        }
+      }
+    };
+    operand_stream<NF, 6>(load, use, pre);
   }
   __builtin_amdgcn_s_waitcnt(0);
 
@@ -519,7 +589,8 @@ void bwd_dkv_bf16_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char stg[2][STAGE];
 
   const Geom& g = a.g;
-  const int F = g.B * g.NB;
+  const int C = a.n_chunks;
+  const int F = g.B * C * g.NB;
   const int item = blockIdx.x;
   if (item >= a.plan_pre[F]) return;
   int lo = 0, hi = F - 1;
@@ -528,10 +599,9 @@ void bwd_dkv_bf16_kernel(BwdArgs a) {
     if (a.plan_pre[mid] <= item) lo = mid; else hi = mid - 1;
   }
   const int f = lo;
-  const int b = f / g.NB, j = f % g.NB;
-  const int i0 = (item - a.plan_pre[f]) * a.chunk_rows;
-  const int n = min(a.chunk_rows, a.plan_nrows[f] - i0);
-  const int base_i = a.plan_first[f] + i0;
+  const int j = f % g.NB, b = f / (g.NB * C);
+  const int n = a.plan_nrows[f];
+  const int base_i = a.plan_first[f];
   auto row_at = [&](int i) -> int {
     const int rr = OP == kGather ? a.g_rows[base_i + i] : base_i + i;
     return min(max(rr, 0), g.Sq - 1);
@@ -589,36 +659,51 @@ void bwd_dkv_bf16_kernel(BwdArgs a) {
     __syncthreads();  // stage s resident; stage s-1 consumed by every wave
     if (s + 1 < 2 * n) stage(s + 1);
 
+    // Stream: 68 fragments of the staged rows for S and dP (per k-step: Q of
+    // head blocks 0 and 1, then dout of both while ks < 16), then 36 Q^T and
+    // 32 dout^T fragments for dKV. P and dS are formed between the two.
+    constexpr int NP1 = 2 * KSTEPS + 2 * VSTEPS, NF = NP1 + DBK + DBV;
     f32x4 sc[2], dp[2];
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      sc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dp[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        sc[hb] = mfma(frag(cur, HGR, ks, hb, l16, grp), kreg[ks], sc[hb]);
-        if (ks < VSTEPS) dp[hb] = mfma(frag(cur + QH, HGR, ks, hb, l16, grp), kreg[ks], dp[hb]);
-      }
-    }
-    // sc[hb][i], dp[hb][i]: head h0 + 16 hb + 4 grp + i, key kloc.
     bf16x8 pb, dsb;
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = valid ? __builtin_amdgcn_exp2f(sc[hb][i] * sl2 - lse2[hb][i]) : 0.f;
-        pb[4 * hb + i] = (bf16)p;
-        dsb[4 * hb + i] = (bf16)(p * (dp[hb][i] - ds[hb][i]) * scale);
+    // phase-1 fragment f: k-step, operand (0 = Q, 1 = dout) and head block
+    auto p1_ks = [](int f) constexpr { return f < 64 ? f >> 2 : 16 + ((f - 64) >> 1); };
+    auto p1_kind = [](int f) constexpr { return f < 64 ? (f & 3) >> 1 : 0; };
+    auto load = [&](auto F) __attribute__((always_inline)) -> bf16x8 {
+      constexpr int f = decltype(F)::value;
+      if constexpr (f < NP1) return frag(cur + (p1_kind(f) ? QH : 0), HGR, p1_ks(f), f & 1, l16, grp);
+      else if constexpr (f - NP1 < DBK) return frag_t(cur, HGR, 0, f - NP1, l16, grp);
+      else return frag_t(cur + QH, HGR, 0, f - NP1 - DBK, l16, grp);
+    };
+    auto use = [&](auto I, bf16x8 fr) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      if constexpr (i < NP1) {
+        constexpr int ks = p1_ks(i), hb = i & 1;
+        if constexpr (p1_kind(i) == 0)
+          sc[hb] = mfma(fr, kreg[ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sc[hb]);
+        else
+          dp[hb] = mfma(fr, kreg[ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : dp[hb]);
+      } else if constexpr (i - NP1 < DBK) {
+        acc[i - NP1] = mfma(fr, dsb, acc[i - NP1]);
+      } else {
+        acc[i - NP1 - DBK] = mfma(fr, pb, acc[i - NP1 - DBK]);
       }
-    }
+    };
+    auto pre = [&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      if constexpr (i == NP1) {
+        // sc[hb][e], dp[hb][e]: head h0 + 16 hb + 4 grp + e, key kloc.
 #pragma unroll
-    for (int db = 0; db < DBK; ++db) acc[db] = mfma(frag_t(cur, HGR, 0, db, l16, grp), dsb, acc[db]);
+        for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
-    for (int db = 0; db < DBV; ++db)
-      acc[db] = mfma(frag_t(cur + QH, HGR, 0, db, l16, grp), pb, acc[db]);
+          for (int e = 0; e < 4; ++e) {
+            const float p = valid ? __builtin_amdgcn_exp2f(sc[hb][e] * sl2 - lse2[hb][e]) : 0.f;
+            pb[4 * hb + e] = (bf16)p;
+            dsb[4 * hb + e] = (bf16)(p * (dp[hb][e] - ds[hb][e]) * scale);
+          }
+        }
+      }
+    };
+    operand_stream<NF, 6>(load, use, pre);
   }
   __builtin_amdgcn_s_waitcnt(0);
 
@@ -629,7 +714,7 @@ void bwd_dkv_bf16_kernel(BwdArgs a) {
 }
 
 // dkv rows of entry b, 64 at a time: each row sums its block's partials in
-// item order; rows past the entry's valid length are zero.
+// chunk order; rows past the entry's valid length are zero.
 __global__ __launch_bounds__(256) void bwd_reduce_bf16_kernel(BwdArgs a) {
   using namespace bw;
   const Geom& g = a.g;
@@ -645,9 +730,11 @@ __global__ __launch_bounds__(256) void bwd_reduce_bf16_kernel(BwdArgs a) {
       const Doc d = doc_of_pos(g, b, i);
       const int j = block_of_pos(g, d, i);
       const int k = i - (d.start + (j - d.blk0) * g.BS);
-      const int f = b * g.NB + j;
-      const int s0 = a.plan_pre[f], s1 = a.plan_pre[f + 1];
-      for (int s = s0; s < s1; ++s) v += *(const f32x4*)(a.part + ((size_t)s * BS + k) * DK + 4 * c4);
+      for (int c = 0; c < a.n_chunks; ++c) {
+        const int f = (b * a.n_chunks + c) * g.NB + j;
+        const int it = a.plan_pre[f];
+        if (a.plan_pre[f + 1] > it) v += *(const f32x4*)(a.part + ((size_t)it * BS + k) * DK + 4 * c4);
+      }
     }
     *(f32x4*)(a.dkv + ((size_t)b * g.Skv + i) * DK + 4 * c4) = v;
   }
@@ -873,40 +960,43 @@ BwdLayout bwd_layout(const Geom& g, int op, int top_k, int window, bool is_bf16)
   L.sink_part = off;
   off = align256(off + (size_t)L.n_pre * g.H * sizeof(float));
   if (is_bf16) {
-    const size_t F = (size_t)g.B * g.NB;
     L.row_tiles = (g.Sq + 63) / 64;
+    // Row chunk R: the largest power of two from 1024 down to 64 that still
+    // gives about 1024 work items (four per compute unit). At R = 1024 the Q
+    // and dout rows of one chunk (142 MB) stay in the 256 MB last-level cache
+    // while the chunk's items run.
+    auto items_for = [&](int R) -> long {
+      const int C = (g.Sq + R - 1) / R;
+      long it = 0;
+      const int oc = op == kSwa ? kSwa : kScore;  // gather rows lie in the causal ones
+      for (int b = 0; b < g.B; ++b)
+        for (int c = 0; c < C; ++c)
+          for (int j = 0; j < g.NB; ++j) {
+            int first;
+            it += item_rows(g, oc, b, c, j, window, R, 0, nullptr, nullptr, nullptr, &first) > 0;
+          }
+      return it;
+    };
+    int R = 1024;
+    while (R > 64 && items_for(R) < 1024) R >>= 1;
+    L.chunk_rows = R;
+    L.n_chunks = (g.Sq + R - 1) / R;
+    L.items = (int)items_for(R);
+    const size_t F = (size_t)g.B * L.n_chunks * g.NB;
     L.first = off;
     off = align256(off + F * sizeof(int));
     L.nrows = off;
     off = align256(off + F * sizeof(int));
     L.pre = off;
     off = align256(off + (F + 1) * sizeof(int));
-    // Rows per work item: the largest power of two from 4096 down to 64 that
-    // still gives about 2048 items (eight per compute unit).
-    auto items_for = [&](int R, long* pairs) -> long {
-      long it = 0, pr = 0;
-      if (op == kGather) {
-        pr = (long)g.B * g.Sq * std::min(top_k, g.NB);
-        it = (pr + R - 1) / R + std::min<long>((long)F, pr);
-      } else {
-        for (int b = 0; b < g.B; ++b)
-          for (int j = 0; j < g.NB; ++j) {
-            int first;
-            const int n = block_row_range(g, op, b, j, window, &first);
-            pr += n;
-            it += (n + R - 1) / R;
-          }
-      }
-      if (pairs) *pairs = pr;
-      return it;
-    };
-    int R = 4096;
-    while (R > 64 && items_for(R, nullptr) < 2048) R >>= 1;
-    L.chunk_rows = R;
-    L.items = (int)items_for(R, nullptr);
     if (op == kGather) {
+      const size_t FB = (size_t)g.B * g.NB;
       L.cnt = off;
       off = align256(off + (size_t)g.B * L.row_tiles * g.NB * sizeof(int));
+      L.total_g = off;
+      off = align256(off + FB * sizeof(int));
+      L.off_g = off;
+      off = align256(off + FB * sizeof(int));
       L.rows = off;
       off = align256(off + rows * std::max(top_k, 1) * sizeof(int));
     }

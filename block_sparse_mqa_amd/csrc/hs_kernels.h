@@ -69,13 +69,19 @@ struct BwdArgs {
   float* dsum;               // [B * Sq * H] dout . out per row and head
   float* sink_part;          // [n_pre, H] per-workgroup sink-gradient partials
   int n_pre, rows_per_pre;
-  int* plan_first;           // [B * NB] first row (range) or list offset (gather)
-  int* plan_nrows;           // [B * NB] rows that reach the block
-  int* plan_pre;             // [B * NB + 1] first work item of each block
+  // Key-block gradient work items: one per (entry b, row chunk c, block j)
+  // whose row set is not empty, in the order (b, c, j), so that the items
+  // running together share the same query rows.
+  int* plan_first;           // [B * C * NB] first row (range) or list position (gather)
+  int* plan_nrows;           // [B * C * NB] rows of the item (0: no item)
+  int* plan_pre;             // [B * C * NB + 1] item index (exclusive prefix)
   int* g_cnt;                // gather: [B, T, NB] per-row-tile counts, then offsets
-  int* g_rows;               // gather: row lists of all blocks
+  int* g_total;              // gather: [B * NB] rows that selected each block
+  int* g_off;                // gather: [B * NB] start of each block's row list
+  int* g_rows;               // gather: row lists of all blocks, rows ascending
   float* part;               // [items, 64, Dk] per-item key-block gradient partials
-  int chunk_rows;            // rows per work item
+  int chunk_rows;            // R: rows per chunk (multiple of 64)
+  int n_chunks;              // C = ceil(Sq / R)
   int items;                 // work items launched (exact or an upper bound)
   int row_tiles;             // T = ceil(Sq / 64)
   Geom g;
@@ -84,8 +90,8 @@ struct BwdArgs {
 // Workspace layout of one gradient call: byte offsets of each piece and the
 // total, plus the work split of the key-block gradient.
 struct BwdLayout {
-  size_t dsum, sink_part, first, nrows, pre, cnt, rows, part, total;
-  int n_pre, rows_per_pre, chunk_rows, items, row_tiles;
+  size_t dsum, sink_part, first, nrows, pre, cnt, total_g, off_g, rows, part, total;
+  int n_pre, rows_per_pre, chunk_rows, n_chunks, items, row_tiles;
 };
 
 BwdLayout bwd_layout(const Geom& g, int op, int top_k, int window, bool bf16);
