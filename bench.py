@@ -303,6 +303,24 @@ def suite_config(c, dev, stream, peaks, oracle_budget):
     }
     calls["block_score"](); calls["topk"](); torch.cuda.synchronize()
     idx_cpu = idx.cpu().numpy()
+    # Gradients of the three attention calls, each from its own forward outputs.
+    dout = inputs.make_dout(p, seed=900 + c).to(dev)
+    fwd = {}
+    for op_name, fn in (("block_score", calls["block_score"]), ("sparse_gather", calls["sparse_gather"]),
+                        ("swa", calls["swa"])):
+        fn(); torch.cuda.synchronize()
+        fwd[op_name] = (out.clone(), lse.clone())
+    dq = torch.empty((p.B, p.Sq, p.H, p.Dk), dtype=torch.float32, device=dev)
+    dkv = torch.empty((p.B, p.Skv, p.Dk), dtype=torch.float32, device=dev)
+    dsink = torch.empty((p.H,), dtype=torch.float32, device=dev)
+    wb1, wb3, wb4 = ws(hs.HS_OP_BLOCK_SCORE_BWD), ws(hs.HS_OP_SPARSE_GATHER_BWD, top_k=p.top_k), \
+        ws(hs.HS_OP_SWA_BWD, window=p.window)
+    calls["block_score_bwd"] = lambda: hs.hs_block_score_bwd(
+        prob, q, kv, sink, *fwd["block_score"], dout, dq, dkv, dsink, wb1, stream)
+    calls["sparse_gather_bwd"] = lambda: hs.hs_sparse_gather_bwd(
+        prob, q, kv, sink, idx, p.top_k, *fwd["sparse_gather"], dout, dq, dkv, dsink, wb3, stream)
+    calls["swa_bwd"] = lambda: hs.hs_swa_bwd(
+        prob, q, kv, sink, p.window, *fwd["swa"], dout, dq, dkv, dsink, wb4, stream)
     causal, window, gather, kv_rows = row_key_counts(p, idx_cpu)
     fpp, H, es = 2 * p.Dk + 2 * p.Dv, p.H, (2 if p.dtype == "bf16" else 4)
     qb, ob, lb = p.B * p.Sq * H * p.Dk * es, p.B * p.Sq * H * p.Dv * es, p.B * p.Sq * H * 4
@@ -316,6 +334,16 @@ def suite_config(c, dev, stream, peaks, oracle_budget):
                           qb + ob + lb + p.B * p.Sq * p.top_k * 4 + int(gather.sum()) * p.Dk * es),
         "swa": (int(window.sum()) * H * fpp, qb + kv_rows["swa"] * p.Dk * es + ob + lb),
     }
+    # Gradients: five contractions per pair (S recomputed, dP, dQ, dK, dV), i.e.
+    # 2 (3 Dk + 2 Dv) flops; bytes: q, kv rows, out, dout, lse, dq and dkv in fp32.
+    fpb = 2 * (3 * p.Dk + 2 * p.Dv)
+    gb = qb + 2 * ob + lb + p.B * p.Sq * H * p.Dk * 4
+    work["block_score_bwd"] = (int(causal.sum()) * H * fpb,
+                               gb + kv_rows["score"] * p.Dk * (es + 4))
+    work["sparse_gather_bwd"] = (int(gather.sum()) * H * fpb,
+                                 gb + p.B * p.Sq * p.top_k * 4 + int(gather.sum()) * p.Dk * es +
+                                 kv_rows["score"] * p.Dk * 4)
+    work["swa_bwd"] = (int(window.sum()) * H * fpb, gb + kv_rows["swa"] * p.Dk * (es + 4))
     peak_f = PEAK_BF16_TFLOPS if p.dtype == "bf16" else PEAK_F32_TFLOPS
     meas_f = peaks["mfma_bf16_tflop_s"] if p.dtype == "bf16" else None
     scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -338,7 +366,7 @@ def suite_config(c, dev, stream, peaks, oracle_budget):
                    "frac_vendor": round(t_roof / warm, 4),
                    "frac_measured_peak": round(t_roof_m / warm, 4) if (meas_f or bound == "hbm") else None}
         print(f"[suite] workload {c} {k}: {rows[k]}", file=sys.stderr, flush=True)
-    del scratch
+    del scratch, dq, dkv, dout, fwd
     path_ms = rows["block_score"]["ms_warm"] + rows["topk"]["ms_warm"] + rows["sparse_gather"]["ms_warm"]
     res = {"workload": p.name, "dtype": p.dtype, "kernels": rows,
            "metric_path_ms": round(path_ms, 4),
@@ -395,6 +423,12 @@ def write_suite_md(path, peaks, results, args):
                      f"{v['tflop']:.3f} | {v['gb_alg']:.3f} | {v['bound']} | {ts} | {v['gb_s_alg']:.0f} | "
                      f"{v['frac_vendor']:.3f} | {fm} |")
     L.append("")
+    L.append("`*_bwd` are the gradient calls (dq, dkv and the sink gradient) of the three attention "
+             "operations, each fed its own forward outputs; their flops are 2 (3 Dk + 2 Dv) per "
+             "(query-head, key) pair (score recomputed, dP, dQ, dK, dV) and their bytes count q, the "
+             "KV rows, out, dout, lse and the fp32 dq and dkv. The implementation recomputes the "
+             "scores and dP in both of its kernels, so the MFMA pipe executes 1.4 times the counted "
+             "flops.\n")
     L.append("`score_topk_fused` is `hs_block_score_topk_fwd` (block scores and the top-k in one call; "
              "its work is counted as the block score's). Metric path (block score + top-k + gather; "
              "with the fused call in place of the first two) and the float64 oracle on the host:\n")
