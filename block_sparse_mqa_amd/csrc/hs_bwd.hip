@@ -514,6 +514,7 @@ void bwd_dq_bf16_kernel(BwdArgs a) {
   }
   const float lse2 = a.lse[row * H + head] * kLog2e;
   const float dsum = a.dsum[row * H + head];
+  const int cp_c8 = (lane & 7) ^ swz(8 * wave + (lane >> 3));  // copy: chunk of this lane
   const float sl2 = g.scale_log2;
   const float scale = g.scale_log2 * kLn2;
 
@@ -528,10 +529,15 @@ void bwd_dq_bf16_kernel(BwdArgs a) {
     const int klo = rr.lo - blk.start, khi = min(rr.hi - blk.start, blk.len - 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // tile t resident; tile t-1 consumed by every wave
-    if (t + 1 < ntiles) {
-      const Blk nb = block_rows(g, b, tile_block(t + 1));
-      stage_kv_tile(buf[(t + 1) & 1], kv_entry, nb.start, nb.len, wave, lane);
-    }
+    // The copy of the next tile is spread over the first 36 MFMAs of the
+    // stream. On the last tile the current block is copied again into the
+    // idle buffer, which keeps the stream free of branches; nothing reads it.
+    const Blk nbk = t + 1 < ntiles ? block_rows(g, b, tile_block(t + 1)) : blk;
+    const int cka = min(8 * wave + (lane >> 3), nbk.len - 1);
+    const int ckb = min(8 * (wave + 4) + (lane >> 3), nbk.len - 1);
+    const char* cp_a = (const char*)(kv_entry + (size_t)(nbk.start + cka) * DK) + 16 * cp_c8;
+    const char* cp_b = (const char*)(kv_entry + (size_t)(nbk.start + ckb) * DK) + 16 * cp_c8;
+    char* cp_dst = buf[(t + 1) & 1] + wave * 1024;
 
     // Stream: 72 K fragments (k-step ks, key block kb), each feeding the
     // score MFMA and, for ks < 16, the dP MFMA; then 72 K^T fragments (k-step
@@ -558,6 +564,11 @@ void bwd_dq_bf16_kernel(BwdArgs a) {
     };
     auto pre = [&](auto I) __attribute__((always_inline)) {
       constexpr int i = decltype(I)::value;
+      if constexpr (i < 36 && (i & 3) == 3) {
+        constexpr int G = i >> 2;
+        dma16(cp_a + 128 * G, cp_dst + G * GR);
+        dma16(cp_b + 128 * G, cp_dst + G * GR + 4096);
+      }
       if constexpr (i == NP1) {
         // s[kb][i], dp[kb][i]: key 16 kb + 4 grp + i of the tile, head l16.
 #pragma unroll
@@ -632,6 +643,8 @@ void bwd_dkv_bf16_kernel(BwdArgs a) {
   }
   const float sl2 = g.scale_log2;
   const float scale = g.scale_log2 * kLn2;
+  const int cp_hr = 8 * wave + (lane >> 3);       // copy: head row of this lane
+  const int cp_c8 = (lane & 7) ^ swz(cp_hr);      // and its chunk
 
   f32x4 acc[DBK];
 #pragma unroll
@@ -657,7 +670,15 @@ void bwd_dkv_bf16_kernel(BwdArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // stage s resident; stage s-1 consumed by every wave
-    if (s + 1 < 2 * n) stage(s + 1);
+    // The copy of the next stage is spread over the 68 MFMAs of phase 1: Q
+    // groups at positions 3, 7, .., 35, dout groups at 39, .., 67. The last
+    // stage copies itself again into the idle buffer (nothing reads it).
+    const int sn = s + 1 < 2 * n ? s + 1 : s;
+    const size_t rwn = (size_t)b * g.Sq + row_at(sn >> 1);
+    const int hn = 32 * (sn & 1) + cp_hr;
+    const char* cq = (const char*)(q + (rwn * H + hn) * DK) + 16 * cp_c8;
+    const char* cd = (const char*)(dout + (rwn * H + hn) * DV) + 16 * cp_c8;
+    char* cp_dst = stg[(s + 1) & 1] + wave * 1024;
 
     // Stream: 68 fragments of the staged rows for S and dP (per k-step: Q of
     // head blocks 0 and 1, then dout of both while ks < 16), then 36 Q^T and
@@ -690,6 +711,11 @@ void bwd_dkv_bf16_kernel(BwdArgs a) {
     };
     auto pre = [&](auto I) __attribute__((always_inline)) {
       constexpr int i = decltype(I)::value;
+      if constexpr (i < NP1 && (i & 3) == 3) {
+        constexpr int G = i >> 2;
+        if constexpr (G < 9) dma16(cq + 128 * G, cp_dst + G * HGR);
+        else dma16(cd + 128 * (G - 9), cp_dst + QH + (G - 9) * HGR);
+      }
       if constexpr (i == NP1) {
         // sc[hb][e], dp[hb][e]: head h0 + 16 hb + 4 grp + e, key kloc.
 #pragma unroll
