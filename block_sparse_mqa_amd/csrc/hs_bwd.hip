@@ -242,12 +242,20 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   }
 }
 
-__global__ __launch_bounds__(64) void bwd_sink_kernel(BwdArgs a) {
-  const int h = threadIdx.x;
-  if (h >= a.g.H) return;
+// One workgroup per head: thread t sums partials t, t + 256, .. in order,
+// then a fixed tree over the 256 threads.
+__global__ __launch_bounds__(256) void bwd_sink_kernel(BwdArgs a) {
+  __shared__ float red[256];
+  const int h = blockIdx.x, t = threadIdx.x;
   float s = 0.f;
-  for (int w = 0; w < a.n_pre; ++w) s += a.sink_part[(size_t)w * a.g.H + h];
-  a.dsink[h] = s;
+  for (int w = t; w < a.n_pre; w += 256) s += a.sink_part[(size_t)w * a.g.H + h];
+  red[t] = s;
+  __syncthreads();
+  for (int k = 128; k >= 1; k >>= 1) {
+    if (t < k) red[t] += red[t + k];
+    __syncthreads();
+  }
+  if (t == 0) a.dsink[h] = red[0];
 }
 
 // ---------------------------------------------------------------------------
@@ -583,7 +591,7 @@ void bwd_dq_bf16_kernel(BwdArgs a) {
         }
       }
     };
-    operand_stream<NF, 6>(load, use, pre);
+    operand_stream<NF, 8>(load, use, pre);
   }
   __builtin_amdgcn_s_waitcnt(0);
 
@@ -729,7 +737,7 @@ void bwd_dkv_bf16_kernel(BwdArgs a) {
         }
       }
     };
-    operand_stream<NF, 6>(load, use, pre);
+    operand_stream<NF, 8>(load, use, pre);
   }
   __builtin_amdgcn_s_waitcnt(0);
 
@@ -1036,7 +1044,7 @@ BwdLayout bwd_layout(const Geom& g, int op, int top_k, int window, bool is_bf16)
 int bwd_launch(int op, const BwdArgs& a, bool is_bf16, hipStream_t s) {
   if (is_bf16) hipLaunchKernelGGL(bwd_pre_kernel<bf16>, dim3(a.n_pre), dim3(256), 0, s, a);
   else hipLaunchKernelGGL(bwd_pre_kernel<float>, dim3(a.n_pre), dim3(256), 0, s, a);
-  if (a.dsink != nullptr) hipLaunchKernelGGL(bwd_sink_kernel, dim3(1), dim3(64), 0, s, a);
+  if (a.dsink != nullptr) hipLaunchKernelGGL(bwd_sink_kernel, dim3(a.g.H), dim3(256), 0, s, a);
   if (is_bf16) {
     if (op == kScore) launch_bf16<kScore>(a, s);
     else if (op == kGather) launch_bf16<kGather>(a, s);
