@@ -995,10 +995,10 @@ BwdLayout bwd_layout(const Geom& g, int op, int top_k, int window, bool is_bf16)
   off = align256(off + (size_t)L.n_pre * g.H * sizeof(float));
   if (is_bf16) {
     L.row_tiles = (g.Sq + 63) / 64;
-    // Row chunk R: the largest power of two from 1024 down to 64 that still
-    // gives about 1024 work items (four per compute unit). At R = 1024 the Q
-    // and dout rows of one chunk (142 MB) stay in the 256 MB last-level cache
-    // while the chunk's items run.
+    // Row chunk R: the largest power of two from 512 down to 64 that still
+    // gives about 1024 work items (four per compute unit). At R = 512 the Q
+    // and dout rows of one chunk (71 MB) stay in the 256 MB last-level cache
+    // while the chunk's items run (1024 and 256 measured within 2 % of it).
     auto items_for = [&](int R) -> long {
       const int C = (g.Sq + R - 1) / R;
       long it = 0;
@@ -1011,7 +1011,7 @@ BwdLayout bwd_layout(const Geom& g, int op, int top_k, int window, bool is_bf16)
           }
       return it;
     };
-    int R = 1024;
+    int R = 512;
     while (R > 64 && items_for(R) < 1024) R >>= 1;
     L.chunk_rows = R;
     L.n_chunks = (g.Sq + R - 1) / R;
