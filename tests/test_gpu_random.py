@@ -2,8 +2,9 @@
 pin down. Each case draws a kind (one sequence, a batch of entries with their
 own cache lengths, packed documents, or single-token decode), its sizes, top-k,
 window and whether a sink is passed, then runs the four calls against the
-oracle exactly as the fixed cases do, and checks that the fused block score +
-top-k call writes what the two separate calls write. The bf16 cases use the
+oracle exactly as the fixed cases do, checks that the fused block score +
+top-k call writes what the two separate calls write, and checks the gradients
+of the three attention calls against the oracle's. The bf16 cases use the
 absorbed-MLA shape, the fp32 cases the small shape (8 heads, Dk 96, Dv 64)."""
 import numpy as np
 import pytest
@@ -12,7 +13,8 @@ import torch
 import block_sparse_mqa_amd as hs
 from block_sparse_mqa_amd import inputs
 
-from gpu_common import Dev, say
+from gpu_common import Dev, np64, say
+from test_gpu_bwd import _gpu_grads, _grad_close, _oracle_grads
 from test_gpu_parity import MLA, _run_all
 
 pytestmark = pytest.mark.gpu
@@ -70,4 +72,16 @@ def test_random_case(i):
     torch.cuda.synchronize()
     for n, f, s in zip(("out", "lse", "block_logit", "block_idx"), fused, (out, lse, bl, idx)):
         assert torch.equal(f, s), f"fused {n} differs from the separate calls"
+    dout_cpu = inputs.make_dout(p, seed=7500 + i)
+    dout = dout_cpu.cuda()
+    idx_cpu = idx.cpu().numpy()
+    for op in ("score", "swa", "gather"):
+        g = _gpu_grads(d, op, dout, idx, p.top_k)
+        torch.cuda.synchronize()
+        w = _oracle_grads(d, op, dout_cpu, idx_cpu)
+        for k, name in enumerate(("dq", "dkv", "dsink")):
+            if w[k] is None:
+                assert g[k] is None
+            else:
+                res[f"{op}_{name}"] = _grad_close(np64(g[k]), w[k], p.dtype, f"{op} {name}")
     say(f"[gpu] random case {i}: {res}")
