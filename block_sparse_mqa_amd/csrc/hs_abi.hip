@@ -353,7 +353,7 @@ hs_status launch_bwd(int op, const hs_problem* p, const void* q, const void* kv,
   a.sink_part = reinterpret_cast<float*>(w + L.sink_part);
   a.n_pre = L.n_pre;
   a.rows_per_pre = L.rows_per_pre;
-  if (bf16) {
+  {
     a.plan_first = reinterpret_cast<int*>(w + L.first);
     a.plan_nrows = reinterpret_cast<int*>(w + L.nrows);
     a.plan_pre = reinterpret_cast<int*>(w + L.pre);

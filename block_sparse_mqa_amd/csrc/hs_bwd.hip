@@ -863,75 +863,93 @@ __global__ __launch_bounds__(f32b::NT) void bwd_dq_f32_kernel(BwdArgs a) {
   }
 }
 
-// One workgroup per (entry, key block); the last B workgroups zero the rows
-// past each entry's valid length.
+// One workgroup per work item (rows of one key block, as for bf16): the item's
+// rows in turn, the next row's q, dout, lse and D fetched into registers while
+// the current one is processed; partial dkv of the block's 64 keys.
 template <int OP>
 __global__ __launch_bounds__(f32b::NT) void bwd_dkv_f32_kernel(BwdArgs a) {
   using namespace f32b;
-  __shared__ float ks[BS * KS], qs[MAXH * MAXD], dos[MAXH * MAXD], ps[MAXH * BS], dss[MAXH * BS];
-  __shared__ float lse2[MAXH], dsum[MAXH];
-  __shared__ int take;
+  __shared__ float ks[BS * KS], qs[2][MAXH * MAXD], dos[2][MAXH * MAXD], ps[MAXH * BS],
+      dss[MAXH * BS];
+  __shared__ float lse2[2][MAXH], dsum[2][MAXH];
   const Geom& g = a.g;
   const int H = g.H, Dk = g.Dk, Dv = g.Dv, tid = threadIdx.x;
+  const int C = a.n_chunks;
+  const int F = g.B * C * g.NB;
+  const int item = blockIdx.x;
+  if (item >= a.plan_pre[F]) return;
+  int lo = 0, hi = F - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.plan_pre[mid] <= item) lo = mid; else hi = mid - 1;
+  }
+  const int f = lo;
+  const int j = f % g.NB, b = f / (g.NB * C);
+  const int n = a.plan_nrows[f];
+  const int base_i = a.plan_first[f];
+  auto row_at = [&](int i) -> int {
+    const int rr = OP == kGather ? a.g_rows[base_i + i] : base_i + i;
+    return min(max(rr, 0), g.Sq - 1);
+  };
   const float* q = static_cast<const float*>(a.q);
   const float* kv = static_cast<const float*>(a.kv);
   const float* dout = static_cast<const float*>(a.dout);
-  if ((int)blockIdx.x >= g.B * g.NB) {
-    const int b = blockIdx.x - g.B * g.NB;
-    const int L = kv_len_of(g, b);
-    for (size_t i = (size_t)L * Dk + tid; i < (size_t)g.Skv * Dk; i += NT)
-      a.dkv[(size_t)b * g.Skv * Dk + i] = 0.f;
-    return;
-  }
-  const int b = blockIdx.x / g.NB, j = blockIdx.x % g.NB;
-  const int nb_b = nb_of_entry(g, b);
-  if (j >= nb_b) return;
   const Blk blk = block_rows(g, b, j);
   const float* kv_entry = kv + (size_t)b * g.Skv * Dk;
   for (int i = tid; i < BS * Dk; i += NT) {
     const int k = i / Dk, d = i % Dk;
     ks[k * KS + d] = kv_entry[(size_t)(blk.start + min(k, blk.len - 1)) * Dk + d];
   }
-  // Candidate rows: the causal range of the block (the window and gather
-  // sets lie inside it).
-  int first;
-  const int n = block_row_range(g, OP == kSwa ? kSwa : kScore, b, j, a.window, &first);
+  // Row data of this thread: q and dout elements tid + NT m, lse and D of head tid.
+  float rq[MAXQ], rd[MAXQ], rl = 0.f, rs = 0.f;
+  auto fetch = [&](int ri) {
+    const size_t row = (size_t)b * g.Sq + row_at(ri);
+#pragma unroll
+    for (int m = 0; m < MAXQ; ++m) {
+      const int e = tid + NT * m;
+      rq[m] = e < H * Dk ? q[row * H * Dk + e] : 0.f;
+      rd[m] = e < H * Dv ? dout[row * H * Dv + e] : 0.f;
+    }
+    if (tid < H) {
+      rl = a.lse[row * H + tid] * kLog2e;
+      rs = a.dsum[row * H + tid];
+    }
+  };
+  auto put = [&](int buf) {
+#pragma unroll
+    for (int m = 0; m < MAXQ; ++m) {
+      const int e = tid + NT * m;
+      if (e < H * Dk) qs[buf][(e / Dk) * MAXD + e % Dk] = rq[m];
+      if (e < H * Dv) dos[buf][(e / Dv) * MAXD + e % Dv] = rd[m];
+    }
+    if (tid < H) {
+      lse2[buf][tid] = rl;
+      dsum[buf][tid] = rs;
+    }
+  };
+  if (n > 0) {
+    fetch(0);
+    put(0);
+  }
   const float sl2 = g.scale_log2, scale = g.scale_log2 * kLn2;
   float acc[MAXK];
 #pragma unroll
   for (int m = 0; m < MAXK; ++m) acc[m] = 0.f;
+  __syncthreads();
   for (int ri = 0; ri < n; ++ri) {
-    const int r = first + ri;
-    const size_t row = (size_t)b * g.Sq + r;
-    const RowRange rr = row_range(g, OP, b, r, a.window);
-    __syncthreads();
-    if (tid == 0) {
-      bool hit = true;
-      if (OP == kGather) {
-        hit = false;
-        for (int k = 0; k < a.top_k; ++k)
-          if (a.block_idx[row * a.top_k + k] == j && gather_hit(g, b, nb_b, rr, j)) hit = true;
-      }
-      take = hit;
-    }
-    for (int i = tid; i < H * Dk; i += NT) qs[(i / Dk) * MAXD + i % Dk] = q[row * H * Dk + i];
-    for (int i = tid; i < H * Dv; i += NT) dos[(i / Dv) * MAXD + i % Dv] = dout[row * H * Dv + i];
-    if (tid < H) {
-      lse2[tid] = a.lse[row * H + tid] * kLog2e;
-      dsum[tid] = a.dsum[row * H + tid];
-    }
-    __syncthreads();
-    if (!take) continue;
+    const int cb = ri & 1;
+    if (ri + 1 < n) fetch(ri + 1);
+    const RowRange rr = row_range(g, OP, b, row_at(ri), a.window);
     for (int i = tid; i < H * BS; i += NT) {
       const int h = i / BS, k = i % BS;
-      float s = 0.f, dp = 0.f;
-      for (int d = 0; d < Dk; ++d) s = fmaf(qs[h * MAXD + d], ks[k * KS + d], s);
-      for (int d = 0; d < Dv; ++d) dp = fmaf(dos[h * MAXD + d], ks[k * KS + d], dp);
+      float sv = 0.f, dp = 0.f;
+      for (int d = 0; d < Dk; ++d) sv = fmaf(qs[cb][h * MAXD + d], ks[k * KS + d], sv);
+      for (int d = 0; d < Dv; ++d) dp = fmaf(dos[cb][h * MAXD + d], ks[k * KS + d], dp);
       const int key = blk.start + k;
       const bool ok = k < blk.len && key >= rr.lo && key <= rr.hi;
-      const float p = ok ? exp2f(s * sl2 - lse2[h]) : 0.f;
+      const float p = ok ? exp2f(sv * sl2 - lse2[cb][h]) : 0.f;
       ps[i] = p;
-      dss[i] = p * (dp - dsum[h]) * scale;
+      dss[i] = p * (dp - dsum[cb][h]) * scale;
     }
     __syncthreads();
 #pragma unroll
@@ -940,17 +958,45 @@ __global__ __launch_bounds__(f32b::NT) void bwd_dkv_f32_kernel(BwdArgs a) {
       if (e < BS * Dk) {
         const int k = e / Dk, d = e % Dk;
         float v = acc[m];
-        for (int h = 0; h < H; ++h) v = fmaf(dss[h * BS + k], qs[h * MAXD + d], v);
+        for (int h = 0; h < H; ++h) v = fmaf(dss[h * BS + k], qs[cb][h * MAXD + d], v);
         if (d < Dv)
-          for (int h = 0; h < H; ++h) v = fmaf(ps[h * BS + k], dos[h * MAXD + d], v);
+          for (int h = 0; h < H; ++h) v = fmaf(ps[h * BS + k], dos[cb][h * MAXD + d], v);
         acc[m] = v;
       }
     }
+    if (ri + 1 < n) put(cb ^ 1);
+    __syncthreads();
   }
 #pragma unroll
   for (int m = 0; m < MAXK; ++m) {
     const int e = tid + NT * m;
-    if (e < blk.len * Dk) a.dkv[((size_t)b * g.Skv + blk.start) * Dk + e] = acc[m];
+    if (e < BS * Dk) a.part[(size_t)item * BS * Dk + e] = acc[m];
+  }
+}
+
+// dkv rows of entry b, 64 at a time, any width: each row sums its block's
+// partials in chunk order; rows past the entry's valid length are zero.
+__global__ __launch_bounds__(256) void bwd_reduce_f32_kernel(BwdArgs a) {
+  const Geom& g = a.g;
+  const int Dk = g.Dk;
+  const int chunks = (g.Skv + 63) / 64;
+  const int b = blockIdx.x / chunks, c = blockIdx.x % chunks;
+  const int L = kv_len_of(g, b);
+  for (int e = threadIdx.x; e < 64 * Dk; e += 256) {
+    const int i = 64 * c + e / Dk, d = e % Dk;
+    if (i >= g.Skv) break;
+    float v = 0.f;
+    if (i < L) {
+      const Doc dc = doc_of_pos(g, b, i);
+      const int j = block_of_pos(g, dc, i);
+      const int k = i - (dc.start + (j - dc.blk0) * g.BS);
+      for (int cc = 0; cc < a.n_chunks; ++cc) {
+        const int f = (b * a.n_chunks + cc) * g.NB + j;
+        const int it = a.plan_pre[f];
+        if (a.plan_pre[f + 1] > it) v += a.part[((size_t)it * 64 + k) * Dk + d];
+      }
+    }
+    a.dkv[((size_t)b * g.Skv + i) * Dk + d] = v;
   }
 }
 
@@ -976,13 +1022,23 @@ void launch_bf16(const BwdArgs& a, hipStream_t s) {
 template <int OP>
 void launch_f32(const BwdArgs& a, hipStream_t s) {
   const Geom& g = a.g;
+  const unsigned F = (unsigned)(g.B * g.NB);  // blocks of all entries
+  if (OP == kGather) {
+    hipLaunchKernelGGL(bwd_gcount_kernel, dim3(g.B * a.row_tiles), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(bwd_gscan_kernel, dim3((F + 255) / 256), dim3(256), 0, s, a);
+  }
+  hipLaunchKernelGGL(bwd_plan_kernel, dim3(1), dim3(256), 0, s, a, OP);
+  if (OP == kGather)
+    hipLaunchKernelGGL(bwd_gfill_kernel, dim3(g.B * a.row_tiles), dim3(256), 0, s, a);
   hipLaunchKernelGGL(bwd_dq_f32_kernel<OP>, dim3(g.B * g.Sq), dim3(f32b::NT), 0, s, a);
-  hipLaunchKernelGGL(bwd_dkv_f32_kernel<OP>, dim3(g.B * g.NB + g.B), dim3(f32b::NT), 0, s, a);
+  if (a.items > 0)
+    hipLaunchKernelGGL(bwd_dkv_f32_kernel<OP>, dim3(a.items), dim3(f32b::NT), 0, s, a);
+  hipLaunchKernelGGL(bwd_reduce_f32_kernel, dim3(g.B * ((g.Skv + 63) / 64)), dim3(256), 0, s, a);
 }
 
 }  // namespace
 
-BwdLayout bwd_layout(const Geom& g, int op, int top_k, int window, bool is_bf16) {
+BwdLayout bwd_layout(const Geom& g, int op, int top_k, int window, bool) {
   BwdLayout L;
   std::memset(&L, 0, sizeof(L));
   const size_t rows = (size_t)g.B * g.Sq;
@@ -993,7 +1049,7 @@ BwdLayout bwd_layout(const Geom& g, int op, int top_k, int window, bool is_bf16)
   off = align256(off + rows * g.H * sizeof(float));
   L.sink_part = off;
   off = align256(off + (size_t)L.n_pre * g.H * sizeof(float));
-  if (is_bf16) {
+  {
     L.row_tiles = (g.Sq + 63) / 64;
     // Row chunk R: the largest power of two from 512 down to 64 that still
     // gives about 1024 work items (four per compute unit). At R = 512 the Q
