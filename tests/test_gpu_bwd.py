@@ -183,3 +183,68 @@ def test_long_context_sampled():
         _grad_close(dkv_last, w[1][:, S - 64:], "bf16", f"{op} dkv last block")
         del g
     say("[gpu] gradients long context: ok")
+
+
+def test_gradients_in_captured_graph():
+    """The gradient calls allocate nothing and write every workspace word before
+    reading it, so one captured graph replays correctly with new upstream
+    gradients. Each replay must equal an eager call bit for bit."""
+    p = _mla("graph", 333, 44, 3, 90)
+    d = Dev(p)
+    out, lse, bl = hs.block_score(d.prob, d.q, d.kv, d.sink)
+    idx = hs.topk_blocks(d.prob, bl, p.top_k)
+    og, lg = hs.sparse_gather(d.prob, d.q, d.kv, d.sink, idx, p.top_k)
+    dout = inputs.make_dout(p, seed=45).cuda()
+    dq = torch.empty((1, p.Sq, p.H, p.Dk), dtype=torch.float32, device="cuda")
+    dkv = torch.empty((1, p.Skv, p.Dk), dtype=torch.float32, device="cuda")
+    dsink = torch.empty((p.H,), dtype=torch.float32, device="cuda")
+    ws = hs._workspace(d.prob, hs.HS_OP_SPARSE_GATHER_BWD, top_k=p.top_k)
+    ws2 = hs._workspace(d.prob, hs.HS_OP_BLOCK_SCORE_BWD)
+
+    def calls():
+        hs.hs_sparse_gather_bwd(d.prob, d.q, d.kv, d.sink, idx, p.top_k, og, lg, dout, dq, dkv,
+                                dsink, ws)
+        hs.hs_block_score_bwd(d.prob, d.q, d.kv, d.sink, out, lse, dout, dq, dkv, dsink, ws2)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        dout.copy_(inputs.make_dout(p, seed=46 + rep).cuda())
+        ws.fill_(float("nan"))
+        ws2.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (dq.clone(), dkv.clone(), dsink.clone())
+        want = hs.block_score_bwd(d.prob, d.q, d.kv, d.sink, out, lse, dout)
+        torch.cuda.synchronize()
+        for g_, w_, n in zip(got, want, ("dq", "dkv", "dsink")):
+            assert torch.equal(g_, w_), f"replay {rep}: {n} differs from the eager call"
+    say("[gpu] gradient graph replays: identical")
+
+
+def test_sink_without_its_gradient():
+    """A sink whose gradient is not asked for (dsink NULL) still shapes dq and
+    dkv."""
+    p = _mla("no_dsink", 150, 47, 2, 40)
+    d = Dev(p)
+    out, lse, _ = hs.block_score(d.prob, d.q, d.kv, d.sink)
+    dout_cpu = inputs.make_dout(p, seed=48)
+    dout = dout_cpu.cuda()
+    dq = torch.empty((1, p.Sq, p.H, p.Dk), dtype=torch.float32, device="cuda")
+    dkv = torch.empty((1, p.Skv, p.Dk), dtype=torch.float32, device="cuda")
+    hs.hs_block_score_bwd(d.prob, d.q, d.kv, d.sink, out, lse, dout, dq, dkv, None,
+                          hs._workspace(d.prob, hs.HS_OP_BLOCK_SCORE_BWD))
+    torch.cuda.synchronize()
+    w = _oracle_grads(d, "score", dout_cpu)
+    _grad_close(np64(dq), w[0], "bf16", "dq")
+    _grad_close(np64(dkv), w[1], "bf16", "dkv")
+    say("[gpu] sink without its gradient: ok")
