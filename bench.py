@@ -7,7 +7,8 @@ top-k block selection (hs_topk_blocks) and block-sparse gather attention
 (hs_sparse_gather_fwd), at S = 32768, 64 query heads, one latent KV head of
 576 columns (value = leading 512), 64-key blocks, top-k 32, learnable sink.
 The sliding-window call (hs_swa_fwd) is timed separately and reported next
-to the metric, not in it.
+to the metric, not in it, and so are the gradient calls of the three
+attention operations (the "gradients" object, timed after the metric).
 
 Prints ONE JSON line. `value` is tokens/s of the metric path with inputs
 resident in HBM; TFLOP/s counts algorithmic (query-head, key) pairs times
@@ -460,6 +461,8 @@ def main():
     ap.add_argument("--workload", type=int, default=3, help="named workload (1-5); 3 is the metric's")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gradients", action="store_true",
+                    help="skip timing the gradient calls after the metric's timed region")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run one 1 GiB device copy (counter calibration)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -557,6 +560,38 @@ def main():
     torch.cuda.synchronize()
     swa_ms = e0.elapsed_time(e1) / max(1, args.steps // 2)
 
+    # Gradient calls of the three attention operations, each fed its own
+    # forward outputs, timed after (and outside) the metric's timed region.
+    grads = None
+    if not args.no_gradients:
+        dout = inputs.make_dout(p, seed=900 + args.workload).to(dev)
+        dq = torch.empty((p.B, p.Sq, p.H, p.Dk), dtype=torch.float32, device=dev)
+        dkv = torch.empty((p.B, p.Skv, p.Dk), dtype=torch.float32, device=dev)
+        dsink = torch.empty((p.H,), dtype=torch.float32, device=dev)
+        wb1 = ws_for(hs.HS_OP_BLOCK_SCORE_BWD)
+        wb3 = ws_for(hs.HS_OP_SPARSE_GATHER_BWD, top_k=p.top_k)
+        wb4 = ws_for(hs.HS_OP_SWA_BWD, window=p.window)
+        gcalls = {
+            "block_score_bwd": lambda: hs.hs_block_score_bwd(
+                prob, q, kv, sink, out, lse, dout, dq, dkv, dsink, wb1, stream),
+            "sparse_gather_bwd": lambda: hs.hs_sparse_gather_bwd(
+                prob, q, kv, sink, idx, p.top_k, og, lg, dout, dq, dkv, dsink, wb3, stream),
+            "swa_bwd": lambda: hs.hs_swa_bwd(
+                prob, q, kv, sink, p.window, osw, lsw, dout, dq, dkv, dsink, wb4, stream)}
+        grads = {"ms": {}}
+        for k, fn in gcalls.items():
+            fn()
+            torch.cuda.synchronize()
+            g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            g0.record(stream)
+            for _ in range(3):
+                fn()
+            g1.record(stream)
+            torch.cuda.synchronize()
+            grads["ms"][k] = round(g0.elapsed_time(g1) / 3, 4)
+        del dout, dq, dkv, wb1, wb3, wb4
+        torch.cuda.empty_cache()
+
     if args.calib_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -606,6 +641,15 @@ def main():
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
     }
+    if grads is not None:
+        # 2 (3 Dk + 2 Dv) flops per pair: score recomputed, dP, dQ, dK, dV.
+        fpb = 2 * (3 * p.Dk + 2 * p.Dv)
+        f_bwd = causal_pairs(p) * fpb
+        t = grads["ms"]["block_score_bwd"]
+        grads["flop_per_pair"] = fpb
+        grads["block_score_bwd_tflop_s"] = round(f_bwd / (t * 1e-3) / 1e12, 2)
+        grads["block_score_bwd_frac"] = round(f_bwd / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        res["gradients"] = grads
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(p, args.cpu_budget)
     print(json.dumps(res), flush=True)
