@@ -1055,6 +1055,8 @@ BwdLayout bwd_layout(const Geom& g, int op, int top_k, int window, bool) {
     // gives about 1024 work items (four per compute unit). At R = 512 the Q
     // and dout rows of one chunk (71 MB) stay in the 256 MB last-level cache
     // while the chunk's items run (1024 and 256 measured within 2 % of it).
+    // Longer sequences double R until at most 32768 items remain, which
+    // bounds the partials at 32768 x 64 x Dk fp32 (4.8 GB for Dk = 576).
     auto items_for = [&](int R) -> long {
       const int C = (g.Sq + R - 1) / R;
       long it = 0;
@@ -1069,6 +1071,7 @@ BwdLayout bwd_layout(const Geom& g, int op, int top_k, int window, bool) {
     };
     int R = 512;
     while (R > 64 && items_for(R) < 1024) R >>= 1;
+    while (R < g.Sq && items_for(R) > 32768) R <<= 1;
     L.chunk_rows = R;
     L.n_chunks = (g.Sq + R - 1) / R;
     L.items = (int)items_for(R);

@@ -234,3 +234,15 @@ def test_device_lengths_validation():
     n = ctypes.c_size_t(0)
     assert lib.hs_workspace_size(ctypes.byref(ok), hs.HS_OP_BLOCK_SCORE, 0, 0, ctypes.byref(n)) == 0
     assert n.value > 0                                          # decode split planned at capacity
+
+
+def test_gradient_workspace_bounded_for_long_sequences():
+    """Work items are capped (longer sequences take longer row chunks), so the
+    gradient workspace stays a few GB even at 4096 key blocks."""
+    sizes = []
+    for S in (32768, 65536, 262144):
+        p = _mla(Sq=S, Skv=S)
+        for op, kw in ((hs.HS_OP_BLOCK_SCORE_BWD, {}), (hs.HS_OP_SPARSE_GATHER_BWD, {"top_k": 64}),
+                       (hs.HS_OP_SWA_BWD, {"window": 4096})):
+            sizes.append(hs.hs_workspace_size(p, op, **kw))
+    assert max(sizes) < 6e9, sizes
