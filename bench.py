@@ -251,10 +251,15 @@ def oracle_time(p, budget_s, seed=0, threads=None):
     order = rng.permutation(p.Sq)
     kv64 = p.kv.to(torch.float64).numpy()
     done, spent, pairs = 0, 0.0, 0
+    last_note = 0.0
     with limit:
         for r in order:
             if spent >= budget_s:
                 break
+            if spent - last_note >= 30.0:
+                last_note = spent
+                print(f"[oracle] {p.name}: {done}/{p.Sq} rows, {spent:.0f} s", file=sys.stderr,
+                      flush=True)
             t0 = time.perf_counter()
             rows = [int(r)]
             _, _, bl = ref.block_score(p.q, kv64, p.sink, p.Dv, p.scale, rows=rows, **kw)
@@ -390,7 +395,8 @@ def run_suite(args):
     print(json.dumps({"suite": "peaks", **peaks}), flush=True)
     results = []
     for c in args.suite_workloads:
-        r = suite_config(c, dev, stream, peaks, args.oracle_budget)
+        budget = float("inf") if c in (args.oracle_full_for or []) else args.oracle_budget
+        r = suite_config(c, dev, stream, peaks, budget)
         results.append(r)
         print(json.dumps({"suite": "workload", **r}), flush=True)
         torch.cuda.empty_cache()
@@ -403,6 +409,8 @@ def write_suite_md(path, peaks, results, args):
          "Command (from the repository root, on one MI355X):\n",
          "```\npython3 bench.py --suite --suite-md " + os.path.relpath(path, ROOT) +
          (" --oracle-full" if args.oracle_full else f" --oracle-budget {args.oracle_budget:g}") +
+         (" --oracle-full-for " + " ".join(str(c) for c in args.oracle_full_for)
+          if args.oracle_full_for and not args.oracle_full else "") +
          "\n```\n",
          f"Attainable peaks measured by the probe kernels (`include/hs_probe.h`): dense bf16 MFMA "
          f"{peaks['mfma_bf16_tflop_s']:.0f} TFLOP/s ({peaks['mfma_probe']}; shader clock while it ran: "
@@ -477,6 +485,8 @@ def main():
     ap.add_argument("--oracle-full", action="store_true",
                     help="suite: run the oracle over every row of every workload (no sampling; "
                          "the S=32768 workload takes about an hour on 16 cores)")
+    ap.add_argument("--oracle-full-for", type=int, nargs="+", default=None,
+                    help="suite: run the oracle over every row of these workloads only")
     args = ap.parse_args()
     if args.oracle_full:
         args.oracle_budget = float("inf")
