@@ -1,0 +1,123 @@
+"""PyTorch autograd functions over the C ABI.
+
+Each function runs its forward and its gradient in the library's kernels
+(hs_block_score_topk_fwd / hs_block_score_bwd, hs_sparse_gather_fwd /
+hs_sparse_gather_bwd, hs_swa_fwd / hs_swa_bwd). This mirrors the autograd
+layers of the page "HySparse MQA sparse attention (FA4 block scoring + SWA
+MQA + block-sparse DSA gather)", section "Core": block scoring trained
+through its autograd layer, and the learnable sink's analytic gradient. As in
+the review of PaddleFleet PR 1453 (block-score PyLayer comments), gradients
+flow to q, the latent kv and the sink only. lse, the block scores and the
+block selection are outputs without gradient.
+
+The library computes gradients in fp32. Autograd needs each gradient in its
+input's dtype, so bf16 inputs receive the fp32 gradients rounded to bf16.
+Nothing else runs outside the kernels.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import (HS_OP_BLOCK_SCORE_BWD, HS_OP_SPARSE_GATHER_BWD, HS_OP_SWA_BWD, Problem, _workspace,
+               block_score_topk, hs_block_score_bwd, hs_sparse_gather_bwd, hs_swa_bwd,
+               sparse_gather, swa)
+
+
+def _grads(prob, q, sink, need_sink):
+    dq = torch.empty((prob.B, prob.Sq, prob.H, prob.Dk), dtype=torch.float32, device=q.device)
+    dkv = torch.empty((prob.B, prob.Skv, prob.Dk), dtype=torch.float32, device=q.device)
+    dsink = (torch.empty((prob.H,), dtype=torch.float32, device=q.device)
+             if (sink is not None and need_sink) else None)
+    return dq, dkv, dsink
+
+
+def _finish(ctx, q, kv, sink, dq, dkv, dsink):
+    gq = dq.to(q.dtype) if ctx.needs_input_grad[0] else None
+    gkv = dkv.to(kv.dtype) if ctx.needs_input_grad[1] else None
+    gs = dsink if (sink is not None and ctx.needs_input_grad[2]) else None
+    return gq, gkv, gs
+
+
+class BlockScoreTopk(torch.autograd.Function):
+    """(out, lse, block_logit, block_idx) of causal attention with block
+    scores and the per-token top-k; gradients reach q, kv and the sink."""
+
+    @staticmethod
+    def forward(ctx, q, kv, sink, prob: Problem, top_k: int):
+        out, lse, bl, idx = block_score_topk(prob, q, kv, sink, top_k)
+        ctx.save_for_backward(q, kv, sink, out, lse)
+        ctx.prob = prob
+        ctx.mark_non_differentiable(lse, bl, idx)
+        return out, lse, bl, idx
+
+    @staticmethod
+    def backward(ctx, dout, _dlse, _dbl, _didx):
+        q, kv, sink, out, lse = ctx.saved_tensors
+        prob = ctx.prob
+        dq, dkv, dsink = _grads(prob, q, sink, ctx.needs_input_grad[2])
+        hs_block_score_bwd(prob, q, kv, sink, out, lse, dout.contiguous(), dq, dkv, dsink,
+                           _workspace(prob, HS_OP_BLOCK_SCORE_BWD))
+        return (*_finish(ctx, q, kv, sink, dq, dkv, dsink), None, None)
+
+
+class SparseGather(torch.autograd.Function):
+    """(out, lse) of the block-sparse gather for a given selection; the
+    selection itself takes no gradient."""
+
+    @staticmethod
+    def forward(ctx, q, kv, sink, block_idx, prob: Problem, top_k: int):
+        out, lse = sparse_gather(prob, q, kv, sink, block_idx, top_k)
+        ctx.save_for_backward(q, kv, sink, block_idx, out, lse)
+        ctx.prob, ctx.top_k = prob, top_k
+        ctx.mark_non_differentiable(lse)
+        return out, lse
+
+    @staticmethod
+    def backward(ctx, dout, _dlse):
+        q, kv, sink, block_idx, out, lse = ctx.saved_tensors
+        prob = ctx.prob
+        dq, dkv, dsink = _grads(prob, q, sink, ctx.needs_input_grad[2])
+        hs_sparse_gather_bwd(prob, q, kv, sink, block_idx, ctx.top_k, out, lse,
+                             dout.contiguous(), dq, dkv, dsink,
+                             _workspace(prob, HS_OP_SPARSE_GATHER_BWD, top_k=ctx.top_k))
+        return (*_finish(ctx, q, kv, sink, dq, dkv, dsink), None, None, None)
+
+
+class SlidingWindow(torch.autograd.Function):
+    """(out, lse) of sliding-window MQA attention."""
+
+    @staticmethod
+    def forward(ctx, q, kv, sink, prob: Problem, window: int):
+        out, lse = swa(prob, q, kv, sink, window)
+        ctx.save_for_backward(q, kv, sink, out, lse)
+        ctx.prob, ctx.window = prob, window
+        ctx.mark_non_differentiable(lse)
+        return out, lse
+
+    @staticmethod
+    def backward(ctx, dout, _dlse):
+        q, kv, sink, out, lse = ctx.saved_tensors
+        prob = ctx.prob
+        dq, dkv, dsink = _grads(prob, q, sink, ctx.needs_input_grad[2])
+        hs_swa_bwd(prob, q, kv, sink, ctx.window, out, lse, dout.contiguous(), dq, dkv, dsink,
+                   _workspace(prob, HS_OP_SWA_BWD, window=ctx.window))
+        return (*_finish(ctx, q, kv, sink, dq, dkv, dsink), None, None)
+
+
+def block_score_attention(q, kv, sink: Optional[torch.Tensor], prob: Problem, top_k: int):
+    """Causal attention with sink, its block scores and the top-k selection:
+    returns (out, lse, block_logit, block_idx); differentiable in q, kv, sink."""
+    return BlockScoreTopk.apply(q, kv, sink, prob, top_k)
+
+
+def sparse_gather_attention(q, kv, sink: Optional[torch.Tensor], block_idx, prob: Problem,
+                            top_k: int):
+    """Block-sparse gather attention: returns (out, lse)."""
+    return SparseGather.apply(q, kv, sink, block_idx, prob, top_k)
+
+
+def sliding_window_attention(q, kv, sink: Optional[torch.Tensor], prob: Problem, window: int):
+    """Sliding-window MQA attention: returns (out, lse)."""
+    return SlidingWindow.apply(q, kv, sink, prob, window)

@@ -1,0 +1,82 @@
+"""GPU checks of the autograd functions (block_sparse_mqa_amd.autograd): a
+backward pass through them must deliver exactly the library's gradients
+(rounded to the inputs' dtype), the block scores, lse and selection must not
+require gradients, and gradients of two calls sharing q and kv must add."""
+import pytest
+import torch
+
+import block_sparse_mqa_amd as hs
+from block_sparse_mqa_amd import autograd as hsa
+from block_sparse_mqa_amd import inputs
+
+from gpu_common import say
+from test_gpu_parity import MLA
+
+pytestmark = pytest.mark.gpu
+
+
+def _leaves(p):
+    q = p.q.cuda().requires_grad_(True)
+    kv = p.kv.cuda().requires_grad_(True)
+    sink = p.sink.cuda().requires_grad_(True)
+    return q, kv, sink
+
+
+def test_autograd_matches_library_gradients():
+    p = inputs.make(1, 200, 200, MLA["H"], MLA["Dk"], MLA["Dv"], seed=81, top_k=3, window=70,
+                    name="autograd")
+    prob = hs.Problem(1, 200, 200, p.H, p.Dk, p.Dv, scale=p.scale)
+    dout = inputs.make_dout(p, seed=82).cuda()
+    q, kv, sink = _leaves(p)
+
+    out, lse, bl, idx = hsa.block_score_attention(q, kv, sink, prob, p.top_k)
+    assert out.requires_grad and not lse.requires_grad and not bl.requires_grad
+    assert not idx.requires_grad and idx.dtype == torch.int32
+    (gq, gkv, gs) = torch.autograd.grad(out, (q, kv, sink), dout)
+    with torch.no_grad():
+        dq, dkv, dsink = hs.block_score_bwd(prob, q, kv, sink, out, lse, dout)
+    torch.cuda.synchronize()
+    assert gq.dtype == q.dtype and gkv.dtype == kv.dtype and gs.dtype == torch.float32
+    assert torch.equal(gq, dq.to(q.dtype)) and torch.equal(gkv, dkv.to(kv.dtype))
+    assert torch.equal(gs, dsink)
+
+    og, lg = hsa.sparse_gather_attention(q, kv, sink, idx, prob, p.top_k)
+    (gq, gkv, gs) = torch.autograd.grad(og, (q, kv, sink), dout)
+    with torch.no_grad():
+        dq, dkv, dsink = hs.sparse_gather_bwd(prob, q, kv, sink, idx, p.top_k, og, lg, dout)
+    assert torch.equal(gq, dq.to(q.dtype)) and torch.equal(gkv, dkv.to(kv.dtype))
+    assert torch.equal(gs, dsink)
+
+    ow, lw = hsa.sliding_window_attention(q, kv, sink, prob, p.window)
+    (gq, gkv, gs) = torch.autograd.grad(ow, (q, kv, sink), dout)
+    with torch.no_grad():
+        dq, dkv, dsink = hs.swa_bwd(prob, q, kv, sink, p.window, ow, lw, dout)
+    assert torch.equal(gq, dq.to(q.dtype)) and torch.equal(gkv, dkv.to(kv.dtype))
+    assert torch.equal(gs, dsink)
+    say("[gpu] autograd functions deliver the library's gradients")
+
+
+def test_autograd_gradients_accumulate_over_branches():
+    """A window branch and a gather branch reading the same q and kv (as the
+    two branches of a layer would): backward through their sum gives the sum
+    of the two calls' gradients, and a sink without requires_grad gets none."""
+    p = inputs.make(1, 150, 150, MLA["H"], MLA["Dk"], MLA["Dv"], seed=83, top_k=2, window=40,
+                    name="autograd_sum")
+    prob = hs.Problem(1, 150, 150, p.H, p.Dk, p.Dv, scale=p.scale)
+    dout = inputs.make_dout(p, seed=84).cuda()
+    q = p.q.cuda().requires_grad_(True)
+    kv = p.kv.cuda().requires_grad_(True)
+    sink = p.sink.cuda()                                   # no gradient asked
+    _, _, _, idx = hsa.block_score_attention(q, kv, sink, prob, p.top_k)
+    og, lg = hsa.sparse_gather_attention(q, kv, sink, idx, prob, p.top_k)
+    ow, lw = hsa.sliding_window_attention(q, kv, sink, prob, p.window)
+    ((og.float() + ow.float()) * dout.float()).sum().backward()
+    with torch.no_grad():
+        a = hs.sparse_gather_bwd(prob, q, kv, sink, idx, p.top_k, og, lg, dout)
+        b = hs.swa_bwd(prob, q, kv, sink, p.window, ow, lw, dout)
+    torch.cuda.synchronize()
+    want_q = a[0].to(q.dtype).float() + b[0].to(q.dtype).float()
+    want_kv = a[1].to(kv.dtype).float() + b[1].to(kv.dtype).float()
+    assert torch.allclose(q.grad.float(), want_q, rtol=1e-2, atol=1e-3)
+    assert torch.allclose(kv.grad.float(), want_kv, rtol=1e-2, atol=1e-3)
+    say("[gpu] autograd gradients accumulate over branches")
