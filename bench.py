@@ -114,14 +114,18 @@ def cpu_baseline(p, budget_s: float, seed: int = 0):
 def counter_traffic(path: str, workload: str, kernel: str):
     """HBM bytes per launch measured by rocprofv3 FETCH_SIZE / WRITE_SIZE runs
     (each scaled by the reading of a 1 GiB copy), or None when no record
-    exists or the kernel source changed since the counters were taken."""
+    exists or the kernel's sources (the files listed in the record, hashed in
+    order) changed since the counters were taken."""
     import hashlib
     try:
         with open(path) as f:
             rec = json.load(f)[workload][kernel]
-        with open(os.path.join(ROOT, rec["source"]), "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest()[:16] != rec["source_sha256_16"]:
-                return None
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest()[:16] != rec["sources_sha256_16"]:
+            return None
         return int(rec["bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None

@@ -60,17 +60,11 @@
 #include <utility>
 
 #include "hs_common.h"
+#include "hs_gfx950.h"
 #include "hs_kernels.h"
 #include "hs_topk_row.h"
 
 namespace hs {
-
-typedef __bf16 bf16;
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-#define HS_LDS __attribute__((address_space(3)))
 
 namespace mla {
 constexpr int H = 64, DK = 576, DV = 512, BS = 64;
@@ -121,9 +115,6 @@ __device__ __forceinline__ float max_row16(float v) {
   return v;
 }
 
-// Chunk swizzle of key k inside a tile row (depends on bits 1 and 2 only).
-__device__ __forceinline__ int swz(int k) { return 3 * ((k >> 2) & 1) + 4 * ((k >> 1) & 1); }
-
 // Wait until at most N LDS operations are outstanding (vmcnt and expcnt left
 // at their maxima).
 template <int N>
@@ -141,16 +132,6 @@ __host__ __device__ constexpr int stream_pending(int i, int la, int nsf, int nf,
   if (iw >= 0 && i > iw && i <= iw + la) n += 1;
   return n;
 }
-// One LDS DMA instruction: lane l copies 16 B from src (per lane) to LDS
-// byte lds + 16 l, the LDS base taken from M0 (the compiler sets it from the
-// operand; one wait state separates that write from the DMA). Issued as
-// inline assembly so that the compiler's wait analysis does not take it for
-// an out-of-order LDS operation and drain every LDS read in flight; it is
-// counted by vmcnt only, and callers wait for it with s_waitcnt vmcnt.
-__device__ __forceinline__ void dma16(const char* src, char* lds) {
-  const unsigned m = (unsigned)(uintptr_t)(HS_LDS char*)lds;
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m) : "memory");
-}
 // Score MFMA with the Q operand read straight from AGPRs (the builtin in the
 // VGPR-accumulator form copies it to VGPRs first: 72 extra instructions per
 // tile). Dependent MFMAs on one accumulator are interlocked by the hardware,
@@ -166,40 +147,6 @@ __device__ __forceinline__ f32x4 mfma_q(bf16x8 k, bf16x8 q, f32x4 c) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(k), "a"(q));
   return c;
 }
-template <typename Fn, int... Is>
-__device__ __forceinline__ void static_for_impl(Fn&& fn, std::integer_sequence<int, Is...>) {
-  (fn(std::integral_constant<int, Is>{}), ...);
-}
-// fn(std::integral_constant<int, i>) for i = 0 .. N-1, with i a constant.
-template <int N, typename Fn>
-__device__ __forceinline__ void static_for(Fn&& fn) {
-  static_for_impl(fn, std::make_integer_sequence<int, N>{});
-}
-
-// Copy one 64-key tile (KV rows base + start .. + len - 1, clamped) into an
-// LDS buffer.
-// Instruction n = (G, kq) = (n / 8, n % 8) fills keys 8kq .. 8kq+7 of column
-// group G; lane l takes key 8kq + l/8 and stores slot l%8, i.e. chunk
-// (l%8) ^ sw(key). Wave w issues n = w + 4i, so kq alternates between w and
-// w + 4 (same key bit 3) and G = i / 2: two source rows per lane, immediate
-// offsets otherwise.
-__device__ __forceinline__ void stage_tile(char* buf, const bf16* base, int start, int len,
-                                           int wave_u, int lane) {
-  using namespace mla;
-  const int kl = lane >> 3;                                    // key inside the octet
-  const int c8 = (lane & 7) ^ swz(8 * wave_u + kl);
-  const int ka = min(8 * wave_u + kl, len - 1);               // kq = w
-  const int kb = min(8 * (wave_u + 4) + kl, len - 1);         // kq = w + 4
-  const char* src_a = (const char*)(base + (size_t)(start + ka) * DK) + 16 * c8;
-  const char* src_b = (const char*)(base + (size_t)(start + kb) * DK) + 16 * c8;
-  char* dst = buf + wave_u * 1024;
-#pragma unroll
-  for (int G = 0; G < NGR; ++G) {
-    dma16(src_a + 128 * G, dst + G * GR_BYTES);
-    dma16(src_b + 128 * G, dst + G * GR_BYTES + 4096);
-  }
-}
-
 template <int OP, bool SPLIT, bool PAGED>
 __global__ __launch_bounds__(mla::NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_bf16_kernel(AttnArgs a) {

@@ -41,8 +41,7 @@
 //     staged in LDS, double-buffered;
 //     S[head, key]  = Q . K^T,   dP[head, key] = dout . V^T  (B = K registers)
 //     dKV^T[dim, key] += Q^T . dS + [dout^T . P, 0]         (A by transpose reads)
-// LDS tiles use the swizzled 64-column-group layout of the forward engine:
-// row k's 16-byte chunk c sits in slot c ^ sw(k), sw(k) = 3 bit2(k) + 4 bit1(k).
+// LDS tiles use the swizzled 64-column-group layout of hs_gfx950.h.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -50,18 +49,12 @@
 #include <utility>
 
 #include "hs_common.h"
+#include "hs_gfx950.h"
 #include "hs_kernels.h"
 
 namespace hs {
 
 namespace {
-
-typedef __bf16 bf16;
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-#define HS_LDS __attribute__((address_space(3)))
 
 namespace bw {
 constexpr int H = 64, DK = 576, DV = 512, BS = 64, NT = 256;
@@ -78,20 +71,8 @@ constexpr int STAGE = QH + 8 * HGR; // + 32 dout rows = 69632
 
 constexpr int kMaxHeads = 64;
 
-__device__ __forceinline__ int swz(int k) { return 3 * ((k >> 2) & 1) + 4 * ((k >> 1) & 1); }
-
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-template <typename Fn, int... Is>
-__device__ __forceinline__ void static_for_impl(Fn&& fn, std::integer_sequence<int, Is...>) {
-  (fn(std::integral_constant<int, Is>{}), ...);
-}
-// fn(std::integral_constant<int, i>) for i = 0 .. N-1, with i a constant.
-template <int N, typename Fn>
-__device__ __forceinline__ void static_for(Fn&& fn) {
-  static_for_impl(fn, std::make_integer_sequence<int, N>{});
 }
 
 // Operand stream: NF LDS fragments consumed in order, each requested LA
@@ -115,14 +96,6 @@ __device__ __forceinline__ void operand_stream(Load&& load, Use&& use, Pre&& pre
     if constexpr (i + LA < NF) fr[(i + LA) % RB] = load(std::integral_constant<int, i + LA>{});
     __builtin_amdgcn_sched_barrier(0);
   });
-}
-
-// One LDS DMA instruction: lane l copies 16 B from src to LDS byte lds + 16 l
-// (base in M0; one wait state separates the M0 write from the DMA). Counted
-// by vmcnt only; callers wait with s_waitcnt vmcnt(0) and a barrier.
-__device__ __forceinline__ void dma16(const char* src, char* lds) {
-  const unsigned m = (unsigned)(uintptr_t)(HS_LDS char*)lds;
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m) : "memory");
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -405,26 +378,6 @@ __global__ __launch_bounds__(256) void bwd_gfill_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernels.
 // ---------------------------------------------------------------------------
-// Copy a 64-row KV tile (rows start .. start+len-1, clamped) into LDS: DMA
-// instruction (G, kq) fills rows 8kq .. 8kq+7 of column group G; wave w
-// issues kq = w and w + 4.
-__device__ __forceinline__ void stage_kv_tile(char* buf, const bf16* base, int start, int len,
-                                              int wave, int lane) {
-  using namespace bw;
-  const int kl = lane >> 3;
-  const int c8 = (lane & 7) ^ swz(8 * wave + kl);
-  const int ka = min(8 * wave + kl, len - 1);
-  const int kb = min(8 * (wave + 4) + kl, len - 1);
-  const char* src_a = (const char*)(base + (size_t)(start + ka) * DK) + 16 * c8;
-  const char* src_b = (const char*)(base + (size_t)(start + kb) * DK) + 16 * c8;
-  char* dst = buf + wave * 1024;
-#pragma unroll
-  for (int G = 0; G < 9; ++G) {
-    dma16(src_a + 128 * G, dst + G * GR);
-    dma16(src_b + 128 * G, dst + G * GR + 4096);
-  }
-}
-
 // Copy 32 head rows of Q (576 wide) and of dout (512 wide) into a stage
 // buffer: wave w fills rows 8w .. 8w+7 of every column group.
 __device__ __forceinline__ void stage_half_rows(char* st, const bf16* qrows, const bf16* drows,
@@ -508,7 +461,7 @@ void bwd_dq_bf16_kernel(BwdArgs a) {
   const bf16* kv_entry = static_cast<const bf16*>(a.kv) + (size_t)b * g.Skv * DK;
   if (ntiles > 0) {
     const Blk b0 = block_rows(g, b, tile_block(0));
-    stage_kv_tile(buf[0], kv_entry, b0.start, b0.len, wave, lane);
+    stage_tile(buf[0], kv_entry, b0.start, b0.len, wave, lane);
   }
 
   bf16x8 qreg[KSTEPS], dreg[VSTEPS];
