@@ -323,7 +323,7 @@ def suite_config(c, dev, stream, peaks, oracle_budget):
     dq = torch.empty((p.B, p.Sq, p.H, p.Dk), dtype=torch.float32, device=dev)
     dkv = torch.empty((p.B, p.Skv, p.Dk), dtype=torch.float32, device=dev)
     dsink = torch.empty((p.H,), dtype=torch.float32, device=dev)
-    wb1, wb3, wb4 = ws(hs.HS_OP_BLOCK_SCORE_BWD), ws(hs.HS_OP_SPARSE_GATHER_BWD, top_k=p.top_k), \
+    wb1, wb3, wb4 = hs.score_bwd_workspace(prob), ws(hs.HS_OP_SPARSE_GATHER_BWD, top_k=p.top_k), \
         ws(hs.HS_OP_SWA_BWD, window=p.window)
     calls["block_score_bwd"] = lambda: hs.hs_block_score_bwd(
         prob, q, kv, sink, *fwd["block_score"], dout, dq, dkv, dsink, wb1, stream)
@@ -582,7 +582,8 @@ def main():
         dq = torch.empty((p.B, p.Sq, p.H, p.Dk), dtype=torch.float32, device=dev)
         dkv = torch.empty((p.B, p.Skv, p.Dk), dtype=torch.float32, device=dev)
         dsink = torch.empty((p.H,), dtype=torch.float32, device=dev)
-        wb1 = ws_for(hs.HS_OP_BLOCK_SCORE_BWD)
+        wb1 = hs.score_bwd_workspace(prob)
+        stored = wb1.numel() * 4 >= hs.hs_workspace_size(prob, hs.HS_OP_BLOCK_SCORE_BWD_STORE_DS)
         wb3 = ws_for(hs.HS_OP_SPARSE_GATHER_BWD, top_k=p.top_k)
         wb4 = ws_for(hs.HS_OP_SWA_BWD, window=p.window)
         gcalls = {
@@ -592,7 +593,7 @@ def main():
                 prob, q, kv, sink, idx, p.top_k, og, lg, dout, dq, dkv, dsink, wb3, stream),
             "swa_bwd": lambda: hs.hs_swa_bwd(
                 prob, q, kv, sink, p.window, osw, lsw, dout, dq, dkv, dsink, wb4, stream)}
-        grads = {"ms": {}}
+        grads = {"ms": {}, "block_score_bwd_dq": "stored dS" if stored else "recomputed dS"}
         for k, fn in gcalls.items():
             fn()
             torch.cuda.synchronize()

@@ -29,6 +29,7 @@ HS_OK, HS_ERR_INVALID_ARG, HS_ERR_UNSUPPORTED, HS_ERR_HIP, HS_ERR_WORKSPACE = 0,
 HS_BF16, HS_F32 = 0, 1
 HS_OP_BLOCK_SCORE, HS_OP_SPARSE_GATHER, HS_OP_SWA = 0, 1, 2
 HS_OP_BLOCK_SCORE_BWD, HS_OP_SPARSE_GATHER_BWD, HS_OP_SWA_BWD = 3, 4, 5
+HS_OP_BLOCK_SCORE_BWD_STORE_DS = 6
 
 EXPORTS = ("hs_num_blocks", "hs_workspace_size", "hs_block_score_fwd", "hs_topk_blocks",
            "hs_block_score_topk_fwd", "hs_sparse_gather_fwd", "hs_swa_fwd",
@@ -335,12 +336,25 @@ def _grad_buffers(prob, q, sink):
     return dq, dkv, dsink
 
 
-def block_score_bwd(prob, q, kv, sink, out, lse, dout, stream=None):
+def score_bwd_workspace(prob, store_ds=None):
+    """Workspace of hs_block_score_bwd. store_ds True: the larger one, in
+    which the key-block pass stores the score gradients for dq; False: the
+    smaller one (dq recomputes them); None: the larger one when it fits in
+    half of the free device memory."""
+    import torch
+    if store_ds is None:
+        n = hs_workspace_size(prob, HS_OP_BLOCK_SCORE_BWD_STORE_DS)
+        store_ds = n <= torch.cuda.mem_get_info()[0] // 2
+    return _workspace(prob, HS_OP_BLOCK_SCORE_BWD_STORE_DS if store_ds else HS_OP_BLOCK_SCORE_BWD)
+
+
+def block_score_bwd(prob, q, kv, sink, out, lse, dout, stream=None, store_ds=None):
     """Gradients (dq, dkv, dsink) of the causal attention of block_score;
-    dsink is None without a sink. All float32."""
+    dsink is None without a sink. All float32. store_ds picks the workspace
+    (score_bwd_workspace)."""
     dq, dkv, dsink = _grad_buffers(prob, q, sink)
     hs_block_score_bwd(prob, q, kv, sink, out, lse, dout, dq, dkv, dsink,
-                       _workspace(prob, HS_OP_BLOCK_SCORE_BWD), stream)
+                       score_bwd_workspace(prob, store_ds), stream)
     return dq, dkv, dsink
 
 

@@ -20,8 +20,8 @@ from typing import Optional
 
 import torch
 
-from . import (HS_OP_BLOCK_SCORE_BWD, HS_OP_SPARSE_GATHER_BWD, HS_OP_SWA_BWD, Problem, _workspace,
-               block_score_topk, hs_block_score_bwd, hs_sparse_gather_bwd, hs_swa_bwd,
+from . import (HS_OP_SPARSE_GATHER_BWD, HS_OP_SWA_BWD, Problem, _workspace, block_score_topk,
+               hs_block_score_bwd, hs_sparse_gather_bwd, hs_swa_bwd, score_bwd_workspace,
                sparse_gather, swa)
 
 
@@ -58,7 +58,7 @@ class BlockScoreTopk(torch.autograd.Function):
         prob = ctx.prob
         dq, dkv, dsink = _grads(prob, q, sink, ctx.needs_input_grad[2])
         hs_block_score_bwd(prob, q, kv, sink, out, lse, dout.contiguous(), dq, dkv, dsink,
-                           _workspace(prob, HS_OP_BLOCK_SCORE_BWD))
+                           score_bwd_workspace(prob))
         return (*_finish(ctx, q, kv, sink, dq, dkv, dsink), None, None)
 
 

@@ -328,7 +328,13 @@ hs_status launch_bwd(int op, const hs_problem* p, const void* q, const void* kv,
     return fail(HS_ERR_INVALID_ARG, "window must be >= 1 (got %d)", window);
   const bool bf16 = p->dtype == HS_BF16;
   const int kop = op == HS_OP_SWA ? hs::kSwa : op == HS_OP_SPARSE_GATHER ? hs::kGather : hs::kScore;
-  const hs::BwdLayout L = hs::bwd_layout(g, kop, top_k, window, bf16);
+  // The stored-score path (causal, bf16) runs when the workspace also holds
+  // the score gradients; otherwise dq recomputes them.
+  hs::BwdLayout L = hs::bwd_layout(g, kop, top_k, window, false);
+  if (bf16 && kop == hs::kScore && ws) {
+    const hs::BwdLayout Ls = hs::bwd_layout(g, kop, top_k, window, true);
+    if (ws_bytes >= Ls.total) L = Ls;
+  }
   if (!ws || ws_bytes < L.total)
     return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", L.total,
                 ws ? ws_bytes : (size_t)0);
@@ -364,6 +370,11 @@ hs_status launch_bwd(int op, const hs_problem* p, const void* q, const void* kv,
       a.g_rows = reinterpret_cast<int*>(w + L.rows);
     }
     a.part = reinterpret_cast<float*>(w + L.part);
+    if (L.store_ds) {
+      a.ds_entry = reinterpret_cast<long long*>(w + L.ds_entry);
+      a.ds_dummy = reinterpret_cast<__bf16*>(w + L.ds_dummy);
+      a.ds_tiles = reinterpret_cast<__bf16*>(w + L.ds_tiles);
+    }
     a.chunk_rows = L.chunk_rows;
     a.n_chunks = L.n_chunks;
     a.items = L.items;
@@ -378,7 +389,7 @@ hs_status launch_bwd(int op, const hs_problem* p, const void* q, const void* kv,
 
 extern "C" {
 
-int32_t hs_version(void) { return 103; }
+int32_t hs_version(void) { return 104; }
 
 const char* hs_status_string(int32_t status) {
   switch (status) {
@@ -405,7 +416,8 @@ hs_status hs_workspace_size(const hs_problem* p, int32_t op, int32_t top_k, int3
   hs_status st = prepare(p, g);
   if (st != HS_OK) return st;
   if (!bytes) return fail(HS_ERR_INVALID_ARG, "bytes is NULL");
-  if (op < HS_OP_BLOCK_SCORE || op > HS_OP_SWA_BWD) return fail(HS_ERR_INVALID_ARG, "unknown op %d", op);
+  if (op < HS_OP_BLOCK_SCORE || op > HS_OP_BLOCK_SCORE_BWD_STORE_DS)
+    return fail(HS_ERR_INVALID_ARG, "unknown op %d", op);
   if (op >= HS_OP_BLOCK_SCORE_BWD) {
     const int kop = op == HS_OP_SWA_BWD ? hs::kSwa : op == HS_OP_SPARSE_GATHER_BWD ? hs::kGather
                                                                                   : hs::kScore;
@@ -413,7 +425,8 @@ hs_status hs_workspace_size(const hs_problem* p, int32_t op, int32_t top_k, int3
       return fail(HS_ERR_INVALID_ARG, "top_k must be in 1..64 (got %d)", top_k);
     if (kop == hs::kSwa && window < 1)
       return fail(HS_ERR_INVALID_ARG, "window must be >= 1 (got %d)", window);
-    *bytes = hs::bwd_layout(g, kop, top_k, window, p->dtype == HS_BF16).total;
+    const bool store = op == HS_OP_BLOCK_SCORE_BWD_STORE_DS && p->dtype == HS_BF16;
+    *bytes = hs::bwd_layout(g, kop, top_k, window, store).total;
     return HS_OK;
   }
   *bytes = p->dtype == HS_BF16 ? split_ws_bytes(g, plan_split(g, op, top_k, window).nsplit) : 0;

@@ -156,6 +156,29 @@ __host__ __device__ inline int block_row_range(const Geom& g, int op, int b, int
   return p_hi - p_lo + 1;
 }
 
+// Sum over x = 0 .. n-1 of (x / bs + 1): the causal key blocks of the rows
+// at positions 0 .. n-1 of a document that starts at position 0.
+__host__ __device__ inline long long causal_tiles_upto(long long n, int bs) {
+  if (n <= 0) return 0;
+  const long long m = n / bs;
+  return n + (long long)bs * m * (m - 1) / 2 + (n - (long long)bs * m) * m;
+}
+
+// Causal key blocks of rows 0 .. r-1 of entry b: a row at position p of a
+// document starting at s walks (p - s) / bs + 1 blocks. Documents tile
+// [0, Sq) with rows at their positions; without documents the rows of entry
+// b sit at kv_len - Sq + r.
+__host__ __device__ inline long long causal_tiles_before(const Geom& g, int b, int r) {
+  if (g.n_docs == 0) {
+    const long long p0 = g.kv_len[b] - g.Sq;
+    return causal_tiles_upto(p0 + r, g.BS) - causal_tiles_upto(p0, g.BS);
+  }
+  long long t = 0;
+  for (int d = 0; d < g.n_docs && g.doc_start[d] < r; ++d)
+    t += causal_tiles_upto((g.doc_end[d] < r ? g.doc_end[d] : r) - g.doc_start[d], g.BS);
+  return t;
+}
+
 // ---------------------------------------------------------------------------
 // Dsum and the sink-gradient partials.
 // ---------------------------------------------------------------------------
@@ -375,6 +398,23 @@ __global__ __launch_bounds__(256) void bwd_gfill_kernel(BwdArgs a) {
   }
 }
 
+// First stored tile of each entry (exclusive prefix of the entries' causal
+// block counts) and the total.
+__global__ __launch_bounds__(256) void bwd_ds_entry_kernel(BwdArgs a) {
+  __shared__ long long tot[kMaxBatch];
+  const Geom& g = a.g;
+  if ((int)threadIdx.x < g.B) tot[threadIdx.x] = causal_tiles_before(g, threadIdx.x, g.Sq);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    long long run = 0;
+    for (int b = 0; b < g.B; ++b) {
+      a.ds_entry[b] = run;
+      run += tot[b];
+    }
+    a.ds_entry[g.B] = run;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernels.
 // ---------------------------------------------------------------------------
@@ -416,6 +456,115 @@ __device__ __forceinline__ bf16x8 frag_t(const char* base, int gs, int kk, int d
   v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
   v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
   return v;
+}
+
+// dq from the stored score gradients (causal): one workgroup per pair of
+// consecutive query rows (heaviest first), 8 waves, two per SIMD: wave w
+// owns heads 16 (w & 3) .. +15 of row r_hi - (w >> 2). Per tile only
+// dQ^T += K^T . dS^T remains, with dS^T read from the stored tile in operand
+// order (16 B per lane and k-step, the next tile's prefetched during the
+// current one). Both rows walk the union of their causal block ranges; a row
+// takes zero dS on a block outside its own range. Each copied K tile serves
+// both rows.
+__global__ __launch_bounds__(2 * bw::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_ds_bf16_kernel(BwdArgs a) {
+  using namespace bw;
+  __shared__ __attribute__((aligned(16))) char buf[2][TILE];
+
+  const Geom& g = a.g;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 0 .. 7
+  const int grp = lane >> 4, l16 = lane & 15;
+  const int hw = wave & 3, rsel = wave >> 2;
+  const int head = 16 * hw + l16;
+  const int npair = (g.Sq + 1) / 2;
+  const int b = blockIdx.x / npair;
+  const int r_hi = g.Sq - 1 - 2 * (blockIdx.x % npair);
+  const int r_lo = r_hi - 1;                       // -1: no second row
+  const RowRange ra = row_range(g, kScore, b, r_hi, 0);
+  const RowRange rb = r_lo >= 0 ? row_range(g, kScore, b, r_lo, 0) : ra;
+  const int jf = min(ra.j_first, rb.j_first), jl = max(ra.j_last, rb.j_last);
+  const int ntiles = jl - jf + 1;
+  // this wave's row
+  const int r = rsel ? r_lo : r_hi;
+  const bool has_row = r >= 0;
+  const RowRange rr = rsel ? rb : ra;
+  const size_t row = (size_t)b * g.Sq + (has_row ? r : 0);
+
+  const bf16* kv_entry = static_cast<const bf16*>(a.kv) + (size_t)b * g.Skv * DK;
+  // copy: wave w fills keys 8w .. 8w+7 of every column group
+  const int cp_c8 = (lane & 7) ^ swz(8 * wave + (lane >> 3));
+  auto copy_tile = [&](char* dst, const Blk& bk, auto&& issue) __attribute__((always_inline)) {
+    const int k = min(8 * wave + (lane >> 3), bk.len - 1);
+    const char* src = (const char*)(kv_entry + (size_t)(bk.start + k) * DK) + 16 * cp_c8;
+    issue(src, dst + wave * 1024);
+  };
+  copy_tile(buf[0], block_rows(g, b, jf), [&](const char* src, char* dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int G = 0; G < 9; ++G) dma16(src + 128 * G, dst + G * GR);
+  });
+  const long long base = has_row ? a.ds_entry[b] + causal_tiles_before(g, b, r) : 0;
+  const bf16* dsp = a.ds_tiles + (base * 4 + hw) * 2 * 512 + lane * 8;  // row tile t: + 4096 t
+  const bf16x8 zero8 = {};
+  auto ds_load = [&](int j, bf16x8* d) __attribute__((always_inline)) {
+    if (has_row && j >= rr.j_first && j <= rr.j_last) {
+      const bf16* q = dsp + (size_t)(j - rr.j_first) * 4096;
+      d[0] = *(const bf16x8*)q;
+      d[1] = *(const bf16x8*)(q + 512);
+    } else {
+      d[0] = zero8;
+      d[1] = zero8;
+    }
+  };
+  bf16x8 dnext[2], dcur[2];
+  ds_load(jf, dnext);
+
+  f32x4 acc[DBK];
+#pragma unroll
+  for (int db = 0; db < DBK; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int t = 0; t < ntiles; ++t) {
+    char* cur = buf[t & 1];
+    const int j = jf + t;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // tile t and its dS resident; tile t-1 consumed by every wave
+    dcur[0] = dnext[0];
+    dcur[1] = dnext[1];
+    ds_load(min(j + 1, jl), dnext);
+    // The copy of the next tile (on the last tile the current one again, into
+    // the idle buffer) is spread over the stream.
+    const Blk nbk = block_rows(g, b, min(j + 1, jl));
+    const int ck = min(8 * wave + (lane >> 3), nbk.len - 1);
+    const char* cp_src = (const char*)(kv_entry + (size_t)(nbk.start + ck) * DK) + 16 * cp_c8;
+    char* cp_dst = buf[(t + 1) & 1] + wave * 1024;
+
+    // 72 K^T fragments, k-step kk major, column block db.
+    constexpr int NF = 2 * DBK;
+    auto load = [&](auto F) __attribute__((always_inline)) -> bf16x8 {
+      constexpr int f = decltype(F)::value;
+      return frag_t(cur, GR, f / DBK, f % DBK, l16, grp);
+    };
+    auto use = [&](auto I, bf16x8 fr) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      acc[i % DBK] = mfma(fr, dcur[i / DBK], acc[i % DBK]);
+    };
+    auto pre = [&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      if constexpr ((i & 7) == 7) {
+        constexpr int G = i >> 3;
+        dma16(cp_src + 128 * G, cp_dst + G * GR);
+      }
+    };
+    operand_stream<NF, 8>(load, use, pre);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // acc[db][i] = dq[head][16 db + 4 grp + i]
+  if (has_row) {
+    float* out = a.dq + (row * H + head) * DK + 4 * grp;
+#pragma unroll
+    for (int db = 0; db < DBK; ++db) *(f32x4*)(out + 16 * db) = acc[db];
+  }
 }
 
 template <int OP>
@@ -554,11 +703,18 @@ void bwd_dq_bf16_kernel(BwdArgs a) {
   for (int db = 0; db < DBK; ++db) *(f32x4*)(out + 16 * db) = acc[db];
 }
 
-template <int OP>
+// STORE (causal only): also write each stage's dS to the stored tiles. The
+// lanes hold dS for one key and eight heads; the dq kernel wants one head and
+// eight keys, so a stage's 64 x 32 dS tile goes through LDS ([key][head], 64 B
+// rows) and is read back one stage later, after that stage's barrier, with
+// transpose reads: wave w then writes head block 2 (s & 1) + (w >> 1), k-step
+// w & 1 of the row's tile, 16 B per lane.
+template <int OP, bool STORE>
 __global__ __launch_bounds__(bw::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkv_bf16_kernel(BwdArgs a) {
   using namespace bw;
   __shared__ __attribute__((aligned(16))) char stg[2][STAGE];
+  __shared__ __attribute__((aligned(16))) char dsl[STORE ? 2 : 1][STORE ? 64 * 64 : 16];
 
   const Geom& g = a.g;
   const int C = a.n_chunks;
@@ -611,12 +767,30 @@ void bwd_dkv_bf16_kernel(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < DBK; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // STORE: first stored tile of the current row (rows of a causal item are
+  // consecutive), the previous stage's target and its transposed dS.
+  long long rbase = 0;
+  int prev_nt = 0;
+  bf16* st_prev = nullptr;
+  const int tr_off = (32 * (wave & 1) + 4 * grp + (l16 >> 2)) * 64 + 32 * (wave >> 1) + 8 * (l16 & 3);
+  if (STORE) {
+    rbase = a.ds_entry[b] + causal_tiles_before(g, b, row_at(0));
+    st_prev = a.ds_dummy + wave * 512 + lane * 8;
+  }
+
   for (int s = 0; s < 2 * n; ++s) {
     const char* cur = stg[s & 1];
     const int r = row_at(s >> 1);
     const size_t rw = (size_t)b * g.Sq + r;
     const int h0 = 32 * (s & 1);
     const RowRange rr = row_range(g, OP, b, r, a.window);
+    bf16* st_cur = nullptr;
+    if (STORE) {
+      if (s > 0 && (s & 1) == 0) rbase += prev_nt;
+      prev_nt = rr.j_last - rr.j_first + 1;
+      const long long slot = rbase + (j - rr.j_first);
+      st_cur = a.ds_tiles + ((slot * 4 + 2 * (s & 1) + (wave >> 1)) * 2 + (wave & 1)) * 512 + lane * 8;
+    }
     const bool valid = kloc < blk.len && key >= rr.lo && key <= rr.hi;
     // heads h0 + 16 hb + 4 grp + i of this lane
     float lse2[2][4], ds[2][4];
@@ -631,6 +805,14 @@ void bwd_dkv_bf16_kernel(BwdArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // stage s resident; stage s-1 consumed by every wave
+    bf16x4 tlo, thi;
+    if (STORE) {
+      // the previous stage's dS, transposed (stage 0: unused contents, written
+      // to the dummy target)
+      const HS_LDS char* tp = (const HS_LDS char*)(dsl[(s + 1) & 1] + tr_off);
+      tlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((HS_LDS bf16x4*)tp);
+      thi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((HS_LDS bf16x4*)(tp + 16 * 64));
+    }
     // The copy of the next stage is spread over the 68 MFMAs of phase 1: Q
     // groups at positions 3, 7, .., 35, dout groups at 39, .., 67. The last
     // stage copies itself again into the idle buffer (nothing reads it).
@@ -677,6 +859,12 @@ void bwd_dkv_bf16_kernel(BwdArgs a) {
         if constexpr (G < 9) dma16(cq + 128 * G, cp_dst + G * HGR);
         else dma16(cd + 128 * (G - 9), cp_dst + QH + (G - 9) * HGR);
       }
+      if constexpr (STORE && i == 6) {
+        bf16x8 v;
+        v[0] = tlo[0]; v[1] = tlo[1]; v[2] = tlo[2]; v[3] = tlo[3];
+        v[4] = thi[0]; v[5] = thi[1]; v[6] = thi[2]; v[7] = thi[3];
+        *(bf16x8*)st_prev = v;
+      }
       if constexpr (i == NP1) {
         // sc[hb][e], dp[hb][e]: head h0 + 16 hb + 4 grp + e, key kloc.
 #pragma unroll
@@ -688,11 +876,32 @@ void bwd_dkv_bf16_kernel(BwdArgs a) {
             dsb[4 * hb + e] = (bf16)(p * (dp[hb][e] - ds[hb][e]) * scale);
           }
         }
+        if (STORE) {
+          // this stage's dS as [key][head of the stage], heads 16 hb + 4 grp ..
+          char* wp = dsl[s & 1] + kloc * 64 + 8 * grp;
+          bf16x4 lo4, hi4;
+          lo4[0] = dsb[0]; lo4[1] = dsb[1]; lo4[2] = dsb[2]; lo4[3] = dsb[3];
+          hi4[0] = dsb[4]; hi4[1] = dsb[5]; hi4[2] = dsb[6]; hi4[3] = dsb[7];
+          *(HS_LDS bf16x4*)(HS_LDS char*)wp = lo4;
+          *(HS_LDS bf16x4*)(HS_LDS char*)(wp + 32) = hi4;
+        }
       }
     };
     operand_stream<NF, 8>(load, use, pre);
+    if (STORE) st_prev = st_cur;
   }
   __builtin_amdgcn_s_waitcnt(0);
+  if (STORE) {
+    // the last stage's dS
+    __syncthreads();
+    const HS_LDS char* tp = (const HS_LDS char*)(dsl[(2 * n + 1) & 1] + tr_off);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((HS_LDS bf16x4*)tp);
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((HS_LDS bf16x4*)(tp + 16 * 64));
+    bf16x8 v;
+    v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+    v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+    *(bf16x8*)st_prev = v;
+  }
 
   // acc[db][i] = dkv[key kloc][16 db + 4 grp + i]
   float* out = a.part + ((size_t)item * BS + kloc) * DK + 4 * grp;
@@ -966,9 +1175,18 @@ void launch_bf16(const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(bwd_plan_kernel, dim3(1), dim3(256), 0, s, a, OP);
   if (OP == kGather)
     hipLaunchKernelGGL(bwd_gfill_kernel, dim3(g.B * a.row_tiles), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(bwd_dq_bf16_kernel<OP>, dim3(g.B * g.Sq), dim3(bw::NT), 0, s, a);
-  if (a.items > 0)
-    hipLaunchKernelGGL(bwd_dkv_bf16_kernel<OP>, dim3(a.items), dim3(bw::NT), 0, s, a);
+  if (OP == kScore && a.ds_tiles != nullptr) {
+    // stored score gradients: the key-block pass writes dS, dq reads it
+    hipLaunchKernelGGL(bwd_ds_entry_kernel, dim3(1), dim3(256), 0, s, a);
+    if (a.items > 0)
+      hipLaunchKernelGGL((bwd_dkv_bf16_kernel<kScore, true>), dim3(a.items), dim3(bw::NT), 0, s, a);
+    hipLaunchKernelGGL(bwd_dq_ds_bf16_kernel, dim3(g.B * ((g.Sq + 1) / 2)), dim3(2 * bw::NT), 0, s,
+                       a);
+  } else {
+    hipLaunchKernelGGL(bwd_dq_bf16_kernel<OP>, dim3(g.B * g.Sq), dim3(bw::NT), 0, s, a);
+    if (a.items > 0)
+      hipLaunchKernelGGL((bwd_dkv_bf16_kernel<OP, false>), dim3(a.items), dim3(bw::NT), 0, s, a);
+  }
   hipLaunchKernelGGL(bwd_reduce_bf16_kernel, dim3(g.B * ((g.Skv + 63) / 64)), dim3(256), 0, s, a);
 }
 
@@ -991,7 +1209,7 @@ void launch_f32(const BwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
-BwdLayout bwd_layout(const Geom& g, int op, int top_k, int window, bool) {
+BwdLayout bwd_layout(const Geom& g, int op, int top_k, int window, bool store_ds) {
   BwdLayout L;
   std::memset(&L, 0, sizeof(L));
   const size_t rows = (size_t)g.B * g.Sq;
@@ -1048,6 +1266,18 @@ BwdLayout bwd_layout(const Geom& g, int op, int top_k, int window, bool) {
     }
     L.part = off;
     off = align256(off + (size_t)L.items * 64 * g.Dk * sizeof(float));
+  }
+  if (store_ds && op == kScore) {
+    // 64 heads x 64 keys of bf16 per (row, causal block)
+    long long tiles = 0;
+    for (int b = 0; b < g.B; ++b) tiles += causal_tiles_before(g, b, g.Sq);
+    L.store_ds = true;
+    L.ds_entry = off;
+    off = align256(off + (size_t)(g.B + 1) * sizeof(long long));
+    L.ds_dummy = off;
+    off = align256(off + 4096);
+    L.ds_tiles = off;
+    off = align256(off + (size_t)tiles * 64 * 64 * sizeof(bf16));
   }
   L.total = off;
   return L;

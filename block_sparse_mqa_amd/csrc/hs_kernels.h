@@ -80,6 +80,14 @@ struct BwdArgs {
   int* g_off;                // gather: [B * NB] start of each block's row list
   int* g_rows;               // gather: row lists of all blocks, rows ascending
   float* part;               // [items, 64, Dk] per-item key-block gradient partials
+  // Stored score gradients (causal bf16 only; nullptr: dq recomputes them).
+  // Row (b, r) owns tiles ds_entry[b] + tiles_before(b, r) .. + its causal
+  // block count; tile t of a row holds dS (scale included, bf16) of its 64
+  // heads x 64 keys in the dq kernel's operand order [head block 4][k-step
+  // 2][lane 64][8].
+  __bf16* ds_tiles;
+  long long* ds_entry;       // [B + 1] first tile of each entry; [B] = total
+  __bf16* ds_dummy;          // 4 KB target of the no-op store of a stage with no predecessor
   int chunk_rows;            // R: rows per chunk (multiple of 64)
   int n_chunks;              // C = ceil(Sq / R)
   int items;                 // work items launched (exact or an upper bound)
@@ -90,11 +98,14 @@ struct BwdArgs {
 // Workspace layout of one gradient call: byte offsets of each piece and the
 // total, plus the work split of the key-block gradient.
 struct BwdLayout {
-  size_t dsum, sink_part, first, nrows, pre, cnt, total_g, off_g, rows, part, total;
+  size_t dsum, sink_part, first, nrows, pre, cnt, total_g, off_g, rows, part, ds_entry, ds_dummy,
+      ds_tiles, total;
   int n_pre, rows_per_pre, chunk_rows, n_chunks, items, row_tiles;
+  bool store_ds;
 };
 
-BwdLayout bwd_layout(const Geom& g, int op, int top_k, int window, bool bf16);
+// store_ds: also lay out the stored score gradients (causal bf16 only).
+BwdLayout bwd_layout(const Geom& g, int op, int top_k, int window, bool store_ds);
 int bwd_launch(int op, const BwdArgs& a, bool bf16, hipStream_t stream);
 
 int attn_bf16_launch(int op, const AttnArgs& a, hipStream_t stream);

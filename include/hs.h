@@ -96,7 +96,9 @@ typedef enum {
   HS_OP_SWA = 2,
   HS_OP_BLOCK_SCORE_BWD = 3,    /* workspace of hs_block_score_bwd   */
   HS_OP_SPARSE_GATHER_BWD = 4,  /* workspace of hs_sparse_gather_bwd */
-  HS_OP_SWA_BWD = 5             /* workspace of hs_swa_bwd           */
+  HS_OP_SWA_BWD = 5,            /* workspace of hs_swa_bwd           */
+  HS_OP_BLOCK_SCORE_BWD_STORE_DS = 6 /* larger workspace of hs_block_score_bwd
+                                        that also holds the score gradients */
 } hs_op;
 
 typedef struct {
@@ -209,7 +211,13 @@ hs_status hs_swa_fwd(const hs_problem* p, const void* q, const void* kv, const f
  * hs_workspace_size with HS_OP_*_BWD and the same top_k / window, 16-byte
  * aligned. Results are deterministic (fixed summation order). Paged KV and
  * device-resident lengths are rejected (HS_ERR_UNSUPPORTED).
- * hs_block_score_bwd: the causal attention of hs_block_score_fwd. */
+ * hs_block_score_bwd: the causal attention of hs_block_score_fwd. Given at
+ * least the HS_OP_BLOCK_SCORE_BWD_STORE_DS workspace (bf16 only; 8 KB per
+ * causal (row, key block) pair, 69 GB at one 32768-token sequence), the
+ * key-block pass stores the bf16 score gradients dS (softmax scale included)
+ * and dq is computed from them instead of recomputing the scores; with the
+ * smaller HS_OP_BLOCK_SCORE_BWD workspace dq recomputes them. Both give the
+ * same gradients up to the rounding of dS. */
 hs_status hs_block_score_bwd(const hs_problem* p, const void* q, const void* kv, const float* sink,
                              const void* out, const float* lse, const void* dout, float* dq,
                              float* dkv, float* dsink, void* ws, size_t ws_bytes, void* stream);

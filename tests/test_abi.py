@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(hs.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.hs_version() == 103
+    assert lib.hs_version() == 104
 
 
 def _mla(**kw):
@@ -246,3 +246,58 @@ def test_gradient_workspace_bounded_for_long_sequences():
                        (hs.HS_OP_SWA_BWD, {"window": 4096})):
             sizes.append(hs.hs_workspace_size(p, op, **kw))
     assert max(sizes) < 6e9, sizes
+
+
+def _causal_pairs(B, Sq, Skv, kv_lens=None, doc_lens=None):
+    """(row, key block) pairs of causal attention, counted row by row: a row
+    at position p of a document starting at s reaches blocks s/64 .. p/64 of
+    that document."""
+    starts = []
+    if doc_lens:
+        at = 0
+        for n in doc_lens:
+            starts.append(at)
+            at += n
+    pairs = 0
+    for b in range(B):
+        L = kv_lens[b] if kv_lens else Skv
+        for r in range(Sq):
+            pos = L - Sq + r
+            s = max([x for x in starts if x <= pos], default=0)
+            pairs += (pos - s) // 64 + 1
+    return pairs
+
+
+@pytest.mark.parametrize("B,Sq,Skv,kv_lens,doc_lens", [
+    (1, 130, 130, None, None),
+    (1, 1, 1, None, None),
+    (2, 70, 200, [200, 150], None),
+    (3, 64, 4000, [64, 4000, 1000], None),
+    (1, 300, 300, None, [70, 1, 63, 100, 66]),
+    (1, 32768, 32768, None, None),
+])
+def test_stored_score_gradient_workspace(B, Sq, Skv, kv_lens, doc_lens):
+    """The larger causal-gradient workspace adds exactly 8 KB per causal
+    (row, key block) pair (bf16 dS of 64 heads x 64 keys), plus the per-entry
+    tile offsets and a 4 KB dummy target, each 256-byte aligned: a check of
+    the closed-form tile count against a row-by-row count."""
+    kw = {}
+    if kv_lens:
+        kw["kv_lens"] = kv_lens
+    if doc_lens:
+        ends = [sum(doc_lens[:i + 1]) for i in range(len(doc_lens))]
+        kw["doc_start"] = [e - n for e, n in zip(ends, doc_lens)]
+        kw["doc_end"] = ends
+    p = hs.Problem(B, Sq, Skv, 64, 576, 512, **kw)
+    n3 = hs.hs_workspace_size(p, hs.HS_OP_BLOCK_SCORE_BWD)
+    n6 = hs.hs_workspace_size(p, hs.HS_OP_BLOCK_SCORE_BWD_STORE_DS)
+    a256 = lambda x: (x + 255) // 256 * 256
+    pairs = _causal_pairs(B, Sq, Skv, kv_lens, doc_lens)
+    assert n6 - n3 == a256((B + 1) * 8) + a256(4096) + a256(pairs * 8192), (n3, n6, pairs)
+
+
+def test_stored_score_gradient_workspace_f32_unchanged():
+    """The fp32 shapes always recompute: both queries give the same size."""
+    p = hs.Problem(1, 100, 100, 8, 96, 64, dtype="f32")
+    assert hs.hs_workspace_size(p, hs.HS_OP_BLOCK_SCORE_BWD_STORE_DS) == \
+        hs.hs_workspace_size(p, hs.HS_OP_BLOCK_SCORE_BWD)

@@ -44,9 +44,12 @@ def _grad_close(got, want, dtype, name):
 
 def _gpu_grads(d, op, dout, idx=None, K=None):
     p = d.p
-    if op == "score":
+    if op in ("score", "score_recompute"):
+        # "score": the larger workspace (dq from the stored score gradients on
+        # bf16 shapes); "score_recompute": the smaller one (dq recomputes them)
         out, lse, _ = hs.block_score(d.prob, d.q, d.kv, d.sink)
-        return hs.block_score_bwd(d.prob, d.q, d.kv, d.sink, out, lse, dout)
+        return hs.block_score_bwd(d.prob, d.q, d.kv, d.sink, out, lse, dout,
+                                  store_ds=op == "score")
     if op == "swa":
         out, lse = hs.swa(d.prob, d.q, d.kv, d.sink, p.window)
         return hs.swa_bwd(d.prob, d.q, d.kv, d.sink, p.window, out, lse, dout)
@@ -57,7 +60,7 @@ def _gpu_grads(d, op, dout, idx=None, K=None):
 def _oracle_grads(d, op, dout_cpu, idx=None, rows=None):
     p = d.p
     kw = dict(d.kw(), rows=rows)
-    if op == "score":
+    if op in ("score", "score_recompute"):
         return ref.block_score_bwd(p.q, p.kv, d.sink_cpu, p.Dv, p.scale, dout_cpu, **kw)
     if op == "swa":
         return ref.swa_bwd(p.q, p.kv, d.sink_cpu, p.Dv, p.scale, p.window, dout_cpu, **kw)
@@ -100,7 +103,7 @@ def test_gradients_match_oracle(name):
     torch.cuda.synchronize()
     idx_cpu = idx.cpu().numpy()
     res = {}
-    for op in ("score", "swa", "gather"):
+    for op in ("score", "score_recompute", "swa", "gather"):
         g = _gpu_grads(d, op, dout, idx, p.top_k)
         torch.cuda.synchronize()
         w = _oracle_grads(d, op, dout_cpu, idx_cpu)
@@ -145,7 +148,7 @@ def test_gradients_are_deterministic():
     dout = inputs.make_dout(p, seed=42).cuda()
     _, _, bl = hs.block_score(d.prob, d.q, d.kv, d.sink)
     idx = hs.topk_blocks(d.prob, bl, p.top_k)
-    for op in ("score", "swa", "gather"):
+    for op in ("score", "score_recompute", "swa", "gather"):
         a = _gpu_grads(d, op, dout, idx, p.top_k)
         b = _gpu_grads(d, op, dout, idx, p.top_k)
         torch.cuda.synchronize()
@@ -199,7 +202,7 @@ def test_gradients_in_captured_graph():
     dkv = torch.empty((1, p.Skv, p.Dk), dtype=torch.float32, device="cuda")
     dsink = torch.empty((p.H,), dtype=torch.float32, device="cuda")
     ws = hs._workspace(d.prob, hs.HS_OP_SPARSE_GATHER_BWD, top_k=p.top_k)
-    ws2 = hs._workspace(d.prob, hs.HS_OP_BLOCK_SCORE_BWD)
+    ws2 = hs.score_bwd_workspace(d.prob, store_ds=True)
 
     def calls():
         hs.hs_sparse_gather_bwd(d.prob, d.q, d.kv, d.sink, idx, p.top_k, og, lg, dout, dq, dkv,
@@ -224,7 +227,7 @@ def test_gradients_in_captured_graph():
         graph.replay()
         torch.cuda.synchronize()
         got = (dq.clone(), dkv.clone(), dsink.clone())
-        want = hs.block_score_bwd(d.prob, d.q, d.kv, d.sink, out, lse, dout)
+        want = hs.block_score_bwd(d.prob, d.q, d.kv, d.sink, out, lse, dout, store_ds=True)
         torch.cuda.synchronize()
         for g_, w_, n in zip(got, want, ("dq", "dkv", "dsink")):
             assert torch.equal(g_, w_), f"replay {rep}: {n} differs from the eager call"
@@ -248,3 +251,21 @@ def test_sink_without_its_gradient():
     _grad_close(np64(dq), w[0], "bf16", "dq")
     _grad_close(np64(dkv), w[1], "bf16", "dkv")
     say("[gpu] sink without its gradient: ok")
+
+
+def test_stored_and_recomputed_score_gradients_agree():
+    """The two workspaces of the causal gradient: the key-block pass is the
+    same arithmetic in both (dkv and dsink bit-identical); dq from the stored
+    bf16 score gradients matches dq that recomputes them up to dS rounding."""
+    p = _mla("paths_S700", 700, 44, 2, 64)
+    say(f"[gpu] stored vs recomputed score gradients, S={p.Sq}")
+    d = Dev(p)
+    dout = inputs.make_dout(p, seed=45).cuda()
+    out, lse, _ = hs.block_score(d.prob, d.q, d.kv, d.sink)
+    a = hs.block_score_bwd(d.prob, d.q, d.kv, d.sink, out, lse, dout, store_ds=True)
+    b = hs.block_score_bwd(d.prob, d.q, d.kv, d.sink, out, lse, dout, store_ds=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+    err = ((a[0] - b[0]).abs().max() / b[0].abs().max()).item()
+    say(f"[gpu] dq stored vs recomputed: max |diff| / max |dq| = {err:.2e}")
+    assert err < 1e-2
