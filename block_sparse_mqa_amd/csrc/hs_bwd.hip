@@ -706,9 +706,11 @@ void bwd_dq_bf16_kernel(BwdArgs a) {
 // STORE (causal only): also write each stage's dS to the stored tiles. The
 // lanes hold dS for one key and eight heads; the dq kernel wants one head and
 // eight keys, so a stage's 64 x 32 dS tile goes through LDS ([key][head], 64 B
-// rows) and is read back one stage later, after that stage's barrier, with
-// transpose reads: wave w then writes head block 2 (s & 1) + (w >> 1), k-step
-// w & 1 of the row's tile, 16 B per lane.
+// rows, written a few MFMAs into phase 2) and read back during phase 1 of
+// the next stage, after its barrier, with transpose reads: wave w then writes
+// head block 2 (s & 1) + (w >> 1), k-step w & 1 of the row's tile, 16 B per
+// lane. (Issued right after the barrier instead, the transpose reads delay
+// the stream's first fragments: 3.5 ms more at S = 32768.)
 template <int OP, bool STORE>
 __global__ __launch_bounds__(bw::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkv_bf16_kernel(BwdArgs a) {
@@ -806,13 +808,7 @@ void bwd_dkv_bf16_kernel(BwdArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // stage s resident; stage s-1 consumed by every wave
     bf16x4 tlo, thi;
-    if (STORE) {
-      // the previous stage's dS, transposed (stage 0: unused contents, written
-      // to the dummy target)
-      const HS_LDS char* tp = (const HS_LDS char*)(dsl[(s + 1) & 1] + tr_off);
-      tlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((HS_LDS bf16x4*)tp);
-      thi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((HS_LDS bf16x4*)(tp + 16 * 64));
-    }
+    const HS_LDS char* tp = (const HS_LDS char*)(dsl[(s + 1) & 1] + tr_off);
     // The copy of the next stage is spread over the 68 MFMAs of phase 1: Q
     // groups at positions 3, 7, .., 35, dout groups at 39, .., 67. The last
     // stage copies itself again into the idle buffer (nothing reads it).
@@ -854,12 +850,29 @@ void bwd_dkv_bf16_kernel(BwdArgs a) {
     };
     auto pre = [&](auto I) __attribute__((always_inline)) {
       constexpr int i = decltype(I)::value;
+      if constexpr (i == NP1 + 4) {
+        if constexpr (STORE) {
+          // this stage's dS as [key][head of the stage], heads 16 hb + 4 grp ..
+          char* wp = dsl[s & 1] + kloc * 64 + 8 * grp;
+          bf16x4 lo4, hi4;
+          lo4[0] = dsb[0]; lo4[1] = dsb[1]; lo4[2] = dsb[2]; lo4[3] = dsb[3];
+          hi4[0] = dsb[4]; hi4[1] = dsb[5]; hi4[2] = dsb[6]; hi4[3] = dsb[7];
+          *(HS_LDS bf16x4*)(HS_LDS char*)wp = lo4;
+          *(HS_LDS bf16x4*)(HS_LDS char*)(wp + 32) = hi4;
+        }
+      }
       if constexpr (i < NP1 && (i & 3) == 3) {
         constexpr int G = i >> 2;
         if constexpr (G < 9) dma16(cq + 128 * G, cp_dst + G * HGR);
         else dma16(cd + 128 * (G - 9), cp_dst + QH + (G - 9) * HGR);
       }
-      if constexpr (STORE && i == 6) {
+      if constexpr (STORE && i == 30) {
+        // the previous stage's dS, transposed (stage 0: unused contents,
+        // written to the dummy target)
+        tlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((HS_LDS bf16x4*)tp);
+        thi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((HS_LDS bf16x4*)(tp + 16 * 64));
+      }
+      if constexpr (STORE && i == 44) {
         bf16x8 v;
         v[0] = tlo[0]; v[1] = tlo[1]; v[2] = tlo[2]; v[3] = tlo[3];
         v[4] = thi[0]; v[5] = thi[1]; v[6] = thi[2]; v[7] = thi[3];
@@ -875,15 +888,6 @@ void bwd_dkv_bf16_kernel(BwdArgs a) {
             pb[4 * hb + e] = (bf16)p;
             dsb[4 * hb + e] = (bf16)(p * (dp[hb][e] - ds[hb][e]) * scale);
           }
-        }
-        if (STORE) {
-          // this stage's dS as [key][head of the stage], heads 16 hb + 4 grp ..
-          char* wp = dsl[s & 1] + kloc * 64 + 8 * grp;
-          bf16x4 lo4, hi4;
-          lo4[0] = dsb[0]; lo4[1] = dsb[1]; lo4[2] = dsb[2]; lo4[3] = dsb[3];
-          hi4[0] = dsb[4]; hi4[1] = dsb[5]; hi4[2] = dsb[6]; hi4[3] = dsb[7];
-          *(HS_LDS bf16x4*)(HS_LDS char*)wp = lo4;
-          *(HS_LDS bf16x4*)(HS_LDS char*)(wp + 32) = hi4;
         }
       }
     };
