@@ -324,7 +324,7 @@ def suite_config(c, dev, stream, peaks, oracle_budget):
     dkv = torch.empty((p.B, p.Skv, p.Dk), dtype=torch.float32, device=dev)
     dsink = torch.empty((p.H,), dtype=torch.float32, device=dev)
     wb1, wb3, wb4 = hs.score_bwd_workspace(prob), ws(hs.HS_OP_SPARSE_GATHER_BWD, top_k=p.top_k), \
-        ws(hs.HS_OP_SWA_BWD, window=p.window)
+        hs.swa_bwd_workspace(prob, p.window)
     calls["block_score_bwd"] = lambda: hs.hs_block_score_bwd(
         prob, q, kv, sink, *fwd["block_score"], dout, dq, dkv, dsink, wb1, stream)
     calls["sparse_gather_bwd"] = lambda: hs.hs_sparse_gather_bwd(
@@ -585,7 +585,9 @@ def main():
         wb1 = hs.score_bwd_workspace(prob)
         stored = wb1.numel() * 4 >= hs.hs_workspace_size(prob, hs.HS_OP_BLOCK_SCORE_BWD_STORE_DS)
         wb3 = ws_for(hs.HS_OP_SPARSE_GATHER_BWD, top_k=p.top_k)
-        wb4 = ws_for(hs.HS_OP_SWA_BWD, window=p.window)
+        wb4 = hs.swa_bwd_workspace(prob, p.window)
+        stored4 = wb4.numel() * 4 >= hs.hs_workspace_size(prob, hs.HS_OP_SWA_BWD_STORE_DS,
+                                                          window=p.window)
         gcalls = {
             "block_score_bwd": lambda: hs.hs_block_score_bwd(
                 prob, q, kv, sink, out, lse, dout, dq, dkv, dsink, wb1, stream),
@@ -593,7 +595,8 @@ def main():
                 prob, q, kv, sink, idx, p.top_k, og, lg, dout, dq, dkv, dsink, wb3, stream),
             "swa_bwd": lambda: hs.hs_swa_bwd(
                 prob, q, kv, sink, p.window, osw, lsw, dout, dq, dkv, dsink, wb4, stream)}
-        grads = {"ms": {}, "block_score_bwd_dq": "stored dS" if stored else "recomputed dS"}
+        grads = {"ms": {}, "block_score_bwd_dq": "stored dS" if stored else "recomputed dS",
+                 "swa_bwd_dq": "stored dS" if stored4 else "recomputed dS"}
         for k, fn in gcalls.items():
             fn()
             torch.cuda.synchronize()

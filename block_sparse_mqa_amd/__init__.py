@@ -29,7 +29,7 @@ HS_OK, HS_ERR_INVALID_ARG, HS_ERR_UNSUPPORTED, HS_ERR_HIP, HS_ERR_WORKSPACE = 0,
 HS_BF16, HS_F32 = 0, 1
 HS_OP_BLOCK_SCORE, HS_OP_SPARSE_GATHER, HS_OP_SWA = 0, 1, 2
 HS_OP_BLOCK_SCORE_BWD, HS_OP_SPARSE_GATHER_BWD, HS_OP_SWA_BWD = 3, 4, 5
-HS_OP_BLOCK_SCORE_BWD_STORE_DS = 6
+HS_OP_BLOCK_SCORE_BWD_STORE_DS, HS_OP_SWA_BWD_STORE_DS = 6, 7
 
 EXPORTS = ("hs_num_blocks", "hs_workspace_size", "hs_block_score_fwd", "hs_topk_blocks",
            "hs_block_score_topk_fwd", "hs_sparse_gather_fwd", "hs_swa_fwd",
@@ -336,16 +336,26 @@ def _grad_buffers(prob, q, sink):
     return dq, dkv, dsink
 
 
+def _stored_ds_workspace(prob, small, large, store_ds, window=0):
+    import torch
+    if store_ds is None:
+        n = hs_workspace_size(prob, large, window=window)
+        store_ds = n <= torch.cuda.mem_get_info()[0] // 2
+    return _workspace(prob, large if store_ds else small, window=window)
+
+
 def score_bwd_workspace(prob, store_ds=None):
     """Workspace of hs_block_score_bwd. store_ds True: the larger one, in
     which the key-block pass stores the score gradients for dq; False: the
     smaller one (dq recomputes them); None: the larger one when it fits in
     half of the free device memory."""
-    import torch
-    if store_ds is None:
-        n = hs_workspace_size(prob, HS_OP_BLOCK_SCORE_BWD_STORE_DS)
-        store_ds = n <= torch.cuda.mem_get_info()[0] // 2
-    return _workspace(prob, HS_OP_BLOCK_SCORE_BWD_STORE_DS if store_ds else HS_OP_BLOCK_SCORE_BWD)
+    return _stored_ds_workspace(prob, HS_OP_BLOCK_SCORE_BWD, HS_OP_BLOCK_SCORE_BWD_STORE_DS,
+                                store_ds)
+
+
+def swa_bwd_workspace(prob, window, store_ds=None):
+    """Workspace of hs_swa_bwd, chosen as for score_bwd_workspace."""
+    return _stored_ds_workspace(prob, HS_OP_SWA_BWD, HS_OP_SWA_BWD_STORE_DS, store_ds, window)
 
 
 def block_score_bwd(prob, q, kv, sink, out, lse, dout, stream=None, store_ds=None):
@@ -366,9 +376,10 @@ def sparse_gather_bwd(prob, q, kv, sink, block_idx, top_k, out, lse, dout, strea
     return dq, dkv, dsink
 
 
-def swa_bwd(prob, q, kv, sink, window, out, lse, dout, stream=None):
-    """Gradients (dq, dkv, dsink) of swa."""
+def swa_bwd(prob, q, kv, sink, window, out, lse, dout, stream=None, store_ds=None):
+    """Gradients (dq, dkv, dsink) of swa. store_ds picks the workspace
+    (swa_bwd_workspace)."""
     dq, dkv, dsink = _grad_buffers(prob, q, sink)
     hs_swa_bwd(prob, q, kv, sink, window, out, lse, dout, dq, dkv, dsink,
-               _workspace(prob, HS_OP_SWA_BWD, window=window), stream)
+               swa_bwd_workspace(prob, window, store_ds), stream)
     return dq, dkv, dsink

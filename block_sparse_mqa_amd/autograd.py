@@ -20,9 +20,9 @@ from typing import Optional
 
 import torch
 
-from . import (HS_OP_SPARSE_GATHER_BWD, HS_OP_SWA_BWD, Problem, _workspace, block_score_topk,
+from . import (HS_OP_SPARSE_GATHER_BWD, Problem, _workspace, block_score_topk,
                hs_block_score_bwd, hs_sparse_gather_bwd, hs_swa_bwd, score_bwd_workspace,
-               sparse_gather, swa)
+               sparse_gather, swa, swa_bwd_workspace)
 
 
 def _grads(prob, q, sink, need_sink):
@@ -102,7 +102,7 @@ class SlidingWindow(torch.autograd.Function):
         prob = ctx.prob
         dq, dkv, dsink = _grads(prob, q, sink, ctx.needs_input_grad[2])
         hs_swa_bwd(prob, q, kv, sink, ctx.window, out, lse, dout.contiguous(), dq, dkv, dsink,
-                   _workspace(prob, HS_OP_SWA_BWD, window=ctx.window))
+                   swa_bwd_workspace(prob, ctx.window))
         return (*_finish(ctx, q, kv, sink, dq, dkv, dsink), None, None)
 
 

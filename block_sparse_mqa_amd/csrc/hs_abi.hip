@@ -328,10 +328,10 @@ hs_status launch_bwd(int op, const hs_problem* p, const void* q, const void* kv,
     return fail(HS_ERR_INVALID_ARG, "window must be >= 1 (got %d)", window);
   const bool bf16 = p->dtype == HS_BF16;
   const int kop = op == HS_OP_SWA ? hs::kSwa : op == HS_OP_SPARSE_GATHER ? hs::kGather : hs::kScore;
-  // The stored-score path (causal, bf16) runs when the workspace also holds
-  // the score gradients; otherwise dq recomputes them.
+  // The stored-score path (causal and window, bf16) runs when the workspace
+  // also holds the score gradients; otherwise dq recomputes them.
   hs::BwdLayout L = hs::bwd_layout(g, kop, top_k, window, false);
-  if (bf16 && kop == hs::kScore && ws) {
+  if (bf16 && kop != hs::kGather && ws) {
     const hs::BwdLayout Ls = hs::bwd_layout(g, kop, top_k, window, true);
     if (ws_bytes >= Ls.total) L = Ls;
   }
@@ -374,6 +374,7 @@ hs_status launch_bwd(int op, const hs_problem* p, const void* q, const void* kv,
       a.ds_entry = reinterpret_cast<long long*>(w + L.ds_entry);
       a.ds_dummy = reinterpret_cast<__bf16*>(w + L.ds_dummy);
       a.ds_tiles = reinterpret_cast<__bf16*>(w + L.ds_tiles);
+      a.ds_stride = L.ds_stride;
     }
     a.chunk_rows = L.chunk_rows;
     a.n_chunks = L.n_chunks;
@@ -389,7 +390,7 @@ hs_status launch_bwd(int op, const hs_problem* p, const void* q, const void* kv,
 
 extern "C" {
 
-int32_t hs_version(void) { return 104; }
+int32_t hs_version(void) { return 105; }
 
 const char* hs_status_string(int32_t status) {
   switch (status) {
@@ -416,16 +417,18 @@ hs_status hs_workspace_size(const hs_problem* p, int32_t op, int32_t top_k, int3
   hs_status st = prepare(p, g);
   if (st != HS_OK) return st;
   if (!bytes) return fail(HS_ERR_INVALID_ARG, "bytes is NULL");
-  if (op < HS_OP_BLOCK_SCORE || op > HS_OP_BLOCK_SCORE_BWD_STORE_DS)
+  if (op < HS_OP_BLOCK_SCORE || op > HS_OP_SWA_BWD_STORE_DS)
     return fail(HS_ERR_INVALID_ARG, "unknown op %d", op);
   if (op >= HS_OP_BLOCK_SCORE_BWD) {
-    const int kop = op == HS_OP_SWA_BWD ? hs::kSwa : op == HS_OP_SPARSE_GATHER_BWD ? hs::kGather
-                                                                                  : hs::kScore;
+    const int kop = (op == HS_OP_SWA_BWD || op == HS_OP_SWA_BWD_STORE_DS) ? hs::kSwa
+                    : op == HS_OP_SPARSE_GATHER_BWD                       ? hs::kGather
+                                                                          : hs::kScore;
     if (kop == hs::kGather && (top_k < 1 || top_k > 64))
       return fail(HS_ERR_INVALID_ARG, "top_k must be in 1..64 (got %d)", top_k);
     if (kop == hs::kSwa && window < 1)
       return fail(HS_ERR_INVALID_ARG, "window must be >= 1 (got %d)", window);
-    const bool store = op == HS_OP_BLOCK_SCORE_BWD_STORE_DS && p->dtype == HS_BF16;
+    const bool store = (op == HS_OP_BLOCK_SCORE_BWD_STORE_DS || op == HS_OP_SWA_BWD_STORE_DS) &&
+                       p->dtype == HS_BF16;
     *bytes = hs::bwd_layout(g, kop, top_k, window, store).total;
     return HS_OK;
   }

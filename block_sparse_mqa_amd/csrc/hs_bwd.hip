@@ -398,6 +398,12 @@ __global__ __launch_bounds__(256) void bwd_gfill_kernel(BwdArgs a) {
   }
 }
 
+// First stored tile of row (b, r).
+__device__ inline long long ds_row_base(const BwdArgs& a, int b, int r) {
+  if (a.ds_stride > 0) return ((long long)b * a.g.Sq + r) * a.ds_stride;
+  return a.ds_entry[b] + causal_tiles_before(a.g, b, r);
+}
+
 // First stored tile of each entry (exclusive prefix of the entries' causal
 // block counts) and the total.
 __global__ __launch_bounds__(256) void bwd_ds_entry_kernel(BwdArgs a) {
@@ -458,14 +464,15 @@ __device__ __forceinline__ bf16x8 frag_t(const char* base, int gs, int kk, int d
   return v;
 }
 
-// dq from the stored score gradients (causal): one workgroup per pair of
-// consecutive query rows (heaviest first), 8 waves, two per SIMD: wave w
+// dq from the stored score gradients (causal or window): one workgroup per
+// pair of consecutive query rows (heaviest first), 8 waves, two per SIMD: wave w
 // owns heads 16 (w & 3) .. +15 of row r_hi - (w >> 2). Per tile only
 // dQ^T += K^T . dS^T remains, with dS^T read from the stored tile in operand
 // order (16 B per lane and k-step, the next tile's prefetched during the
 // current one). Both rows walk the union of their causal block ranges; a row
 // takes zero dS on a block outside its own range. Each copied K tile serves
 // both rows.
+template <int OP>
 __global__ __launch_bounds__(2 * bw::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_ds_bf16_kernel(BwdArgs a) {
   using namespace bw;
@@ -481,8 +488,8 @@ void bwd_dq_ds_bf16_kernel(BwdArgs a) {
   const int b = blockIdx.x / npair;
   const int r_hi = g.Sq - 1 - 2 * (blockIdx.x % npair);
   const int r_lo = r_hi - 1;                       // -1: no second row
-  const RowRange ra = row_range(g, kScore, b, r_hi, 0);
-  const RowRange rb = r_lo >= 0 ? row_range(g, kScore, b, r_lo, 0) : ra;
+  const RowRange ra = row_range(g, OP, b, r_hi, a.window);
+  const RowRange rb = r_lo >= 0 ? row_range(g, OP, b, r_lo, a.window) : ra;
   const int jf = min(ra.j_first, rb.j_first), jl = max(ra.j_last, rb.j_last);
   const int ntiles = jl - jf + 1;
   // this wave's row
@@ -503,7 +510,7 @@ void bwd_dq_ds_bf16_kernel(BwdArgs a) {
 #pragma unroll
     for (int G = 0; G < 9; ++G) dma16(src + 128 * G, dst + G * GR);
   });
-  const long long base = has_row ? a.ds_entry[b] + causal_tiles_before(g, b, r) : 0;
+  const long long base = has_row ? ds_row_base(a, b, r) : 0;
   const bf16* dsp = a.ds_tiles + (base * 4 + hw) * 2 * 512 + lane * 8;  // row tile t: + 4096 t
   const bf16x8 zero8 = {};
   auto ds_load = [&](int j, bf16x8* d) __attribute__((always_inline)) {
@@ -703,7 +710,7 @@ void bwd_dq_bf16_kernel(BwdArgs a) {
   for (int db = 0; db < DBK; ++db) *(f32x4*)(out + 16 * db) = acc[db];
 }
 
-// STORE (causal only): also write each stage's dS to the stored tiles. The
+// STORE (causal and window): also write each stage's dS to the stored tiles. The
 // lanes hold dS for one key and eight heads; the dq kernel wants one head and
 // eight keys, so a stage's 64 x 32 dS tile goes through LDS ([key][head], 64 B
 // rows, written a few MFMAs into phase 2) and read back during phase 1 of
@@ -769,14 +776,14 @@ void bwd_dkv_bf16_kernel(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < DBK; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // STORE: first stored tile of the current row (rows of a causal item are
-  // consecutive), the previous stage's target and its transposed dS.
+  // STORE: first stored tile of the current row (rows of a causal or window
+  // item are consecutive), the previous stage's target and its transposed dS.
   long long rbase = 0;
   int prev_nt = 0;
   bf16* st_prev = nullptr;
   const int tr_off = (32 * (wave & 1) + 4 * grp + (l16 >> 2)) * 64 + 32 * (wave >> 1) + 8 * (l16 & 3);
   if (STORE) {
-    rbase = a.ds_entry[b] + causal_tiles_before(g, b, row_at(0));
+    rbase = ds_row_base(a, b, row_at(0));
     st_prev = a.ds_dummy + wave * 512 + lane * 8;
   }
 
@@ -788,7 +795,7 @@ void bwd_dkv_bf16_kernel(BwdArgs a) {
     const RowRange rr = row_range(g, OP, b, r, a.window);
     bf16* st_cur = nullptr;
     if (STORE) {
-      if (s > 0 && (s & 1) == 0) rbase += prev_nt;
+      if (s > 0 && (s & 1) == 0) rbase += a.ds_stride > 0 ? a.ds_stride : prev_nt;
       prev_nt = rr.j_last - rr.j_first + 1;
       const long long slot = rbase + (j - rr.j_first);
       st_cur = a.ds_tiles + ((slot * 4 + 2 * (s & 1) + (wave >> 1)) * 2 + (wave & 1)) * 512 + lane * 8;
@@ -1179,13 +1186,14 @@ void launch_bf16(const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(bwd_plan_kernel, dim3(1), dim3(256), 0, s, a, OP);
   if (OP == kGather)
     hipLaunchKernelGGL(bwd_gfill_kernel, dim3(g.B * a.row_tiles), dim3(256), 0, s, a);
-  if (OP == kScore && a.ds_tiles != nullptr) {
+  if (OP != kGather && a.ds_tiles != nullptr) {
     // stored score gradients: the key-block pass writes dS, dq reads it
-    hipLaunchKernelGGL(bwd_ds_entry_kernel, dim3(1), dim3(256), 0, s, a);
+    if (a.ds_stride == 0) hipLaunchKernelGGL(bwd_ds_entry_kernel, dim3(1), dim3(256), 0, s, a);
     if (a.items > 0)
-      hipLaunchKernelGGL((bwd_dkv_bf16_kernel<kScore, true>), dim3(a.items), dim3(bw::NT), 0, s, a);
-    hipLaunchKernelGGL(bwd_dq_ds_bf16_kernel, dim3(g.B * ((g.Sq + 1) / 2)), dim3(2 * bw::NT), 0, s,
-                       a);
+      hipLaunchKernelGGL((bwd_dkv_bf16_kernel<OP == kGather ? kScore : OP, true>), dim3(a.items),
+                         dim3(bw::NT), 0, s, a);
+    hipLaunchKernelGGL(bwd_dq_ds_bf16_kernel<OP == kGather ? kScore : OP>,
+                       dim3(g.B * ((g.Sq + 1) / 2)), dim3(2 * bw::NT), 0, s, a);
   } else {
     hipLaunchKernelGGL(bwd_dq_bf16_kernel<OP>, dim3(g.B * g.Sq), dim3(bw::NT), 0, s, a);
     if (a.items > 0)
@@ -1271,10 +1279,17 @@ BwdLayout bwd_layout(const Geom& g, int op, int top_k, int window, bool store_ds
     L.part = off;
     off = align256(off + (size_t)L.items * 64 * g.Dk * sizeof(float));
   }
-  if (store_ds && op == kScore) {
-    // 64 heads x 64 keys of bf16 per (row, causal block)
+  if (store_ds && op != kGather) {
+    // 64 heads x 64 keys of bf16 per (row, block of its range); a window of
+    // W keys meets at most ceil((W - 1) / BS) + 1 blocks
     long long tiles = 0;
-    for (int b = 0; b < g.B; ++b) tiles += causal_tiles_before(g, b, g.Sq);
+    if (op == kScore) {
+      for (int b = 0; b < g.B; ++b) tiles += causal_tiles_before(g, b, g.Sq);
+    } else {
+      const long long per = std::min<long long>((window - 1 + (long long)g.BS - 1) / g.BS + 1, g.NB);
+      L.ds_stride = (int)per;
+      tiles = (long long)g.B * g.Sq * per;
+    }
     L.store_ds = true;
     L.ds_entry = off;
     off = align256(off + (size_t)(g.B + 1) * sizeof(long long));

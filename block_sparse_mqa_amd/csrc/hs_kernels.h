@@ -80,13 +80,15 @@ struct BwdArgs {
   int* g_off;                // gather: [B * NB] start of each block's row list
   int* g_rows;               // gather: row lists of all blocks, rows ascending
   float* part;               // [items, 64, Dk] per-item key-block gradient partials
-  // Stored score gradients (causal bf16 only; nullptr: dq recomputes them).
-  // Row (b, r) owns tiles ds_entry[b] + tiles_before(b, r) .. + its causal
-  // block count; tile t of a row holds dS (scale included, bf16) of its 64
-  // heads x 64 keys in the dq kernel's operand order [head block 4][k-step
-  // 2][lane 64][8].
+  // Stored score gradients (causal and window, bf16; nullptr: dq recomputes
+  // them). Tile t of a row holds dS (scale included, bf16) of its 64 heads x
+  // the 64 keys of the row's t-th block, in the dq kernel's operand order
+  // [head block 4][k-step 2][lane 64][8]. Causal (ds_stride 0): row (b, r)
+  // owns tiles ds_entry[b] + tiles_before(b, r) .. + its block count; window:
+  // tiles (b Sq + r) ds_stride .. (ds_stride bounds a row's block count).
   __bf16* ds_tiles;
-  long long* ds_entry;       // [B + 1] first tile of each entry; [B] = total
+  int ds_stride;
+  long long* ds_entry;       // causal: [B + 1] first tile of each entry; [B] = total
   __bf16* ds_dummy;          // 4 KB target of the no-op store of a stage with no predecessor
   int chunk_rows;            // R: rows per chunk (multiple of 64)
   int n_chunks;              // C = ceil(Sq / R)
@@ -100,11 +102,11 @@ struct BwdArgs {
 struct BwdLayout {
   size_t dsum, sink_part, first, nrows, pre, cnt, total_g, off_g, rows, part, ds_entry, ds_dummy,
       ds_tiles, total;
-  int n_pre, rows_per_pre, chunk_rows, n_chunks, items, row_tiles;
+  int n_pre, rows_per_pre, chunk_rows, n_chunks, items, row_tiles, ds_stride;
   bool store_ds;
 };
 
-// store_ds: also lay out the stored score gradients (causal bf16 only).
+// store_ds: also lay out the stored score gradients (causal and window).
 BwdLayout bwd_layout(const Geom& g, int op, int top_k, int window, bool store_ds);
 int bwd_launch(int op, const BwdArgs& a, bool bf16, hipStream_t stream);
 

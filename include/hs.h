@@ -97,8 +97,9 @@ typedef enum {
   HS_OP_BLOCK_SCORE_BWD = 3,    /* workspace of hs_block_score_bwd   */
   HS_OP_SPARSE_GATHER_BWD = 4,  /* workspace of hs_sparse_gather_bwd */
   HS_OP_SWA_BWD = 5,            /* workspace of hs_swa_bwd           */
-  HS_OP_BLOCK_SCORE_BWD_STORE_DS = 6 /* larger workspace of hs_block_score_bwd
-                                        that also holds the score gradients */
+  HS_OP_BLOCK_SCORE_BWD_STORE_DS = 6, /* larger workspace of hs_block_score_bwd
+                                         that also holds the score gradients */
+  HS_OP_SWA_BWD_STORE_DS = 7    /* the same for hs_swa_bwd           */
 } hs_op;
 
 typedef struct {
@@ -232,7 +233,11 @@ hs_status hs_sparse_gather_bwd(const hs_problem* p, const void* q, const void* k
 
 /* Gradients of hs_swa_fwd (review of PaddleFleet PR 1453, the windowed
  * backward comments: a sequence length that is not a multiple of the tile
- * must read no row past its end; here every row index is bounded by Sq). */
+ * must read no row past its end; here every row index is bounded by Sq).
+ * Given at least the HS_OP_SWA_BWD_STORE_DS workspace (bf16 only; 8 KB per
+ * row and per block a window of that size can meet, ceil((window - 1) / 64)
+ * + 1, at most the block count), dq is computed from the score gradients the
+ * key-block pass stores, as for hs_block_score_bwd. */
 hs_status hs_swa_bwd(const hs_problem* p, const void* q, const void* kv, const float* sink,
                      int32_t window, const void* out, const float* lse, const void* dout,
                      float* dq, float* dkv, float* dsink, void* ws, size_t ws_bytes,

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(hs.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.hs_version() == 104
+    assert lib.hs_version() == 105
 
 
 def _mla(**kw):
@@ -301,3 +301,29 @@ def test_stored_score_gradient_workspace_f32_unchanged():
     p = hs.Problem(1, 100, 100, 8, 96, 64, dtype="f32")
     assert hs.hs_workspace_size(p, hs.HS_OP_BLOCK_SCORE_BWD_STORE_DS) == \
         hs.hs_workspace_size(p, hs.HS_OP_BLOCK_SCORE_BWD)
+
+
+@pytest.mark.parametrize("B,Sq,Skv,window,kv_lens,per_row", [
+    (1, 130, 130, 70, None, 3),            # ceil(69 / 64) + 1
+    (1, 32768, 32768, 1024, None, 17),
+    (1, 300, 300, 1, None, 1),
+    (1, 100, 100, 5000, None, 2),          # capped at the block count
+    (2, 70, 200, 64, [200, 150], 2),
+])
+def test_stored_window_gradient_workspace(B, Sq, Skv, window, kv_lens, per_row):
+    """The larger window-gradient workspace adds 8 KB per row for each block a
+    window of that size can meet (ceil((window - 1) / 64) + 1, at most the
+    block count), plus the same small pieces as the causal one; that bound
+    holds for every row (checked row by row)."""
+    kw = {"kv_lens": kv_lens} if kv_lens else {}
+    p = hs.Problem(B, Sq, Skv, 64, 576, 512, **kw)
+    n5 = hs.hs_workspace_size(p, hs.HS_OP_SWA_BWD, window=window)
+    n7 = hs.hs_workspace_size(p, hs.HS_OP_SWA_BWD_STORE_DS, window=window)
+    a256 = lambda x: (x + 255) // 256 * 256
+    assert n7 - n5 == a256((B + 1) * 8) + a256(4096) + a256(B * Sq * per_row * 8192), (n5, n7)
+    for b in range(B):
+        L = kv_lens[b] if kv_lens else Skv
+        for r in range(0, Sq, max(1, Sq // 500)):
+            pos = L - Sq + r
+            lo = max(pos - window + 1, 0)
+            assert pos // 64 - lo // 64 + 1 <= per_row

@@ -50,9 +50,10 @@ def _gpu_grads(d, op, dout, idx=None, K=None):
         out, lse, _ = hs.block_score(d.prob, d.q, d.kv, d.sink)
         return hs.block_score_bwd(d.prob, d.q, d.kv, d.sink, out, lse, dout,
                                   store_ds=op == "score")
-    if op == "swa":
+    if op in ("swa", "swa_recompute"):
         out, lse = hs.swa(d.prob, d.q, d.kv, d.sink, p.window)
-        return hs.swa_bwd(d.prob, d.q, d.kv, d.sink, p.window, out, lse, dout)
+        return hs.swa_bwd(d.prob, d.q, d.kv, d.sink, p.window, out, lse, dout,
+                          store_ds=op == "swa")
     out, lse = hs.sparse_gather(d.prob, d.q, d.kv, d.sink, idx, K)
     return hs.sparse_gather_bwd(d.prob, d.q, d.kv, d.sink, idx, K, out, lse, dout)
 
@@ -62,7 +63,7 @@ def _oracle_grads(d, op, dout_cpu, idx=None, rows=None):
     kw = dict(d.kw(), rows=rows)
     if op in ("score", "score_recompute"):
         return ref.block_score_bwd(p.q, p.kv, d.sink_cpu, p.Dv, p.scale, dout_cpu, **kw)
-    if op == "swa":
+    if op in ("swa", "swa_recompute"):
         return ref.swa_bwd(p.q, p.kv, d.sink_cpu, p.Dv, p.scale, p.window, dout_cpu, **kw)
     return ref.sparse_gather_bwd(p.q, p.kv, d.sink_cpu, p.Dv, p.scale, idx, dout_cpu, **kw)
 
@@ -103,7 +104,7 @@ def test_gradients_match_oracle(name):
     torch.cuda.synchronize()
     idx_cpu = idx.cpu().numpy()
     res = {}
-    for op in ("score", "score_recompute", "swa", "gather"):
+    for op in ("score", "score_recompute", "swa", "swa_recompute", "gather"):
         g = _gpu_grads(d, op, dout, idx, p.top_k)
         torch.cuda.synchronize()
         w = _oracle_grads(d, op, dout_cpu, idx_cpu)
@@ -148,7 +149,7 @@ def test_gradients_are_deterministic():
     dout = inputs.make_dout(p, seed=42).cuda()
     _, _, bl = hs.block_score(d.prob, d.q, d.kv, d.sink)
     idx = hs.topk_blocks(d.prob, bl, p.top_k)
-    for op in ("score", "score_recompute", "swa", "gather"):
+    for op in ("score", "score_recompute", "swa", "swa_recompute", "gather"):
         a = _gpu_grads(d, op, dout, idx, p.top_k)
         b = _gpu_grads(d, op, dout, idx, p.top_k)
         torch.cuda.synchronize()
@@ -254,18 +255,25 @@ def test_sink_without_its_gradient():
 
 
 def test_stored_and_recomputed_score_gradients_agree():
-    """The two workspaces of the causal gradient: the key-block pass is the
-    same arithmetic in both (dkv and dsink bit-identical); dq from the stored
-    bf16 score gradients matches dq that recomputes them up to dS rounding."""
+    """The two workspaces of the causal and window gradients: the key-block
+    pass is the same arithmetic in both (dkv and dsink bit-identical); dq from
+    the stored bf16 score gradients matches dq that recomputes them up to dS
+    rounding."""
     p = _mla("paths_S700", 700, 44, 2, 64)
     say(f"[gpu] stored vs recomputed score gradients, S={p.Sq}")
     d = Dev(p)
     dout = inputs.make_dout(p, seed=45).cuda()
     out, lse, _ = hs.block_score(d.prob, d.q, d.kv, d.sink)
-    a = hs.block_score_bwd(d.prob, d.q, d.kv, d.sink, out, lse, dout, store_ds=True)
-    b = hs.block_score_bwd(d.prob, d.q, d.kv, d.sink, out, lse, dout, store_ds=False)
-    torch.cuda.synchronize()
-    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
-    err = ((a[0] - b[0]).abs().max() / b[0].abs().max()).item()
-    say(f"[gpu] dq stored vs recomputed: max |diff| / max |dq| = {err:.2e}")
-    assert err < 1e-2
+    ow, lw = hs.swa(d.prob, d.q, d.kv, d.sink, p.window)
+    for name, call in (
+            ("causal", lambda st: hs.block_score_bwd(d.prob, d.q, d.kv, d.sink, out, lse, dout,
+                                                     store_ds=st)),
+            ("window", lambda st: hs.swa_bwd(d.prob, d.q, d.kv, d.sink, p.window, ow, lw, dout,
+                                             store_ds=st))):
+        a = call(True)
+        b = call(False)
+        torch.cuda.synchronize()
+        assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2]), name
+        err = ((a[0] - b[0]).abs().max() / b[0].abs().max()).item()
+        say(f"[gpu] {name} dq stored vs recomputed: max |diff| / max |dq| = {err:.2e}")
+        assert err < 1e-2, name
