@@ -22,6 +22,9 @@
 //   dq      : one workgroup per query row, walking the row's key tiles
 //   dkv     : one workgroup per (key block, chunk of rows): partial gradients
 //   reduce  : fixed-order sum of each block's partials into dkv
+// With the larger causal or window workspace, dkv runs first and also stores
+// the bf16 score gradients dS, and dq (one workgroup per pair of rows) reads
+// them instead of recomputing the scores (bwd_dq_ds_bf16_kernel).
 // Every workspace word is written before it is read (no memset), and every
 // sum runs in a fixed order, so results are reproducible bit for bit.
 //
@@ -469,9 +472,9 @@ __device__ __forceinline__ bf16x8 frag_t(const char* base, int gs, int kk, int d
 // owns heads 16 (w & 3) .. +15 of row r_hi - (w >> 2). Per tile only
 // dQ^T += K^T . dS^T remains, with dS^T read from the stored tile in operand
 // order (16 B per lane and k-step, the next tile's prefetched during the
-// current one). Both rows walk the union of their causal block ranges; a row
-// takes zero dS on a block outside its own range. Each copied K tile serves
-// both rows.
+// current one). Both rows walk the union of their block ranges; a row takes
+// zero dS on a block outside its own range. Each copied K tile serves both
+// rows.
 template <int OP>
 __global__ __launch_bounds__(2 * bw::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_ds_bf16_kernel(BwdArgs a) {
