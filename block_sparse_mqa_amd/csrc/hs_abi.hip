@@ -19,6 +19,7 @@
 
 #include "../../include/hs.h"
 #include "hs_common.h"
+#include "hs_bwd_args.h"
 #include "hs_kernels.h"
 
 namespace {

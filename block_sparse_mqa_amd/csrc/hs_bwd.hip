@@ -53,7 +53,7 @@
 
 #include "hs_common.h"
 #include "hs_gfx950.h"
-#include "hs_kernels.h"
+#include "hs_bwd_args.h"
 
 namespace hs {
 
