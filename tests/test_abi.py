@@ -297,10 +297,23 @@ def test_stored_score_gradient_workspace(B, Sq, Skv, kv_lens, doc_lens):
 
 
 def test_stored_score_gradient_workspace_f32_unchanged():
-    """The fp32 shapes always recompute: both queries give the same size."""
+    """The fp32 shapes always recompute: both queries give the same size, for
+    the causal and the window gradient."""
     p = hs.Problem(1, 100, 100, 8, 96, 64, dtype="f32")
     assert hs.hs_workspace_size(p, hs.HS_OP_BLOCK_SCORE_BWD_STORE_DS) == \
         hs.hs_workspace_size(p, hs.HS_OP_BLOCK_SCORE_BWD)
+    assert hs.hs_workspace_size(p, hs.HS_OP_SWA_BWD_STORE_DS, window=30) == \
+        hs.hs_workspace_size(p, hs.HS_OP_SWA_BWD, window=30)
+
+
+def test_workspace_query_rejects_unknown_ops():
+    """Op codes past the last one and a window below 1 for the window
+    gradient's larger workspace are errors."""
+    p = _mla()
+    with pytest.raises(ValueError):
+        hs.hs_workspace_size(p, hs.HS_OP_SWA_BWD_STORE_DS + 1)
+    with pytest.raises(ValueError):
+        hs.hs_workspace_size(p, hs.HS_OP_SWA_BWD_STORE_DS, window=0)
 
 
 @pytest.mark.parametrize("B,Sq,Skv,window,kv_lens,per_row", [

@@ -176,16 +176,22 @@ def test_long_context_sampled():
     sampled = np.array([0, 1, 63, 64, 65, 1000, 4095, 4096, 20000, S - 65])
     rows = np.concatenate([sampled, last])
     idx_cpu = idx.cpu().numpy()
-    for op in ("score", "swa", "gather"):
-        g = _gpu_grads(d, op, dout, idx, p.top_k)
-        torch.cuda.synchronize()
-        dq = np64(g[0][0, torch.from_numpy(rows).cuda()])[None]
-        dkv_last = np64(g[1][0, S - 64:])[None]
+    # the causal and window calls through both workspaces (stored and
+    # recomputed score gradients), against one oracle evaluation each
+    for op, variants in (("score", ("score", "score_recompute")), ("swa", ("swa", "swa_recompute")),
+                         ("gather", ("gather",))):
+        got = []
+        for v in variants:
+            g = _gpu_grads(d, v, dout, idx, p.top_k)
+            torch.cuda.synchronize()
+            got.append((v, np64(g[0][0, torch.from_numpy(rows).cuda()])[None],
+                        np64(g[1][0, S - 64:])[None]))
+            del g
         say(f"[gpu] gradients long context {op}: GPU done, oracle on {len(rows)} rows")
         w = _oracle_grads(d, op, dout_cpu[:, rows], idx_cpu, rows=rows)
-        _grad_close(dq, w[0], "bf16", f"{op} dq sampled")
-        _grad_close(dkv_last, w[1][:, S - 64:], "bf16", f"{op} dkv last block")
-        del g
+        for v, dq, dkv_last in got:
+            _grad_close(dq, w[0], "bf16", f"{v} dq sampled")
+            _grad_close(dkv_last, w[1][:, S - 64:], "bf16", f"{v} dkv last block")
     say("[gpu] gradients long context: ok")
 
 
