@@ -157,8 +157,7 @@ void attn_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char buf_a[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char buf_b[TILE_BYTES];
   __shared__ float bl_slot[2][NW];
-  __shared__ int tile_list[64];
-  __shared__ int tile_count;
+  __shared__ int tile_list[NW][64];
 
   const Geom& g = a.g;
   const int lane = threadIdx.x & 63;
@@ -182,23 +181,23 @@ void attn_bf16_kernel(AttnArgs a) {
   // allowed key range (compacted in order of the list).
   int ntiles;
   if (OP == kGather) {
-    if (wave == 0) {
-      int j = -1;
-      bool ok = false;
-      if (lane < a.top_k) {
-        j = a.block_idx[row * a.top_k + lane];
-        if (j >= 0 && j < nb_b) {
-          const Blk bk = block_rows<PAGED>(g, b, j);
-          ok = !(bk.start > rr.hi || bk.start + bk.len - 1 < rr.lo);
-        }
+    // Every wave builds its own copy of the list (same indices, same result),
+    // so no workgroup barrier separates it from the first copy and Q loads.
+    int j = -1;
+    bool ok = false;
+    if (lane < a.top_k) {
+      j = a.block_idx[row * a.top_k + lane];
+      if (j >= 0 && j < nb_b) {
+        const Blk bk = block_rows<PAGED>(g, b, j);
+        ok = !(bk.start > rr.hi || bk.start + bk.len - 1 < rr.lo);
       }
-      const unsigned long long m = __ballot(ok);
-      const int pos = __popcll(m & ((1ull << lane) - 1ull));
-      if (ok) tile_list[pos] = j;
-      if (lane == 0) tile_count = __popcll(m);
     }
-    __syncthreads();
-    ntiles = tile_count;
+    const unsigned long long m = __ballot(ok);
+    const int pos = __popcll(m & ((1ull << lane) - 1ull));
+    if (ok) tile_list[wave][pos] = j;
+    ntiles = __popcll(m);
+    // LDS operations of one wave complete in order: the reads below see these writes
+    __builtin_amdgcn_wave_barrier();
   } else {
     ntiles = rr.j_last - rr.j_first + 1;
   }
@@ -216,7 +215,7 @@ void attn_bf16_kernel(AttnArgs a) {
       return;
     }
   }
-  auto tile_block = [&](int t) -> int { return OP == kGather ? tile_list[t] : rr.j_first + t; };
+  auto tile_block = [&](int t) -> int { return OP == kGather ? tile_list[wave][t] : rr.j_first + t; };
 
   // Block-score columns this row never visits are -inf.
   if (OP == kScore && split == 0) {
