@@ -311,6 +311,12 @@ def suite_config(c, dev, stream, peaks, oracle_budget):
                                                          w3, stream),
         "swa": lambda: hs.hs_swa_fwd(prob, q, kv, sink, p.window, out, lse, w4, stream),
     }
+    # both branches of a sliding-window layer in one call (window, then the
+    # selected blocks of this workload's own top-k)
+    out2, lse2 = torch.empty_like(out), torch.empty_like(lse)
+    w8 = ws(hs.HS_OP_SWA_SPARSE, top_k=p.top_k, window=p.window)
+    calls["swa_sparse"] = lambda: hs.hs_swa_sparse_fwd(prob, q, kv, sink, p.window, idx, p.top_k,
+                                                       out2, lse2, out, lse, w8, stream)
     calls["block_score"](); calls["topk"](); torch.cuda.synchronize()
     idx_cpu = idx.cpu().numpy()
     # Gradients of the three attention calls, each from its own forward outputs.
@@ -344,6 +350,9 @@ def suite_config(c, dev, stream, peaks, oracle_budget):
                           qb + ob + lb + p.B * p.Sq * p.top_k * 4 + int(gather.sum()) * p.Dk * es),
         "swa": (int(window.sum()) * H * fpp, qb + kv_rows["swa"] * p.Dk * es + ob + lb),
     }
+    work["swa_sparse"] = (int(window.sum()) * H * fpp + int(gather.sum()) * H * fpp,
+                          qb + kv_rows["swa"] * p.Dk * es + 2 * (ob + lb) +
+                          p.B * p.Sq * p.top_k * 4 + int(gather.sum()) * p.Dk * es)
     # Gradients: five contractions per pair (S recomputed, dP, dQ, dK, dV), i.e.
     # 2 (3 Dk + 2 Dv) flops; bytes: q, kv rows, out, dout, lse, dq and dkv in fp32.
     fpb = 2 * (3 * p.Dk + 2 * p.Dv)
@@ -439,9 +448,13 @@ def write_suite_md(path, peaks, results, args):
     L.append("`*_bwd` are the gradient calls (dq, dkv and the sink gradient) of the three attention "
              "operations, each fed its own forward outputs; their flops are 2 (3 Dk + 2 Dv) per "
              "(query-head, key) pair (score recomputed, dP, dQ, dK, dV) and their bytes count q, the "
-             "KV rows, out, dout, lse and the fp32 dq and dkv. The implementation recomputes the "
-             "scores and dP in both of its kernels, so the MFMA pipe executes 1.4 times the counted "
-             "flops.\n")
+             "KV rows, out, dout, lse and the fp32 dq and dkv. With the larger workspaces (chosen "
+             "when they fit in half the free memory) the causal and window calls store the score "
+             "gradients and execute exactly the counted flops; the gather call and the fp32 shapes "
+             "recompute the scores and dP in both of their kernels, 1.4 times the counted flops.\n")
+    L.append("`swa_sparse` is `hs_swa_sparse_fwd`: the window and the selected-block branches of a "
+             "sliding-window layer in one call (separate outputs), its work the sum of `swa` and "
+             "`sparse_gather`.\n")
     L.append("`score_topk_fused` is `hs_block_score_topk_fwd` (block scores and the top-k in one call; "
              "its work is counted as the block score's). Metric path (block score + top-k + gather; "
              "with the fused call in place of the first two) and the float64 oracle on the host:\n")

@@ -3,7 +3,7 @@ MQA sparse-attention path (forward operations and their gradients).
 
 The entry points mirror the C ABI of ``include/hs.h`` one to one
 (``hs_block_score_fwd``, ``hs_topk_blocks``, ``hs_block_score_topk_fwd``,
-``hs_sparse_gather_fwd``, ``hs_swa_fwd``, the gradients ``hs_block_score_bwd``,
+``hs_sparse_gather_fwd``, ``hs_swa_fwd``, ``hs_swa_sparse_fwd``, the gradients ``hs_block_score_bwd``,
 ``hs_sparse_gather_bwd`` and ``hs_swa_bwd``, ``hs_num_blocks``,
 ``hs_workspace_size``). They only marshal
 arguments: tensors are device buffers owned by the caller (PyTorch provides
@@ -30,9 +30,10 @@ HS_BF16, HS_F32 = 0, 1
 HS_OP_BLOCK_SCORE, HS_OP_SPARSE_GATHER, HS_OP_SWA = 0, 1, 2
 HS_OP_BLOCK_SCORE_BWD, HS_OP_SPARSE_GATHER_BWD, HS_OP_SWA_BWD = 3, 4, 5
 HS_OP_BLOCK_SCORE_BWD_STORE_DS, HS_OP_SWA_BWD_STORE_DS = 6, 7
+HS_OP_SWA_SPARSE = 8
 
 EXPORTS = ("hs_num_blocks", "hs_workspace_size", "hs_block_score_fwd", "hs_topk_blocks",
-           "hs_block_score_topk_fwd", "hs_sparse_gather_fwd", "hs_swa_fwd",
+           "hs_block_score_topk_fwd", "hs_sparse_gather_fwd", "hs_swa_fwd", "hs_swa_sparse_fwd",
            "hs_block_score_bwd", "hs_sparse_gather_bwd", "hs_swa_bwd", "hs_status_string",
            "hs_last_error", "hs_version")
 
@@ -80,6 +81,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hs_sparse_gather_fwd.restype = i32
     lib.hs_swa_fwd.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, sz, vp]
     lib.hs_swa_fwd.restype = i32
+    lib.hs_swa_sparse_fwd.argtypes = [P, vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.hs_swa_sparse_fwd.restype = i32
     lib.hs_block_score_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hs_block_score_bwd.restype = i32
     lib.hs_sparse_gather_bwd.argtypes = [P, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz,
@@ -235,6 +238,18 @@ def hs_swa_fwd(prob, q, kv, sink, window, out, lse, ws=None, stream=None):
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def hs_swa_sparse_fwd(prob, q, kv, sink, window, block_idx, top_k, out_swa, lse_swa, out_sparse,
+                      lse_sparse, ws=None, stream=None):
+    for n, t in (("q", q), ("kv", kv), ("sink", sink), ("block_idx", block_idx),
+                 ("out_swa", out_swa), ("lse_swa", lse_swa), ("out_sparse", out_sparse),
+                 ("lse_sparse", lse_sparse), ("ws", ws)):
+        _dev(n, t)
+    _check(load_library().hs_swa_sparse_fwd(
+        prob.ref, _ptr(q), _ptr(kv), _ptr(sink), int(window), _ptr(block_idx), int(top_k),
+        _ptr(out_swa), _ptr(lse_swa), _ptr(out_sparse), _ptr(lse_sparse), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
 def _nbytes(ws) -> int:
     return 0 if ws is None else ws.numel() * ws.element_size()
 
@@ -326,6 +341,22 @@ def swa(prob, q, kv, sink, window, stream=None):
     hs_swa_fwd(prob, q, kv, sink, window, out, lse, _workspace(prob, HS_OP_SWA, window=window),
                stream)
     return out, lse
+
+
+def swa_sparse(prob, q, kv, sink, window, block_idx, top_k, stream=None):
+    """Both branches of a sliding-window layer over the shared latent KV and a
+    given block selection: (out_swa, lse_swa, out_sparse, lse_sparse), equal
+    to swa(...) and sparse_gather(...) for the same arguments."""
+    import torch
+    shape_o = (prob.B, prob.Sq, prob.H, prob.Dv)
+    shape_l = (prob.B, prob.Sq, prob.H)
+    ow = torch.empty(shape_o, dtype=_torch_dtype(prob), device=q.device)
+    lw = torch.empty(shape_l, dtype=torch.float32, device=q.device)
+    og = torch.empty(shape_o, dtype=_torch_dtype(prob), device=q.device)
+    lg = torch.empty(shape_l, dtype=torch.float32, device=q.device)
+    hs_swa_sparse_fwd(prob, q, kv, sink, window, block_idx, top_k, ow, lw, og, lg,
+                      _workspace(prob, HS_OP_SWA_SPARSE, top_k=top_k, window=window), stream)
+    return ow, lw, og, lg
 
 
 def _grad_buffers(prob, q, sink):

@@ -391,7 +391,7 @@ hs_status launch_bwd(int op, const hs_problem* p, const void* q, const void* kv,
 
 extern "C" {
 
-int32_t hs_version(void) { return 105; }
+int32_t hs_version(void) { return 106; }
 
 const char* hs_status_string(int32_t status) {
   switch (status) {
@@ -418,8 +418,19 @@ hs_status hs_workspace_size(const hs_problem* p, int32_t op, int32_t top_k, int3
   hs_status st = prepare(p, g);
   if (st != HS_OK) return st;
   if (!bytes) return fail(HS_ERR_INVALID_ARG, "bytes is NULL");
-  if (op < HS_OP_BLOCK_SCORE || op > HS_OP_SWA_BWD_STORE_DS)
+  if (op < HS_OP_BLOCK_SCORE || op > HS_OP_SWA_SPARSE)
     return fail(HS_ERR_INVALID_ARG, "unknown op %d", op);
+  if (op == HS_OP_SWA_SPARSE) {
+    // the two branches run one after the other when they do not run as one
+    // pass, so the larger of their workspaces serves both
+    if (top_k < 1 || top_k > 64) return fail(HS_ERR_INVALID_ARG, "top_k must be in 1..64 (got %d)", top_k);
+    if (window < 1) return fail(HS_ERR_INVALID_ARG, "window must be >= 1 (got %d)", window);
+    *bytes = p->dtype == HS_BF16
+                 ? std::max(split_ws_bytes(g, plan_split(g, HS_OP_SWA, top_k, window).nsplit),
+                            split_ws_bytes(g, plan_split(g, HS_OP_SPARSE_GATHER, top_k, window).nsplit))
+                 : 0;
+    return HS_OK;
+  }
   if (op >= HS_OP_BLOCK_SCORE_BWD) {
     const int kop = (op == HS_OP_SWA_BWD || op == HS_OP_SWA_BWD_STORE_DS) ? hs::kSwa
                     : op == HS_OP_SPARSE_GATHER_BWD                       ? hs::kGather
@@ -450,6 +461,54 @@ hs_status hs_block_score_topk_fwd(const hs_problem* p, const void* q, const void
                                   size_t ws_bytes, void* stream) {
   return launch_attn(HS_OP_BLOCK_SCORE, p, q, kv, sink, nullptr, 0, 0, out, lse, block_logit, ws,
                      ws_bytes, stream, block_idx, top_k);
+}
+
+hs_status hs_swa_sparse_fwd(const hs_problem* p, const void* q, const void* kv, const float* sink,
+                            int32_t window, const int32_t* block_idx, int32_t top_k, void* out_swa,
+                            float* lse_swa, void* out_sparse, float* lse_sparse, void* ws,
+                            size_t ws_bytes, void* stream) {
+  hs::Geom g;
+  hs_status st = prepare(p, g);
+  if (st != HS_OK) return st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(kv, "kv")) ||
+      (st = check_ptr(out_swa, "out_swa")) || (st = check_ptr(lse_swa, "lse_swa", 4)) ||
+      (st = check_ptr(out_sparse, "out_sparse")) || (st = check_ptr(lse_sparse, "lse_sparse", 4)) ||
+      (st = check_ptr(block_idx, "block_idx", 4)))
+    return st;
+  if (top_k < 1) return fail(HS_ERR_INVALID_ARG, "top_k must be >= 1 (got %d)", top_k);
+  if (top_k > 64) return fail(HS_ERR_UNSUPPORTED, "top_k %d exceeds 64", top_k);
+  if (window < 1) return fail(HS_ERR_INVALID_ARG, "window must be >= 1 (got %d)", window);
+  if (sink && reinterpret_cast<uintptr_t>(sink) % 4 != 0)
+    return fail(HS_ERR_INVALID_ARG, "sink is not 4-byte aligned");
+  // One pass over both branches on the in-place bf16 path when neither splits
+  // its key range; otherwise the two operations, one after the other.
+  const bool one_pass = p->dtype == HS_BF16 && !p->page_table && !p->kv_lens_device &&
+                        plan_split(g, HS_OP_SWA, top_k, window).nsplit == 1 &&
+                        plan_split(g, HS_OP_SPARSE_GATHER, top_k, window).nsplit == 1;
+  if (!one_pass) {
+    st = launch_attn(HS_OP_SWA, p, q, kv, sink, nullptr, 0, window, out_swa, lse_swa, nullptr, ws,
+                     ws_bytes, stream);
+    if (st != HS_OK) return st;
+    return launch_attn(HS_OP_SPARSE_GATHER, p, q, kv, sink, block_idx, top_k, 0, out_sparse,
+                       lse_sparse, nullptr, ws, ws_bytes, stream);
+  }
+  if (g.Sq * g.B == 0) return HS_OK;
+  hs::AttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = static_cast<const __bf16*>(q);
+  a.kv = static_cast<const __bf16*>(kv);
+  a.sink = sink;
+  a.out = static_cast<__bf16*>(out_sparse);
+  a.lse = lse_sparse;
+  a.out2 = static_cast<__bf16*>(out_swa);
+  a.lse2 = lse_swa;
+  a.block_idx = block_idx;
+  a.top_k = top_k;
+  a.window = window;
+  a.nsplit = 1;
+  a.g = g;
+  return hip_status(hs::attn_bf16_launch(hs::kSwaSparse, a, static_cast<hipStream_t>(stream)),
+                    "attention launch");
 }
 
 hs_status hs_sparse_gather_fwd(const hs_problem* p, const void* q, const void* kv,

@@ -174,13 +174,16 @@ void attn_bf16_kernel(AttnArgs a) {
   const int r = g.Sq - 1 - (w % g.Sq);
   const size_t row = (size_t)b * g.Sq + r;
 
-  const RowRange rr = row_range<PAGED>(g, OP, b, r, a.window);
+  const RowRange rr = row_range<PAGED>(g, OP == kSwaSparse ? kGather : OP, b, r, a.window);
   const int nb_b = nb_of_entry<PAGED>(g, b);
+  // window-and-sparse: the window branch's range; its n_w tiles come first
+  const RowRange rw = OP == kSwaSparse ? row_range<PAGED>(g, kSwa, b, r, a.window) : rr;
+  const int n_w = OP == kSwaSparse ? rw.j_last - rw.j_first + 1 : 0;
 
   // Tile sequence: a block range, or the listed blocks that intersect the
   // allowed key range (compacted in order of the list).
   int ntiles;
-  if (OP == kGather) {
+  if (OP == kGather || OP == kSwaSparse) {
     // Every wave builds its own copy of the list (same indices, same result),
     // so no workgroup barrier separates it from the first copy and Q loads.
     int j = -1;
@@ -195,7 +198,7 @@ void attn_bf16_kernel(AttnArgs a) {
     const unsigned long long m = __ballot(ok);
     const int pos = __popcll(m & ((1ull << lane) - 1ull));
     if (ok) tile_list[wave][pos] = j;
-    ntiles = __popcll(m);
+    ntiles = n_w + __popcll(m);
     // LDS operations of one wave complete in order: the reads below see these writes
     __builtin_amdgcn_wave_barrier();
   } else {
@@ -215,7 +218,10 @@ void attn_bf16_kernel(AttnArgs a) {
       return;
     }
   }
-  auto tile_block = [&](int t) -> int { return OP == kGather ? tile_list[wave][t] : rr.j_first + t; };
+  auto tile_block = [&](int t) -> int {
+    if (OP == kSwaSparse) return t < n_w ? rw.j_first + t : tile_list[wave][t - n_w];
+    return OP == kGather ? tile_list[wave][t] : rr.j_first + t;
+  };
 
   // Block-score columns this row never visits are -inf.
   if (OP == kScore && split == 0) {
@@ -272,15 +278,47 @@ void attn_bf16_kernel(AttnArgs a) {
   // chunk (l%8) ^ sw(key) in slot l%8; wave w issues kq = w and w + 4.
   const int cp_c8 = (lane & 7) ^ swz(8 * wave + (lane >> 3));
 
+  // Window-and-sparse: normalise and store one branch's output, then restart
+  // the online softmax (the sink again as the initial reference) for the next.
+  auto finalize_to = [&](bf16* outp, float* lsep) __attribute__((always_inline)) {
+    const float l_tot = sum_xor32(sum_xor16(l_run));
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    bf16* op = outp + (row * H + head) * DV + 4 * grp;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+      bf16x4 v;
+      v[0] = (bf16)(oacc[db][0] * inv);
+      v[1] = (bf16)(oacc[db][1] * inv);
+      v[2] = (bf16)(oacc[db][2] * inv);
+      v[3] = (bf16)(oacc[db][3] * inv);
+      *(bf16x4*)(op + 16 * db) = v;
+    }
+    if (grp == 0) lsep[row * H + head] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
+  };
+  auto restart = [&]() __attribute__((always_inline)) {
+    m_run = sk;
+    l_run = (sk > -INFINITY && grp == 0) ? 1.0f : 0.0f;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
   // One tile, processed as two 32-key halves so that in-order issue can
   // overlap VALU with MFMA: the softmax of half 0 runs between the score
   // MFMAs of half 1, the softmax of half 1 between the PV MFMAs of half 0,
   // and the block score between those of half 1. The copy of the next tile
   // is spread over the score MFMAs of half 0.
   auto step = [&](char* cur, char* nxt, int t) __attribute__((always_inline)) {
+    if constexpr (OP == kSwaSparse) {
+      if (t == n_w) {  // first selected block: the window branch is complete
+        finalize_to(a.out2, a.lse2);
+        restart();
+      }
+    }
     const int j = tile_block(t);
     const Blk blk = block_rows<PAGED>(g, b, j);
-    const int klo = rr.lo - blk.start, khi = min(rr.hi - blk.start, blk.len - 1);
+    const int rlo = (OP == kSwaSparse && t < n_w) ? rw.lo : rr.lo;
+    const int rhi = (OP == kSwaSparse && t < n_w) ? rw.hi : rr.hi;
+    const int klo = rlo - blk.start, khi = min(rhi - blk.start, blk.len - 1);
 
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // tile t resident; tile t-1 fully consumed; partials visible
@@ -487,6 +525,12 @@ void attn_bf16_kernel(AttnArgs a) {
     if (t + 1 < t_end) step(buf_b, buf_a, t + 1);
   }
   __builtin_amdgcn_s_waitcnt(0);  // the last tile's spare copy has landed
+  if constexpr (OP == kSwaSparse) {
+    if (t_end <= n_w) {  // no selected block met the row: the sparse branch is empty
+      finalize_to(a.out2, a.lse2);
+      restart();
+    }
+  }
 
   if (OP == kScore) {
     __syncthreads();
@@ -587,7 +631,8 @@ void launch_attn_kernels(int op, const AttnArgs& a, dim3 grid, dim3 block, hipSt
   if (a.nsplit == 1) {
     if (op == kScore) hipLaunchKernelGGL((attn_bf16_kernel<kScore, false, PAGED>), grid, block, 0, stream, a);
     else if (op == kGather) hipLaunchKernelGGL((attn_bf16_kernel<kGather, false, PAGED>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<kSwa, false, PAGED>), grid, block, 0, stream, a);
+    else if (op == kSwa) hipLaunchKernelGGL((attn_bf16_kernel<kSwa, false, PAGED>), grid, block, 0, stream, a);
+    else if constexpr (!PAGED) hipLaunchKernelGGL((attn_bf16_kernel<kSwaSparse, false, false>), grid, block, 0, stream, a);
   } else {
     if (op == kScore) hipLaunchKernelGGL((attn_bf16_kernel<kScore, true, PAGED>), grid, block, 0, stream, a);
     else if (op == kGather) hipLaunchKernelGGL((attn_bf16_kernel<kGather, true, PAGED>), grid, block, 0, stream, a);

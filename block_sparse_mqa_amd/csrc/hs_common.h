@@ -93,7 +93,9 @@ __host__ __device__ inline int block_of_pos(const Geom& g, const Doc& d, int p) 
 
 // Key range [lo, hi] a row may attend to for each operation, and the block
 // range that covers it.
-enum Op { kScore = 0, kGather = 1, kSwa = 2 };
+// kSwaSparse: both branches of a sliding-window layer in one pass, the
+// window's tiles and then the selected blocks' (separate outputs).
+enum Op { kScore = 0, kGather = 1, kSwa = 2, kSwaSparse = 3 };
 
 struct RowRange {
   int pos, lo, hi, j_first, j_last;

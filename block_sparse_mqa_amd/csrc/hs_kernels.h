@@ -18,6 +18,8 @@ struct AttnArgs {
   float* lse;
   float* block_logit;        // score operation only
   const int* block_idx;      // gather operation only
+  __bf16* out2;              // window-and-sparse operation: the window branch's out
+  float* lse2;               // and lse (out / lse hold the sparse branch's)
   int top_k;
   int window;
   int nsplit;                // > 1: split key range, partials merged after

@@ -99,7 +99,8 @@ typedef enum {
   HS_OP_SWA_BWD = 5,            /* workspace of hs_swa_bwd           */
   HS_OP_BLOCK_SCORE_BWD_STORE_DS = 6, /* larger workspace of hs_block_score_bwd
                                          that also holds the score gradients */
-  HS_OP_SWA_BWD_STORE_DS = 7    /* the same for hs_swa_bwd           */
+  HS_OP_SWA_BWD_STORE_DS = 7,   /* the same for hs_swa_bwd           */
+  HS_OP_SWA_SPARSE = 8          /* workspace of hs_swa_sparse_fwd    */
 } hs_op;
 
 typedef struct {
@@ -194,6 +195,24 @@ hs_status hs_sparse_gather_fwd(const hs_problem* p, const void* q, const void* k
 hs_status hs_swa_fwd(const hs_problem* p, const void* q, const void* kv, const float* sink,
                      int32_t window, void* out, float* lse, void* ws, size_t ws_bytes,
                      void* stream);
+
+/* Both attention branches of a sliding-window layer that reuses a full
+ * layer's shared latent KV and block selection (same page, Changes list: the
+ * full layer emits the shared KV and block indices, and the window kernel
+ * serves the sliding-window layer's main branch; per-file table row for
+ * transformer_layer.py: KV shared across layers). One call returns the two
+ * branch outputs separately, exactly as hs_swa_fwd (out_swa, lse_swa) and
+ * hs_sparse_gather_fwd (out_sparse, lse_sparse) would for the same
+ * arguments; how a layer combines them is not stated on the pages and is
+ * left to the caller. On the bf16 path with an in-place cache and no split
+ * of either branch's keys (every shape except single-token decode), one
+ * launch walks each row's window blocks and then its selected blocks,
+ * loading the row's queries once; otherwise the two operations run one
+ * after the other. Workspace: hs_workspace_size with HS_OP_SWA_SPARSE. */
+hs_status hs_swa_sparse_fwd(const hs_problem* p, const void* q, const void* kv, const float* sink,
+                            int32_t window, const int32_t* block_idx, int32_t top_k, void* out_swa,
+                            float* lse_swa, void* out_sparse, float* lse_sparse, void* ws,
+                            size_t ws_bytes, void* stream);
 
 /* Gradients (page "HySparse MQA sparse attention ...", section "Core": block
  * scoring trained through its autograd layer and the analytic gradient of

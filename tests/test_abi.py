@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(hs.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.hs_version() == 105
+    assert lib.hs_version() == 106
 
 
 def _mla(**kw):

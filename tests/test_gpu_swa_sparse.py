@@ -1,0 +1,108 @@
+"""GPU checks of hs_swa_sparse_fwd, both branches of a sliding-window layer
+over the shared latent KV and a full layer's block selection in one call.
+Its outputs must equal, bit for bit, those of hs_swa_fwd and
+hs_sparse_gather_fwd for the same arguments (the one-pass kernel runs the
+same per-tile arithmetic in the same order; decode and fp32 shapes run the
+two operations), and on one case match the float64 oracle directly."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_mqa_amd as hs
+from block_sparse_mqa_amd import inputs
+from oracle import hysparse_ref as ref
+
+from gpu_common import BF16_TOL, Dev, assert_close, np64, say
+from test_gpu_parity import MLA
+
+pytestmark = pytest.mark.gpu
+
+
+def _mla(name, S, seed, top_k, window, B=1, Sq=None, Skv=None, kv_lens=None, docs=None):
+    return inputs.make(B, Sq or S, Skv or S, MLA["H"], MLA["Dk"], MLA["Dv"], seed=seed,
+                       top_k=top_k, window=window, kv_lens=kv_lens, doc_lens=docs, name=name)
+
+
+CASES = {
+    "S130_tail": lambda: _mla("S130_tail", 130, 71, 2, 70),
+    "S300_docs": lambda: _mla("S300_docs", 300, 72, 3, 40, docs=[70, 1, 63, 100, 66]),
+    "chunked_prefill": lambda: _mla("chunked_prefill", 0, 73, 3, 100, B=2, Sq=70, Skv=200,
+                                    kv_lens=[200, 150]),
+    "S2048_window_past_start": lambda: _mla("S2048", 2048, 74, 8, 5000),
+    "decode_split": lambda: _mla("decode", 0, 75, 4, 256, B=3, Sq=1, Skv=3000,
+                                 kv_lens=[3000, 1200, 64]),
+    "tiny_f32": lambda: inputs.config(1),
+}
+
+
+def _both(d, p, idx):
+    ow, lw, og, lg = hs.swa_sparse(d.prob, d.q, d.kv, d.sink, p.window, idx, p.top_k)
+    sw = hs.swa(d.prob, d.q, d.kv, d.sink, p.window)
+    sg = hs.sparse_gather(d.prob, d.q, d.kv, d.sink, idx, p.top_k)
+    torch.cuda.synchronize()
+    return (ow, lw, og, lg), (*sw, *sg)
+
+
+def _equal(got, want, name):
+    for g, w, n in zip(got, want, ("out_swa", "lse_swa", "out_sparse", "lse_sparse")):
+        assert torch.equal(g, w), f"{name}: {n} differs from the separate call"
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_equals_separate_calls(name):
+    p = CASES[name]()
+    say(f"[gpu] swa+sparse {name}: B={p.B} Sq={p.Sq} Skv={p.Skv} dtype={p.dtype} "
+        f"top_k={p.top_k} window={p.window}")
+    d = Dev(p)
+    _, _, bl = hs.block_score(d.prob, d.q, d.kv, d.sink)
+    idx = hs.topk_blocks(d.prob, bl, p.top_k)
+    got, want = _both(d, p, idx)
+    _equal(got, want, name)
+    say(f"[gpu] swa+sparse {name}: identical to the separate calls")
+
+
+def test_rows_with_empty_sparse_branch():
+    """Rows whose selection holds no valid block (all -1, or ids past the
+    block count) get the sink-only sparse result, as from the gather call."""
+    p = _mla("empty_sparse", 200, 76, 3, 64)
+    d = Dev(p)
+    rng = np.random.default_rng(77)
+    nb = hs.hs_num_blocks(d.prob)
+    idx = rng.integers(0, nb, size=(1, p.Sq, p.top_k)).astype(np.int32)
+    idx[0, ::3] = -1
+    idx[0, 1::7] = nb + 5
+    idx = torch.from_numpy(idx).cuda()
+    got, want = _both(d, p, idx)
+    _equal(got, want, "empty sparse rows")
+    say("[gpu] swa+sparse with empty sparse rows: identical")
+
+
+def test_matches_oracle_docs():
+    """Against the float64 oracle directly: documents, a ragged tail."""
+    p = _mla("oracle_docs", 333, 78, 3, 90, docs=[100, 33, 200])
+    d = Dev(p)
+    _, _, bl = hs.block_score(d.prob, d.q, d.kv, d.sink)
+    idx = hs.topk_blocks(d.prob, bl, p.top_k)
+    ow, lw, og, lg = hs.swa_sparse(d.prob, d.q, d.kv, d.sink, p.window, idx, p.top_k)
+    torch.cuda.synchronize()
+    idx_np = idx.cpu().numpy()
+    os_ref, ls_ref = ref.swa(p.q, p.kv, d.sink_cpu, p.Dv, p.scale, p.window, **d.kw())
+    og_ref, lg_ref = ref.sparse_gather(p.q, p.kv, d.sink_cpu, p.Dv, p.scale, idx_np, **d.kw())
+    errs = [assert_close(np64(ow), os_ref, BF16_TOL, "swa out"),
+            assert_close(np64(lw), ls_ref, BF16_TOL, "swa lse"),
+            assert_close(np64(og), og_ref, BF16_TOL, "sparse out"),
+            assert_close(np64(lg), lg_ref, BF16_TOL, "sparse lse")]
+    say(f"[gpu] swa+sparse vs oracle: {max(errs):.2e} worst")
+
+
+def test_long_context_full_size():
+    """S = 32768, top-k 32, window 1024: the one-pass launch the benchmark
+    times, identical to the two separate calls."""
+    p = inputs.config(3)
+    say("[gpu] swa+sparse long context: inputs ready")
+    d = Dev(p)
+    _, _, bl = hs.block_score(d.prob, d.q, d.kv, d.sink)
+    idx = hs.topk_blocks(d.prob, bl, p.top_k)
+    got, want = _both(d, p, idx)
+    _equal(got, want, "long context")
+    say("[gpu] swa+sparse long context: identical")
