@@ -22,7 +22,7 @@ import torch
 
 from . import (HS_OP_SPARSE_GATHER_BWD, Problem, _workspace, block_score_topk,
                hs_block_score_bwd, hs_sparse_gather_bwd, hs_swa_bwd, score_bwd_workspace,
-               sparse_gather, swa, swa_bwd_workspace)
+               sparse_gather, swa, swa_bwd_workspace, swa_sparse)
 
 
 def _grads(prob, q, sink, need_sink):
@@ -104,6 +104,52 @@ class SlidingWindow(torch.autograd.Function):
         hs_swa_bwd(prob, q, kv, sink, ctx.window, out, lse, dout.contiguous(), dq, dkv, dsink,
                    swa_bwd_workspace(prob, ctx.window))
         return (*_finish(ctx, q, kv, sink, dq, dkv, dsink), None, None)
+
+
+class SlidingWindowLayer(torch.autograd.Function):
+    """(out_swa, lse_swa, out_sparse, lse_sparse): both branches of a
+    sliding-window layer over a full layer's KV and block selection
+    (hs_swa_sparse_fwd). The gradient is the sum of the two branches'
+    (hs_swa_bwd and hs_sparse_gather_bwd); a branch whose output receives no
+    gradient is skipped."""
+
+    @staticmethod
+    def forward(ctx, q, kv, sink, block_idx, prob: Problem, window: int, top_k: int):
+        ow, lw, og, lg = swa_sparse(prob, q, kv, sink, window, block_idx, top_k)
+        ctx.save_for_backward(q, kv, sink, block_idx, ow, lw, og, lg)
+        ctx.prob, ctx.window, ctx.top_k = prob, window, top_k
+        ctx.set_materialize_grads(False)
+        ctx.mark_non_differentiable(lw, lg)
+        return ow, lw, og, lg
+
+    @staticmethod
+    def backward(ctx, dout_swa, _dlw, dout_sparse, _dlg):
+        q, kv, sink, block_idx, ow, lw, og, lg = ctx.saved_tensors
+        prob = ctx.prob
+        total = None
+        for dout, run in (
+                (dout_swa, lambda g, d: hs_swa_bwd(
+                    prob, q, kv, sink, ctx.window, ow, lw, d, *g,
+                    swa_bwd_workspace(prob, ctx.window))),
+                (dout_sparse, lambda g, d: hs_sparse_gather_bwd(
+                    prob, q, kv, sink, block_idx, ctx.top_k, og, lg, d, *g,
+                    _workspace(prob, HS_OP_SPARSE_GATHER_BWD, top_k=ctx.top_k)))):
+            if dout is None:
+                continue
+            g = _grads(prob, q, sink, ctx.needs_input_grad[2])
+            run(g, dout.contiguous())
+            total = g if total is None else tuple(
+                None if a is None else a + b for a, b in zip(total, g))
+        if total is None:
+            return None, None, None, None, None, None, None
+        return (*_finish(ctx, q, kv, sink, *total), None, None, None, None)
+
+
+def sliding_window_layer(q, kv, sink: Optional[torch.Tensor], block_idx, prob: Problem,
+                         window: int, top_k: int):
+    """Both branches of a sliding-window layer: returns (out_swa, lse_swa,
+    out_sparse, lse_sparse); differentiable in q, kv and sink."""
+    return SlidingWindowLayer.apply(q, kv, sink, block_idx, prob, window, top_k)
 
 
 def block_score_attention(q, kv, sink: Optional[torch.Tensor], prob: Problem, top_k: int):

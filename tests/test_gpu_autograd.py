@@ -80,3 +80,32 @@ def test_autograd_gradients_accumulate_over_branches():
     assert torch.allclose(q.grad.float(), want_q, rtol=1e-2, atol=1e-3)
     assert torch.allclose(kv.grad.float(), want_kv, rtol=1e-2, atol=1e-3)
     say("[gpu] autograd gradients accumulate over branches")
+
+
+def test_sliding_window_layer_gradients():
+    """The layer function (both branches from one forward call) gives the
+    gradients of the two separate functions summed, in fp32 before rounding
+    to the inputs' dtype, and a branch left out of the loss costs no gradient
+    call of its own."""
+    p = inputs.make(1, 180, 180, MLA["H"], MLA["Dk"], MLA["Dv"], seed=85, top_k=3, window=50,
+                    name="layer_fn")
+    prob = hs.Problem(1, 180, 180, p.H, p.Dk, p.Dv, scale=p.scale)
+    q, kv, sink = _leaves(p)
+    with torch.no_grad():
+        _, _, _, idx = hsa.block_score_attention(q, kv, sink, prob, p.top_k)
+    d1 = inputs.make_dout(p, seed=86).cuda()
+    d2 = inputs.make_dout(p, seed=87).cuda()
+    ow, lw, og, lg = hsa.sliding_window_layer(q, kv, sink, idx, prob, p.window, p.top_k)
+    gq, gkv, gs = torch.autograd.grad((ow, og), (q, kv, sink), (d1, d2))
+    with torch.no_grad():
+        a = hs.swa_bwd(prob, q, kv, sink, p.window, ow, lw, d1)
+        b = hs.sparse_gather_bwd(prob, q, kv, sink, idx, p.top_k, og, lg, d2)
+    torch.cuda.synchronize()
+    assert torch.equal(gq, (a[0] + b[0]).to(q.dtype))
+    assert torch.equal(gkv, (a[1] + b[1]).to(kv.dtype))
+    assert torch.equal(gs, a[2] + b[2])
+    # only the window branch in the loss
+    ow, lw, og, lg = hsa.sliding_window_layer(q, kv, sink, idx, prob, p.window, p.top_k)
+    gq1, = torch.autograd.grad(ow, (q,), d1)
+    assert torch.equal(gq1, a[0].to(q.dtype))
+    say("[gpu] sliding-window layer function: gradients of both branches")
