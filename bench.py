@@ -74,41 +74,55 @@ def flops_per_pair(p) -> int:
     return 2 * p.Dk + 2 * p.Dv
 
 
-def blas_threads() -> int:
-    try:
-        from threadpoolctl import threadpool_info
-        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
-        if n:
-            return int(max(n))
-    except Exception:
-        pass
-    return os.cpu_count() or 1
+def roofline_entry(kernel, flops, compulsory_bytes, ms, traffic=None, **extra):
+    """Roofline of one kernel: t_roof = max(flops / MFMA peak, compulsory bytes /
+    HBM peak); `achieved` is the rate on the bounding resource over the
+    kernel's mean launch time (HIP events on its stream)."""
+    t_m = flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_h = compulsory_bytes / (PEAK_HBM_GBS * 1e9)
+    s = ms * 1e-3
+    if t_m >= t_h:
+        ach, peak, unit, bound = flops / s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma"
+    else:
+        ach, peak, unit, bound = compulsory_bytes / s / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
+    r = {"kernel": kernel, "bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+         "frac": round(ach / peak, 4), "traffic": traffic, "flop": flops,
+         "compulsory_bytes": int(compulsory_bytes), "ms": round(ms, 4)}
+    r.update(extra)
+    return r
 
 
-def cpu_baseline(p, budget_s: float, seed: int = 0):
-    """Time the oracle (block scores, top-k, gather) on uniformly drawn query
-    rows until `budget_s` of CPU time is spent; tokens/s = rows / seconds."""
-    from oracle import hysparse_ref as ref
+def cpu_baseline(p, budget_s: float, seed: int = 0, group: int = 4):
+    """Time the oracle (block scores, top-k, gather; float64) on a bounded
+    sample of query rows: groups of `group` consecutive rows at uniformly drawn
+    starts, computed by one thread per host core with one BLAS thread each
+    (oracle/parallel.py), until about `budget_s` seconds of wall time have
+    passed. tokens/s = rows / wall seconds."""
+    from oracle import parallel as par
     rng = np.random.default_rng(seed)
     kv64 = p.kv.to(torch.float64).numpy()
-    sink = p.sink
-    rows_done, spent = 0, 0.0
-    while spent < budget_s and rows_done < p.Sq:
-        r = int(rng.integers(0, p.Sq))
-        t0 = time.perf_counter()
-        _, _, bl = ref.block_score(p.q, kv64, sink, p.Dv, p.scale, block_size=p.block_size,
-                                   rows=[r])
-        own = ref.own_blocks(1, p.Sq, p.Skv, p.block_size, rows=[r])
-        idx_r = ref.topk_blocks(bl, own, p.top_k)
-        idx = np.full((1, p.Sq, p.top_k), -1, dtype=np.int64)
-        idx[0, r] = idx_r[0, 0]
-        ref.sparse_gather(p.q, kv64, sink, p.Dv, p.scale, idx, block_size=p.block_size, rows=[r])
-        spent += time.perf_counter() - t0
-        rows_done += 1
-    return {"value": rows_done / spent, "unit": "tokens/s", "cores": blas_threads(),
+    workers = par.default_workers()
+    starts = rng.integers(0, max(1, p.Sq - group + 1), size=4096)
+    kw = dict(block_size=p.block_size, kv_lens=p.kv_lens, doc_start=p.doc_start,
+              doc_end=p.doc_end)
+
+    def fn(rows):
+        return par.metric_path_rows(p.q, kv64, p.sink, p.Dv, p.scale, p.top_k, rows, **kw)[3]
+
+    done, t0 = 0, time.perf_counter()
+    batch = 2 * workers
+    for i in range(0, len(starts), batch):
+        rows = np.concatenate([np.arange(s0, s0 + group) for s0 in starts[i:i + batch]])
+        for c, _ in par.map_row_chunks(fn, rows, group, workers):
+            done += len(c)
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    spent = time.perf_counter() - t0
+    return {"value": round(done * p.B / spent, 3), "unit": "tokens/s", "cores": workers,
             "kind": "oracle",
-            "sample": f"{rows_done} query rows drawn uniformly from S={p.Sq} "
-                      f"(block scores + top-k + gather per row, float64), {spent:.1f} s"}
+            "sample": f"{done} query rows in groups of {group} consecutive rows at uniformly drawn "
+                      f"starts of S={p.Sq} (block scores + top-k + gather per row, float64), "
+                      f"{workers} threads x 1 BLAS thread, {spent:.1f} s wall"}
 
 
 def counter_traffic(path: str, workload: str, kernel: str):
@@ -238,50 +252,45 @@ def measure_peaks(dev, stream):
             "copy_probe": f"{nbytes >> 30} GiB read + {nbytes >> 30} GiB written, 16 B per lane, nontemporal"}
 
 
-def oracle_time(p, budget_s, seed=0, threads=None):
-    """Oracle (block scores, top-k, gather; float64) on the workload's rows:
-    all of them when they fit in `budget_s`, else a uniform sample, with the
-    full-run time extrapolated by causal pairs (labelled)."""
-    import contextlib
-    from oracle import hysparse_ref as ref
-    kw = dict(block_size=p.block_size, kv_lens=p.kv_lens, doc_start=p.doc_start, doc_end=p.doc_end)
-    limit = contextlib.nullcontext()
-    if threads is not None:
-        from threadpoolctl import threadpool_limits
-        limit = threadpool_limits(threads)
+def oracle_time(p, budget_s, seed=0, threads=None, group=4):
+    """Oracle (block scores, top-k, gather; float64) on the workload's rows,
+    run by `threads` worker threads (default: one per host core) with one BLAS
+    thread each: all rows when they fit in `budget_s`, else groups of `group`
+    consecutive rows at uniformly drawn starts, with the full-run time
+    extrapolated by causal pairs (labelled)."""
+    from oracle import parallel as par
     causal, _, _, _ = row_key_counts(p)
     per_row = causal.reshape(p.B, p.Sq).sum(axis=0)       # pairs per row index, all batch entries
     rng = np.random.default_rng(seed)
-    order = rng.permutation(p.Sq)
+    order = rng.permutation(np.arange(0, p.Sq, group))
     kv64 = p.kv.to(torch.float64).numpy()
-    done, spent, pairs = 0, 0.0, 0
-    last_note = 0.0
-    with limit:
-        for r in order:
-            if spent >= budget_s:
-                break
-            if spent - last_note >= 30.0:
-                last_note = spent
-                print(f"[oracle] {p.name}: {done}/{p.Sq} rows, {spent:.0f} s", file=sys.stderr,
-                      flush=True)
-            t0 = time.perf_counter()
-            rows = [int(r)]
-            _, _, bl = ref.block_score(p.q, kv64, p.sink, p.Dv, p.scale, rows=rows, **kw)
-            own = ref.own_blocks(p.B, p.Sq, p.Skv, p.block_size, p.kv_lens, p.doc_start, p.doc_end,
-                                 rows=rows)
-            sel = ref.topk_blocks(bl, own, p.top_k)
-            idx = np.full((p.B, p.Sq, p.top_k), -1, dtype=np.int64)
-            idx[:, r] = sel[:, 0]
-            ref.sparse_gather(p.q, kv64, p.sink, p.Dv, p.scale, idx, rows=rows, **kw)
-            spent += time.perf_counter() - t0
-            done += 1
-            pairs += int(per_row[r])
+    workers = threads or par.default_workers()
+    kw = dict(block_size=p.block_size, kv_lens=p.kv_lens, doc_start=p.doc_start, doc_end=p.doc_end)
+
+    def fn(rows):
+        return par.metric_path_rows(p.q, kv64, p.sink, p.Dv, p.scale, p.top_k, rows, **kw)[3]
+
+    done, pairs, t0, last_note = 0, 0, time.perf_counter(), 0.0
+    batch = 2 * workers
+    for i in range(0, len(order), batch):
+        rows = np.concatenate([np.arange(s0, min(p.Sq, s0 + group)) for s0 in order[i:i + batch]])
+        for c, _ in par.map_row_chunks(fn, rows, group, workers):
+            done += len(c)
+            pairs += int(per_row[c].sum())
+        spent = time.perf_counter() - t0
+        if spent - last_note >= 30.0:
+            last_note = spent
+            print(f"[oracle] {p.name}: {done}/{p.Sq} rows, {spent:.0f} s", file=sys.stderr,
+                  flush=True)
+        if spent >= budget_s:
+            break
+    spent = time.perf_counter() - t0
     full = done == p.Sq
     est_full_s = spent if full else spent * float(per_row.sum()) / max(pairs, 1)
     return {"tokens_s": round(done * p.B / spent, 3), "rows": done * p.B, "seconds": round(spent, 2),
             "full": full, "full_run_s": round(est_full_s, 1),
             "full_run_s_is": "measured" if full else "extrapolated by causal pairs from the sample",
-            "threads": threads if threads is not None else blas_threads()}
+            "threads": workers}
 
 
 def suite_config(c, dev, stream, peaks, oracle_budget):
@@ -329,8 +338,8 @@ def suite_config(c, dev, stream, peaks, oracle_budget):
     dq = torch.empty((p.B, p.Sq, p.H, p.Dk), dtype=torch.float32, device=dev)
     dkv = torch.empty((p.B, p.Skv, p.Dk), dtype=torch.float32, device=dev)
     dsink = torch.empty((p.H,), dtype=torch.float32, device=dev)
-    wb1, wb3, wb4 = hs.score_bwd_workspace(prob), ws(hs.HS_OP_SPARSE_GATHER_BWD, top_k=p.top_k), \
-        hs.swa_bwd_workspace(prob, p.window)
+    wb1, wb3, wb4 = hs.score_bwd_workspace(prob, store_ds=True), \
+        ws(hs.HS_OP_SPARSE_GATHER_BWD, top_k=p.top_k), hs.swa_bwd_workspace(prob, p.window, store_ds=True)
     calls["block_score_bwd"] = lambda: hs.hs_block_score_bwd(
         prob, q, kv, sink, *fwd["block_score"], dout, dq, dkv, dsink, wb1, stream)
     calls["sparse_gather_bwd"] = lambda: hs.hs_sparse_gather_bwd(
@@ -346,13 +355,16 @@ def suite_config(c, dev, stream, peaks, oracle_budget):
         "topk": (0, p.B * p.Sq * (NB + p.top_k) * 4),
         "score_topk_fused": (int(causal.sum()) * H * fpp,
                              qb + kv_rows["score"] * p.Dk * es + ob + lb + p.B * p.Sq * NB * 4),
+        # compulsory bytes: every KV row at most once (the per-token selected rows,
+        # reported separately, are served largely from L2 and the MALL)
         "sparse_gather": (int(gather.sum()) * H * fpp,
-                          qb + ob + lb + p.B * p.Sq * p.top_k * 4 + int(gather.sum()) * p.Dk * es),
+                          qb + ob + lb + p.B * p.Sq * p.top_k * 4 + kv_rows["score"] * p.Dk * es),
         "swa": (int(window.sum()) * H * fpp, qb + kv_rows["swa"] * p.Dk * es + ob + lb),
     }
     work["swa_sparse"] = (int(window.sum()) * H * fpp + int(gather.sum()) * H * fpp,
-                          qb + kv_rows["swa"] * p.Dk * es + 2 * (ob + lb) +
-                          p.B * p.Sq * p.top_k * 4 + int(gather.sum()) * p.Dk * es)
+                          qb + kv_rows["score"] * p.Dk * es + 2 * (ob + lb) +
+                          p.B * p.Sq * p.top_k * 4)
+    l2_served = {"sparse_gather": qb + ob + lb + int(gather.sum()) * p.Dk * es}
     # Gradients: five contractions per pair (S recomputed, dP, dQ, dK, dV), i.e.
     # 2 (3 Dk + 2 Dv) flops; bytes: q, kv rows, out, dout, lse, dq and dkv in fp32.
     fpb = 2 * (3 * p.Dk + 2 * p.Dv)
@@ -360,8 +372,7 @@ def suite_config(c, dev, stream, peaks, oracle_budget):
     work["block_score_bwd"] = (int(causal.sum()) * H * fpb,
                                gb + kv_rows["score"] * p.Dk * (es + 4))
     work["sparse_gather_bwd"] = (int(gather.sum()) * H * fpb,
-                                 gb + p.B * p.Sq * p.top_k * 4 + int(gather.sum()) * p.Dk * es +
-                                 kv_rows["score"] * p.Dk * 4)
+                                 gb + p.B * p.Sq * p.top_k * 4 + kv_rows["score"] * p.Dk * (es + 4))
     work["swa_bwd"] = (int(window.sum()) * H * fpb, gb + kv_rows["swa"] * p.Dk * (es + 4))
     peak_f = PEAK_BF16_TFLOPS if p.dtype == "bf16" else PEAK_F32_TFLOPS
     meas_f = peaks["mfma_bf16_tflop_s"] if p.dtype == "bf16" else None
@@ -384,6 +395,8 @@ def suite_config(c, dev, stream, peaks, oracle_budget):
                    "gb_s_alg": round(Bts / (warm * 1e-3) / 1e9, 1),
                    "frac_vendor": round(t_roof / warm, 4),
                    "frac_measured_peak": round(t_roof_m / warm, 4) if (meas_f or bound == "hbm") else None}
+        if k in l2_served:
+            rows[k]["gb_s_per_token_kv_l2_served"] = round(l2_served[k] / (warm * 1e-3) / 1e9, 1)
         print(f"[suite] workload {c} {k}: {rows[k]}", file=sys.stderr, flush=True)
     del scratch, dq, dkv, dout, fwd
     path_ms = rows["block_score"]["ms_warm"] + rows["topk"]["ms_warm"] + rows["sparse_gather"]["ms_warm"]
@@ -432,9 +445,11 @@ def write_suite_md(path, peaks, results, args):
          "MFMA, 157.3 TFLOP/s fp32 vector, 8000 GB/s HBM.\n",
          "Times are medians of 20 launches after 3 warm-ups (warm) and of 10 launches each after "
          "writing a 1 GiB buffer, which evicts the 256 MB MALL and the L2 (cold). f = t_roof / t_warm "
-         "with t_roof = max(flops / peak, algorithmic bytes / bandwidth); gather bytes count each "
-         "token's selected KV rows once (shared by its 64 heads), so f can exceed 1 when KV is "
-         "served from cache.\n",
+         "with t_roof = max(flops / peak, compulsory bytes / bandwidth); compulsory bytes read "
+         "every input and write every output once (the gather's KV rows at most once). The "
+         "gather's per-token selected KV rows (each token's rows once, shared by its 64 heads) "
+         "are served largely from L2 and the MALL; their rate is listed after the table, not "
+         "used as a bound.\n",
          "| Workload | Kernel | Warm ms | Cold ms | TFLOP | Alg. GB | Bound | TFLOP/s | GB/s (alg.) | f vendor | f measured peak |",
          "|---|---|---|---|---|---|---|---|---|---|---|"]
     for r in results:
@@ -445,6 +460,11 @@ def write_suite_md(path, peaks, results, args):
                      f"{v['tflop']:.3f} | {v['gb_alg']:.3f} | {v['bound']} | {ts} | {v['gb_s_alg']:.0f} | "
                      f"{v['frac_vendor']:.3f} | {fm} |")
     L.append("")
+    L.append("Gather, per-token selected KV rows (served largely from L2 and the MALL, not HBM "
+             "traffic): " + "; ".join(
+                 f"{r['workload']} {r['kernels']['sparse_gather']['gb_s_per_token_kv_l2_served']:.0f} GB/s"
+                 for r in results if "gb_s_per_token_kv_l2_served" in r["kernels"].get("sparse_gather", {}))
+             + ".\n")
     L.append("`*_bwd` are the gradient calls (dq, dkv and the sink gradient) of the three attention "
              "operations, each fed its own forward outputs; their flops are 2 (3 Dk + 2 Dv) per "
              "(query-head, key) pair (score recomputed, dP, dQ, dK, dV) and their bytes count q, the "
@@ -595,10 +615,10 @@ def main():
         dq = torch.empty((p.B, p.Sq, p.H, p.Dk), dtype=torch.float32, device=dev)
         dkv = torch.empty((p.B, p.Skv, p.Dk), dtype=torch.float32, device=dev)
         dsink = torch.empty((p.H,), dtype=torch.float32, device=dev)
-        wb1 = hs.score_bwd_workspace(prob)
+        wb1 = hs.score_bwd_workspace(prob, store_ds=True)
         stored = wb1.numel() * 4 >= hs.hs_workspace_size(prob, hs.HS_OP_BLOCK_SCORE_BWD_STORE_DS)
         wb3 = ws_for(hs.HS_OP_SPARSE_GATHER_BWD, top_k=p.top_k)
-        wb4 = hs.swa_bwd_workspace(prob, p.window)
+        wb4 = hs.swa_bwd_workspace(prob, p.window, store_ds=True)
         stored4 = wb4.numel() * 4 >= hs.hs_workspace_size(prob, hs.HS_OP_SWA_BWD_STORE_DS,
                                                           window=p.window)
         gcalls = {
@@ -640,9 +660,34 @@ def main():
     tokens = p.B * p.Sq
     tok_s = tokens / (ms_per_step * 1e-3)
     tflops = ((f_score + (f_gather or 0)) / (ms_per_step * 1e-3) / 1e12)
-    achieved = f_score / (k_ms[0] * 1e-3) / 1e12
 
-    traffic = counter_traffic(args.traffic_json, p.name, "block_score")
+    # Compulsory HBM bytes (each input read once, each output written once).
+    es = 2 if p.dtype == "bf16" else 4
+    qb = tokens * p.H * p.Dk * es
+    ob = tokens * p.H * p.Dv * es
+    lb = tokens * p.H * 4
+    kvb = p.B * p.Skv * p.Dk * es
+    c_score = qb + kvb + ob + lb + tokens * NB * 4
+    c_topk = tokens * (NB + p.top_k) * 4
+    c_gather = qb + kvb + ob + lb + tokens * p.top_k * 4
+    c_swa = qb + kvb + ob + lb
+    tr = lambda k: counter_traffic(args.traffic_json, p.name, k)
+    rooflines = {
+        "block_score": roofline_entry("block_score (hs_block_score_fwd)", f_score, c_score,
+                                      float(k_ms[0]), tr("block_score")),
+        "topk": roofline_entry("topk (hs_topk_blocks)", 0, c_topk, float(k_ms[1]), tr("topk")),
+    }
+    if f_gather:
+        # Per-token selected KV rows, each token's gather counted once (shared by its
+        # heads): bytes the method moves per token, served largely from L2 and the
+        # MALL (the whole KV is 37.7 MB), so they are reported, not used as the bound.
+        l2 = gather_pairs_from_idx(p, idx_cpu) // p.H * p.Dk * es + qb + ob + lb
+        rooflines["sparse_gather"] = roofline_entry(
+            "sparse_gather (hs_sparse_gather_fwd)", f_gather, c_gather, float(k_ms[2]),
+            tr("sparse_gather"), per_token_kv_bytes_l2_served=int(l2),
+            per_token_kv_rate_gb_s=round(l2 / (k_ms[2] * 1e-3) / 1e9, 1))
+    if f_swa:
+        rooflines["swa"] = roofline_entry("swa (hs_swa_fwd)", f_swa, c_swa, swa_ms, tr("swa"))
 
     res = {
         "metric": METRIC,
@@ -668,9 +713,9 @@ def main():
             "sparse_gather": round(f_gather / (k_ms[2] * 1e-3) / 1e12, 2) if f_gather else None,
             "swa": round(f_swa / (swa_ms * 1e-3) / 1e12, 2) if f_swa else None},
         "wall_s_timed": round(wall, 3),
-        "roofline": {"kernel": "block_score (hs_block_score_fwd)", "bound": "mfma",
-                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+        "roofline": {k: v for k, v in rooflines["block_score"].items()
+                     if k in ("kernel", "bound", "achieved", "peak", "unit", "frac", "traffic")},
+        "rooflines": rooflines,
     }
     if grads is not None:
         # 2 (3 Dk + 2 Dv) flops per pair: score recomputed, dP, dQ, dK, dV.

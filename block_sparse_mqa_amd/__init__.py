@@ -124,13 +124,16 @@ class Problem:
         then the capacity). Both tensors must outlive the calls."""
         self.B, self.Sq, self.Skv, self.H, self.Dk, self.Dv = B, Sq, Skv, H, Dk, Dv
         self.page_table = page_table
-        if page_table is not None:
-            _dev("page_table", page_table)
-            if page_table.dim() != 2 or page_table.shape[0] != B:
+        self.block_size = block_size
+        if page_table is not None or kv_lens_device is not None:
+            import torch
+            if page_table is not None and (page_table.dim() != 2 or page_table.shape[0] != B):
                 raise ValueError("page_table must be [B, max_pages]")
+            _meta("page_table", page_table, torch.int32)
+            _meta("kv_lens_device", kv_lens_device, torch.int32, (B,))
+            _dev("page_table", page_table)
+            _dev("kv_lens_device", kv_lens_device)
         self.kv_lens_device = kv_lens_device
-        if kv_lens_device is not None:
-            _dev("kv_lens_device", kv_lens_device, shape=(B,))
         self.dtype = dtype
         self._kv = (ctypes.c_int32 * len(kv_lens))(*kv_lens) if kv_lens is not None else None
         self._ds = (ctypes.c_int32 * len(doc_start))(*doc_start) if doc_start is not None else None
@@ -164,17 +167,73 @@ def _stream(stream) -> Optional[int]:
     return int(torch.cuda.current_stream().cuda_stream)
 
 
-def _dev(name, t, dtype=None, shape=None):
+def _meta(name, t, dtype=None, shape=None):
+    """Reject a tensor of the wrong dtype or shape (the C ABI sees only a
+    pointer and cannot check either)."""
     if t is None:
         return
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _dev(name, t, dtype=None, shape=None):
+    """_meta, then reject host memory and non-contiguous layouts."""
+    if t is None:
+        return
+    _meta(name, t, dtype, shape)
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def _tdt(prob):
+    import torch
+    return torch.bfloat16 if prob.dtype == "bf16" else torch.float32
+
+
+def _check_io(prob, **tensors):
+    """Dtype and shape of every tensor argument by its role (include/hs.h), all
+    of them first; then that each is contiguous device memory."""
+    import torch
+    B, Sq, Skv, H, Dk, Dv = prob.B, prob.Sq, prob.Skv, prob.H, prob.Dk, prob.Dv
+    f32, i32, dt = torch.float32, torch.int32, _tdt(prob)
+    k = tensors.pop("_top_k", None)
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if name == "q":
+            _meta(name, t, dt, (B, Sq, H, Dk))
+        elif name == "kv":
+            _meta(name, t, dt)
+            if prob.page_table is not None:
+                if t.dim() != 3 or tuple(t.shape[1:]) != (prob.block_size, Dk):
+                    raise ValueError(f"paged kv must be [n_pages, {prob.block_size}, {Dk}], "
+                                     f"got {tuple(t.shape)}")
+            else:
+                _meta(name, t, dt, (B, Skv, Dk))
+        elif name in ("sink", "dsink"):
+            _meta(name, t, f32, (H,))
+        elif name in ("gate_swa", "gate_sparse"):
+            _meta(name, t, f32, (B, Sq, H))
+        elif name in ("out", "dout", "out_swa", "out_sparse", "out_mix"):
+            _meta(name, t, dt, (B, Sq, H, Dv))
+        elif name in ("lse", "lse_swa", "lse_sparse"):
+            _meta(name, t, f32, (B, Sq, H))
+        elif name in ("block_logit", "block_prob"):
+            _meta(name, t, f32, (B, Sq, hs_num_blocks(prob)))
+        elif name == "block_idx":
+            _meta(name, t, i32, (B, Sq, k) if k is not None else None)
+        elif name == "dq":
+            _meta(name, t, f32, (B, Sq, H, Dk))
+        elif name == "dkv":
+            _meta(name, t, f32, (B, Skv, Dk))
+        elif name != "ws":  # pragma: no cover - a caller passed an unknown role
+            raise AssertionError(name)
+    for name, t in tensors.items():
+        _dev(name, t)
 
 
 # ---------------------------------------------------------------------------
@@ -194,26 +253,22 @@ def hs_workspace_size(prob: Problem, op: int, top_k: int = 0, window: int = 0) -
 
 
 def hs_block_score_fwd(prob, q, kv, sink, out, lse, block_logit, ws=None, stream=None):
-    for n, t in (("q", q), ("kv", kv), ("sink", sink), ("out", out), ("lse", lse),
-                 ("block_logit", block_logit), ("ws", ws)):
-        _dev(n, t)
+    _check_io(prob, q=q, kv=kv, sink=sink, out=out, lse=lse, block_logit=block_logit, ws=ws)
     _check(load_library().hs_block_score_fwd(
         prob.ref, _ptr(q), _ptr(kv), _ptr(sink), _ptr(out), _ptr(lse), _ptr(block_logit),
         _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def hs_topk_blocks(prob, block_logit, top_k, block_idx, stream=None):
-    _dev("block_logit", block_logit)
-    _dev("block_idx", block_idx)
+    _check_io(prob, block_logit=block_logit, block_idx=block_idx, _top_k=int(top_k))
     _check(load_library().hs_topk_blocks(prob.ref, _ptr(block_logit), int(top_k),
                                          _ptr(block_idx), _stream(stream)))
 
 
 def hs_block_score_topk_fwd(prob, q, kv, sink, top_k, out, lse, block_logit, block_idx, ws=None,
                             stream=None):
-    for n, t in (("q", q), ("kv", kv), ("sink", sink), ("out", out), ("lse", lse),
-                 ("block_logit", block_logit), ("block_idx", block_idx), ("ws", ws)):
-        _dev(n, t)
+    _check_io(prob, q=q, kv=kv, sink=sink, out=out, lse=lse, block_logit=block_logit,
+              block_idx=block_idx, ws=ws, _top_k=int(top_k))
     _check(load_library().hs_block_score_topk_fwd(
         prob.ref, _ptr(q), _ptr(kv), _ptr(sink), int(top_k), _ptr(out), _ptr(lse),
         _ptr(block_logit), _ptr(block_idx), _ptr(ws),
@@ -221,9 +276,8 @@ def hs_block_score_topk_fwd(prob, q, kv, sink, top_k, out, lse, block_logit, blo
 
 
 def hs_sparse_gather_fwd(prob, q, kv, sink, block_idx, top_k, out, lse, ws=None, stream=None):
-    for n, t in (("q", q), ("kv", kv), ("sink", sink), ("block_idx", block_idx), ("out", out),
-                 ("lse", lse), ("ws", ws)):
-        _dev(n, t)
+    _check_io(prob, q=q, kv=kv, sink=sink, block_idx=block_idx, out=out, lse=lse, ws=ws,
+              _top_k=int(top_k))
     _check(load_library().hs_sparse_gather_fwd(
         prob.ref, _ptr(q), _ptr(kv), _ptr(sink), _ptr(block_idx), int(top_k), _ptr(out),
         _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
@@ -231,8 +285,7 @@ def hs_sparse_gather_fwd(prob, q, kv, sink, block_idx, top_k, out, lse, ws=None,
 
 
 def hs_swa_fwd(prob, q, kv, sink, window, out, lse, ws=None, stream=None):
-    for n, t in (("q", q), ("kv", kv), ("sink", sink), ("out", out), ("lse", lse), ("ws", ws)):
-        _dev(n, t)
+    _check_io(prob, q=q, kv=kv, sink=sink, out=out, lse=lse, ws=ws)
     _check(load_library().hs_swa_fwd(
         prob.ref, _ptr(q), _ptr(kv), _ptr(sink), int(window), _ptr(out), _ptr(lse), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
@@ -240,10 +293,8 @@ def hs_swa_fwd(prob, q, kv, sink, window, out, lse, ws=None, stream=None):
 
 def hs_swa_sparse_fwd(prob, q, kv, sink, window, block_idx, top_k, out_swa, lse_swa, out_sparse,
                       lse_sparse, ws=None, stream=None):
-    for n, t in (("q", q), ("kv", kv), ("sink", sink), ("block_idx", block_idx),
-                 ("out_swa", out_swa), ("lse_swa", lse_swa), ("out_sparse", out_sparse),
-                 ("lse_sparse", lse_sparse), ("ws", ws)):
-        _dev(n, t)
+    _check_io(prob, q=q, kv=kv, sink=sink, block_idx=block_idx, out_swa=out_swa, lse_swa=lse_swa,
+              out_sparse=out_sparse, lse_sparse=lse_sparse, ws=ws, _top_k=int(top_k))
     _check(load_library().hs_swa_sparse_fwd(
         prob.ref, _ptr(q), _ptr(kv), _ptr(sink), int(window), _ptr(block_idx), int(top_k),
         _ptr(out_swa), _ptr(lse_swa), _ptr(out_sparse), _ptr(lse_sparse), _ptr(ws),
@@ -255,9 +306,8 @@ def _nbytes(ws) -> int:
 
 
 def hs_block_score_bwd(prob, q, kv, sink, out, lse, dout, dq, dkv, dsink, ws, stream=None):
-    for n, t in (("q", q), ("kv", kv), ("sink", sink), ("out", out), ("lse", lse),
-                 ("dout", dout), ("dq", dq), ("dkv", dkv), ("dsink", dsink), ("ws", ws)):
-        _dev(n, t)
+    _check_io(prob, q=q, kv=kv, sink=sink, out=out, lse=lse, dout=dout, dq=dq, dkv=dkv,
+              dsink=dsink, ws=ws)
     _check(load_library().hs_block_score_bwd(
         prob.ref, _ptr(q), _ptr(kv), _ptr(sink), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
         _ptr(dkv), _ptr(dsink), _ptr(ws), _nbytes(ws), _stream(stream)))
@@ -265,10 +315,8 @@ def hs_block_score_bwd(prob, q, kv, sink, out, lse, dout, dq, dkv, dsink, ws, st
 
 def hs_sparse_gather_bwd(prob, q, kv, sink, block_idx, top_k, out, lse, dout, dq, dkv, dsink,
                          ws, stream=None):
-    for n, t in (("q", q), ("kv", kv), ("sink", sink), ("block_idx", block_idx), ("out", out),
-                 ("lse", lse), ("dout", dout), ("dq", dq), ("dkv", dkv), ("dsink", dsink),
-                 ("ws", ws)):
-        _dev(n, t)
+    _check_io(prob, q=q, kv=kv, sink=sink, block_idx=block_idx, out=out, lse=lse, dout=dout,
+              dq=dq, dkv=dkv, dsink=dsink, ws=ws, _top_k=int(top_k))
     _check(load_library().hs_sparse_gather_bwd(
         prob.ref, _ptr(q), _ptr(kv), _ptr(sink), _ptr(block_idx), int(top_k), _ptr(out),
         _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dkv), _ptr(dsink), _ptr(ws), _nbytes(ws),
@@ -276,9 +324,8 @@ def hs_sparse_gather_bwd(prob, q, kv, sink, block_idx, top_k, out, lse, dout, dq
 
 
 def hs_swa_bwd(prob, q, kv, sink, window, out, lse, dout, dq, dkv, dsink, ws, stream=None):
-    for n, t in (("q", q), ("kv", kv), ("sink", sink), ("out", out), ("lse", lse),
-                 ("dout", dout), ("dq", dq), ("dkv", dkv), ("dsink", dsink), ("ws", ws)):
-        _dev(n, t)
+    _check_io(prob, q=q, kv=kv, sink=sink, out=out, lse=lse, dout=dout, dq=dq, dkv=dkv,
+              dsink=dsink, ws=ws)
     _check(load_library().hs_swa_bwd(
         prob.ref, _ptr(q), _ptr(kv), _ptr(sink), int(window), _ptr(out), _ptr(lse), _ptr(dout),
         _ptr(dq), _ptr(dkv), _ptr(dsink), _ptr(ws), _nbytes(ws), _stream(stream)))
@@ -368,28 +415,25 @@ def _grad_buffers(prob, q, sink):
 
 
 def _stored_ds_workspace(prob, small, large, store_ds, window=0):
-    import torch
-    if store_ds is None:
-        n = hs_workspace_size(prob, large, window=window)
-        store_ds = n <= torch.cuda.mem_get_info()[0] // 2
     return _workspace(prob, large if store_ds else small, window=window)
 
 
-def score_bwd_workspace(prob, store_ds=None):
-    """Workspace of hs_block_score_bwd. store_ds True: the larger one, in
-    which the key-block pass stores the score gradients for dq; False: the
-    smaller one (dq recomputes them); None: the larger one when it fits in
-    half of the free device memory."""
+def score_bwd_workspace(prob, store_ds=False):
+    """Workspace of hs_block_score_bwd. store_ds True (opt-in): the larger one,
+    in which the key-block pass stores the score gradients for dq (8 KB per
+    causal (row, key block) pair: 69 GB for one 32768-token sequence);
+    False: the smaller one, and dq recomputes them."""
     return _stored_ds_workspace(prob, HS_OP_BLOCK_SCORE_BWD, HS_OP_BLOCK_SCORE_BWD_STORE_DS,
                                 store_ds)
 
 
-def swa_bwd_workspace(prob, window, store_ds=None):
-    """Workspace of hs_swa_bwd, chosen as for score_bwd_workspace."""
+def swa_bwd_workspace(prob, window, store_ds=False):
+    """Workspace of hs_swa_bwd, chosen as for score_bwd_workspace (the
+    stored form is 8 KB per row and per block a window can meet)."""
     return _stored_ds_workspace(prob, HS_OP_SWA_BWD, HS_OP_SWA_BWD_STORE_DS, store_ds, window)
 
 
-def block_score_bwd(prob, q, kv, sink, out, lse, dout, stream=None, store_ds=None):
+def block_score_bwd(prob, q, kv, sink, out, lse, dout, stream=None, store_ds=False):
     """Gradients (dq, dkv, dsink) of the causal attention of block_score;
     dsink is None without a sink. All float32. store_ds picks the workspace
     (score_bwd_workspace)."""
@@ -407,7 +451,7 @@ def sparse_gather_bwd(prob, q, kv, sink, block_idx, top_k, out, lse, dout, strea
     return dq, dkv, dsink
 
 
-def swa_bwd(prob, q, kv, sink, window, out, lse, dout, stream=None, store_ds=None):
+def swa_bwd(prob, q, kv, sink, window, out, lse, dout, stream=None, store_ds=False):
     """Gradients (dq, dkv, dsink) of swa. store_ds picks the workspace
     (swa_bwd_workspace)."""
     dq, dkv, dsink = _grad_buffers(prob, q, sink)

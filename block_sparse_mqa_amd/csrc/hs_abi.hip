@@ -423,7 +423,8 @@ hs_status hs_workspace_size(const hs_problem* p, int32_t op, int32_t top_k, int3
   if (op == HS_OP_SWA_SPARSE) {
     // the two branches run one after the other when they do not run as one
     // pass, so the larger of their workspaces serves both
-    if (top_k < 1 || top_k > 64) return fail(HS_ERR_INVALID_ARG, "top_k must be in 1..64 (got %d)", top_k);
+    if (top_k < 1) return fail(HS_ERR_INVALID_ARG, "top_k must be >= 1 (got %d)", top_k);
+    if (top_k > 64) return fail(HS_ERR_UNSUPPORTED, "top_k %d exceeds 64", top_k);
     if (window < 1) return fail(HS_ERR_INVALID_ARG, "window must be >= 1 (got %d)", window);
     *bytes = p->dtype == HS_BF16
                  ? std::max(split_ws_bytes(g, plan_split(g, HS_OP_SWA, top_k, window).nsplit),
@@ -435,8 +436,10 @@ hs_status hs_workspace_size(const hs_problem* p, int32_t op, int32_t top_k, int3
     const int kop = (op == HS_OP_SWA_BWD || op == HS_OP_SWA_BWD_STORE_DS) ? hs::kSwa
                     : op == HS_OP_SPARSE_GATHER_BWD                       ? hs::kGather
                                                                           : hs::kScore;
-    if (kop == hs::kGather && (top_k < 1 || top_k > 64))
-      return fail(HS_ERR_INVALID_ARG, "top_k must be in 1..64 (got %d)", top_k);
+    if (kop == hs::kGather && top_k < 1)
+      return fail(HS_ERR_INVALID_ARG, "top_k must be >= 1 (got %d)", top_k);
+    if (kop == hs::kGather && top_k > 64)
+      return fail(HS_ERR_UNSUPPORTED, "top_k %d exceeds 64", top_k);
     if (kop == hs::kSwa && window < 1)
       return fail(HS_ERR_INVALID_ARG, "window must be >= 1 (got %d)", window);
     const bool store = (op == HS_OP_BLOCK_SCORE_BWD_STORE_DS || op == HS_OP_SWA_BWD_STORE_DS) &&

@@ -204,11 +204,14 @@ hs_status hs_swa_fwd(const hs_problem* p, const void* q, const void* kv, const f
  * branch outputs separately, exactly as hs_swa_fwd (out_swa, lse_swa) and
  * hs_sparse_gather_fwd (out_sparse, lse_sparse) would for the same
  * arguments; how a layer combines them is not stated on the pages and is
- * left to the caller. On the bf16 path with an in-place cache and no split
- * of either branch's keys (every shape except single-token decode), one
- * launch walks each row's window blocks and then its selected blocks,
+ * left to the caller. On the bf16 path with an in-place cache, whenever
+ * neither branch splits its key range across workgroups (few rows with long
+ * ranges do, e.g. single-token decode or a short chunk over a long cache),
+ * one launch walks each row's window blocks and then its selected blocks,
  * loading the row's queries once; otherwise the two operations run one
- * after the other. Workspace: hs_workspace_size with HS_OP_SWA_SPARSE. */
+ * after the other. top_k < 1 and window < 1 are HS_ERR_INVALID_ARG, top_k >
+ * 64 is HS_ERR_UNSUPPORTED (as for hs_sparse_gather_fwd). Workspace:
+ * hs_workspace_size with HS_OP_SWA_SPARSE. */
 hs_status hs_swa_sparse_fwd(const hs_problem* p, const void* q, const void* kv, const float* sink,
                             int32_t window, const int32_t* block_idx, int32_t top_k, void* out_swa,
                             float* lse_swa, void* out_sparse, float* lse_sparse, void* ws,

@@ -72,8 +72,10 @@ def assert_close(got, want, tol, name):
 
 def check_topk_margin(idx_gpu, bl_oracle, own, K):
     """Index parity under the margin rule: exact where the oracle's k-th gap
-    exceeds MARGIN, otherwise a valid choice among near-ties. Returns the share
-    of rows checked exactly."""
+    exceeds MARGIN; otherwise a valid choice among near-ties: the own block,
+    K distinct ascending entries, none more than MARGIN below the cut (the
+    oracle's last selected value) and every block more than MARGIN above the
+    cut present. Returns the share of rows checked exactly."""
     idx_gpu = np.asarray(idx_gpu)
     rows = idx_gpu.reshape(-1, K)
     blf = bl_oracle.reshape(rows.shape[0], -1)
@@ -99,10 +101,13 @@ def check_topk_margin(idx_gpu, bl_oracle, own, K):
             assert np.all(got >= 0) and len(set(got.tolist())) == K and np.all(np.diff(got) > 0)
             if o in C:
                 assert o in got
-            thr = vals[kk - 1] - MARGIN
+            cut = vals[kk - 1]
             for j in got:
                 if j != o:
-                    assert blf[i, j] >= thr, (i, j, blf[i, j], thr)
+                    assert blf[i, j] >= cut - MARGIN, (i, j, blf[i, j], cut)
+            # every block clearly above the cut must be selected
+            clear = others[blf[i, others] > cut + MARGIN]
+            assert np.isin(clear, got).all(), (i, clear, got, cut)
     return exact / max(1, rows.shape[0])
 
 

@@ -340,3 +340,85 @@ def test_stored_window_gradient_workspace(B, Sq, Skv, window, kv_lens, per_row):
             pos = L - Sq + r
             lo = max(pos - window + 1, 0)
             assert pos // 64 - lo // 64 + 1 <= per_row
+
+
+def test_binding_rejects_wrong_dtype_and_shape():
+    """The C ABI sees pointers only; the binding checks every tensor's dtype
+    and shape by its role before the call (the checks run before the device
+    check, so host tensors exercise them here)."""
+    import torch
+    p = _mla(Sq=128, Skv=128)
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    q = torch.zeros(1, 128, 64, 576, dtype=bf)
+    kv = torch.zeros(1, 128, 576, dtype=bf)
+    out = torch.zeros(1, 128, 64, 512, dtype=bf)
+    lse = torch.zeros(1, 128, 64, dtype=f32)
+    bl = torch.zeros(1, 128, 2, dtype=f32)
+    idx = torch.zeros(1, 128, 4, dtype=i32)
+    sink = torch.zeros(64, dtype=f32)
+    cases = [
+        (dict(sink=sink.to(bf)), "sink"),                                   # bf16 sink
+        (dict(sink=torch.zeros(32, dtype=f32)), "sink"),                    # wrong head count
+        (dict(q=q.to(f32)), "q"),                                           # fp32 q for bf16
+        (dict(q=q[:, :64]), "q"),                                           # short q
+        (dict(kv=kv[:, :, :512]), "kv"),                                    # kv without rope
+        (dict(lse=lse.to(torch.float64)), "lse"),
+        (dict(out=out[..., :256]), "out"),
+        (dict(block_logit=torch.zeros(1, 128, 3, dtype=f32)), "block_logit"),  # NB is 2
+    ]
+    for over, name in cases:
+        a = dict(q=q, kv=kv, sink=sink, out=out, lse=lse, block_logit=bl)
+        a.update(over)
+        with pytest.raises(ValueError, match=name):
+            hs.hs_block_score_fwd(p, a["q"], a["kv"], a["sink"], a["out"], a["lse"],
+                                  a["block_logit"])
+    # int64 selections (what torch.topk returns) and the wrong width
+    for bad in (idx.to(torch.int64), torch.zeros(1, 128, 5, dtype=i32)):
+        with pytest.raises(ValueError, match="block_idx"):
+            hs.hs_sparse_gather_fwd(p, q, kv, sink, bad, 4, out, lse)
+        with pytest.raises(ValueError, match="block_idx"):
+            hs.hs_topk_blocks(p, bl, 4, bad)
+    with pytest.raises(ValueError, match="dq"):
+        hs.hs_block_score_bwd(p, q, kv, sink, out, lse, out, q, kv.to(f32), None, None)
+    with pytest.raises(ValueError, match="page_table"):
+        hs.Problem(1, 1, 640, 64, 576, 512, page_table=torch.zeros(1, 10, dtype=torch.int64))
+    with pytest.raises(ValueError, match="kv_lens_device"):
+        hs.Problem(2, 1, 640, 64, 576, 512, page_table=torch.zeros(2, 10, dtype=i32),
+                   kv_lens_device=torch.zeros(2, dtype=torch.int64))
+    # paged pools are [n_pages, 64, Dk] (the role check reads prob.page_table;
+    # a host table stands in for the device one here)
+    pp = hs.Problem(1, 1, 640, 64, 576, 512)
+    pp.page_table = torch.zeros(1, 10, dtype=i32)
+    with pytest.raises(ValueError, match="paged kv"):
+        hs.hs_block_score_fwd(pp, q[:, :1], torch.zeros(10, 32, 576, dtype=bf), sink,
+                              out[:, :1], lse[:, :1], torch.zeros(1, 1, 10, dtype=f32))
+
+
+def test_window_and_sparse_call_rejects_before_launch():
+    """Host validation of hs_swa_sparse_fwd and its workspace query: NULL
+    outputs, top_k and window ranges (top_k > 64 is unsupported, as for the
+    gather), checked before any launch."""
+    lib = hs.load_library()
+    p = _mla()
+    f = ctypes.c_void_p(4096)
+
+    def call(top_k=4, window=16, out_swa=f, lse_swa=f, out_sparse=f, lse_sparse=f, idx=f):
+        return lib.hs_swa_sparse_fwd(p.ref, f, f, None, window, idx, top_k, out_swa, lse_swa,
+                                     out_sparse, lse_sparse, None, 0, None)
+    assert call(out_swa=None) == hs.HS_ERR_INVALID_ARG and b"out_swa" in lib.hs_last_error()
+    assert call(lse_sparse=None) == hs.HS_ERR_INVALID_ARG and b"lse_sparse" in lib.hs_last_error()
+    assert call(idx=None) == hs.HS_ERR_INVALID_ARG and b"block_idx" in lib.hs_last_error()
+    assert call(top_k=0) == hs.HS_ERR_INVALID_ARG
+    assert call(top_k=65) == hs.HS_ERR_UNSUPPORTED
+    assert call(window=0) == hs.HS_ERR_INVALID_ARG and b"window" in lib.hs_last_error()
+    n = ctypes.c_size_t(0)
+    ws = lambda k, w: lib.hs_workspace_size(p.ref, hs.HS_OP_SWA_SPARSE, k, w, ctypes.byref(n))
+    assert ws(4, 16) == hs.HS_OK and n.value == 0
+    assert ws(0, 16) == hs.HS_ERR_INVALID_ARG
+    assert ws(65, 16) == hs.HS_ERR_UNSUPPORTED
+    assert ws(4, 0) == hs.HS_ERR_INVALID_ARG
+    assert lib.hs_workspace_size(p.ref, hs.HS_OP_SPARSE_GATHER_BWD, 65, 0,
+                                 ctypes.byref(n)) == hs.HS_ERR_UNSUPPORTED
+    # a decode shape that splits both branches needs the workspace
+    d = _mla(B=2, Sq=1, Skv=65536, kv_lens=[65536, 30000])
+    assert hs.hs_workspace_size(d, hs.HS_OP_SWA_SPARSE, top_k=32, window=1024) > 0

@@ -141,3 +141,35 @@ def test_paged_device_lengths_and_graph_replay():
              "swa_out": assert_close(np64(osw), os_, tol, f"replay {rep} swa out"),
              "swa_lse": assert_close(np64(lsw), ls, tol, f"replay {rep} swa lse")}
         say(f"[gpu] graph replay {rep} lengths {min(lens)}..{max(lens)}: {e}")
+
+
+def test_paged_window_and_sparse_call():
+    """hs_swa_sparse_fwd on a paged pool runs the two operations one after the
+    other; both outputs must equal the separate paged calls bit for bit and
+    the oracle on the contiguous cache."""
+    lens = [700, 333, 1100]
+    p = inputs.make(3, 200, 1100, MLA["H"], MLA["Dk"], MLA["Dv"], seed=44, kv_lens=lens,
+                    top_k=4, window=150, name="paged_swa_sparse")
+    say("[gpu] paged KV window-and-sparse call")
+    pool, pt = _paged(p, seed=45)
+    pool, pt = pool.cuda(), pt.cuda()
+    q, sink = p.q.cuda(), p.sink.cuda()
+    prob = hs.Problem(p.B, p.Sq, p.Skv, p.H, p.Dk, p.Dv, kv_lens=p.kv_lens, page_table=pt)
+    _, _, bl = hs.block_score(prob, q, pool, sink)
+    idx = hs.topk_blocks(prob, bl, p.top_k)
+    ow, lw, og, lg = hs.swa_sparse(prob, q, pool, sink, p.window, idx, p.top_k)
+    sw = hs.swa(prob, q, pool, sink, p.window)
+    sg = hs.sparse_gather(prob, q, pool, sink, idx, p.top_k)
+    torch.cuda.synchronize()
+    for g, w, n in zip((ow, lw, og, lg), (*sw, *sg), ("out_swa", "lse_swa", "out_sparse",
+                                                      "lse_sparse")):
+        assert torch.equal(g, w), n
+    kw = dict(block_size=p.block_size, kv_lens=p.kv_lens)
+    idx_np = idx.cpu().numpy()
+    os_ref, ls_ref = ref.swa(p.q, p.kv, p.sink, p.Dv, p.scale, p.window, **kw)
+    og_ref, lg_ref = ref.sparse_gather(p.q, p.kv, p.sink, p.Dv, p.scale, idx_np, **kw)
+    tol = tol_for(p)
+    e = [assert_close(np64(ow), os_ref, tol, "swa out"), assert_close(np64(lw), ls_ref, tol, "swa lse"),
+         assert_close(np64(og), og_ref, tol, "sparse out"),
+         assert_close(np64(lg), lg_ref, tol, "sparse lse")]
+    say(f"[gpu] paged window-and-sparse: identical to the separate calls, oracle {max(e):.2e}")

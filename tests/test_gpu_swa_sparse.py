@@ -63,18 +63,23 @@ def test_equals_separate_calls(name):
 
 def test_rows_with_empty_sparse_branch():
     """Rows whose selection holds no valid block (all -1, or ids past the
-    block count) get the sink-only sparse result, as from the gather call."""
+    block count) get the sink-only sparse result, as from the gather call and
+    the oracle. Ids are distinct within each row (the gather's precondition)."""
     p = _mla("empty_sparse", 200, 76, 3, 64)
     d = Dev(p)
     rng = np.random.default_rng(77)
     nb = hs.hs_num_blocks(d.prob)
-    idx = rng.integers(0, nb, size=(1, p.Sq, p.top_k)).astype(np.int32)
+    assert nb >= p.top_k
+    idx = np.stack([rng.permutation(nb)[:p.top_k] for _ in range(p.Sq)])[None].astype(np.int32)
     idx[0, ::3] = -1
-    idx[0, 1::7] = nb + 5
-    idx = torch.from_numpy(idx).cuda()
-    got, want = _both(d, p, idx)
+    idx[0, 1::7] = nb + np.arange(p.top_k)
+    idx_t = torch.from_numpy(idx).cuda()
+    got, want = _both(d, p, idx_t)
     _equal(got, want, "empty sparse rows")
-    say("[gpu] swa+sparse with empty sparse rows: identical")
+    og_ref, lg_ref = ref.sparse_gather(p.q, p.kv, d.sink_cpu, p.Dv, p.scale, idx, **d.kw())
+    e = [assert_close(np64(got[2]), og_ref, BF16_TOL, "sparse out"),
+         assert_close(np64(got[3]), lg_ref, BF16_TOL, "sparse lse")]
+    say(f"[gpu] swa+sparse with empty sparse rows: identical, oracle {max(e):.2e}")
 
 
 def test_matches_oracle_docs():
