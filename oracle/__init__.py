@@ -19,4 +19,6 @@ from .hysparse_ref import (  # noqa: F401
     block_score_bwd,
     sparse_gather_bwd,
     swa_bwd,
+    block_prob,
+    gated_combine,
 )

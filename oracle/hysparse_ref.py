@@ -317,8 +317,9 @@ def sparse_gather(q, kv, sink, Dv, scale, block_idx, block_size=64, kv_lens=None
 # Gradients of the three attention operations.
 # ---------------------------------------------------------------------------
 def _op_bwd(kind, q, kv, sink, Dv, scale, dout, block_size, kv_lens=None, doc_start=None,
-            doc_end=None, window=None, block_idx=None, chunk=None, rows=None):
-    """Gradients of L = sum(dout * out) for one attention operation.
+            doc_end=None, window=None, block_idx=None, chunk=None, rows=None, dlse=None):
+    """Gradients of L = sum(dout * out) + sum(dlse * lse) for one attention
+    operation (dlse optional: [B, Sq, H], or the rows' when rows is given).
 
     The pages train through these kernels: page "HySparse MQA sparse attention
     ...", section "Core" (block scoring with gradients routed through the
@@ -337,8 +338,9 @@ def _op_bwd(kind, q, kv, sink, Dv, scale, dout, block_size, kv_lens=None, doc_st
         dq   = scale sum_i dL/ds_i k_i,
         dk_i = scale sum_{rows, heads} dL/ds_i q,   dv_i = sum_{rows, heads} P_i dout.
     The latent row kv_i serves as both key and value (value = its leading Dv
-    columns), so dkv_i = dk_i + [dv_i, 0]. Reading: lse receives no incoming
-    gradient (it is a saved statistic of the forward). Returns dq [B,Sq,H,Dk],
+    columns), so dkv_i = dk_i + [dv_i, 0]. An incoming gradient of lse adds
+    dL/ds_i += dlse P_i (d lse / d s_i = P_i) and dL/dsigma += dlse P_sink, so
+    both formulas hold with Dsum replaced by Dsum - dlse. Returns dq [B,Sq,H,Dk],
     dkv [B,Skv,Dk] (zero past each entry's valid length) and dsink [H]
     (None without a sink).
 
@@ -350,6 +352,7 @@ def _op_bwd(kind, q, kv, sink, Dv, scale, dout, block_size, kv_lens=None, doc_st
     B, Sq, H, Dk = q.shape
     Skv = kv.shape[1]
     g_all = dout
+    dl_all = None if dlse is None else _to64(dlse)
     rows_sel = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
     dq = np.zeros((B, len(rows_sel), H, Dk))
     dkv = np.zeros((B, Skv, Dk))
@@ -371,6 +374,8 @@ def _op_bwd(kind, q, kv, sink, Dv, scale, dout, block_size, kv_lens=None, doc_st
         P = np.where(allowed[:, None, :] & fin[:, :, None], np.exp(s - lse_s[:, :, None]), 0.0)
         dP = np.einsum("rhd,id->rhi", g, v, optimize=True)
         Dsum = np.einsum("rhd,rhd->rh", g, out, optimize=True)
+        if dl_all is not None:
+            Dsum = Dsum - dl_all[b, rr]
         dS = P * (dP - Dsum[:, :, None])
         dq[b, rr] = scale * np.einsum("rhi,id->rhd", dS, k, optimize=True)
         dkv[b, kmin:kmax] += scale * np.einsum("rhi,rhd->id", dS, qr, optimize=True)
@@ -382,26 +387,26 @@ def _op_bwd(kind, q, kv, sink, Dv, scale, dout, block_size, kv_lens=None, doc_st
 
 
 def block_score_bwd(q, kv, sink, Dv, scale, dout, block_size=64, kv_lens=None,
-                    doc_start=None, doc_end=None, chunk=None, rows=None):
+                    doc_start=None, doc_end=None, chunk=None, rows=None, dlse=None):
     """Gradients of the causal attention of block_score (block_logit has none)."""
     return _op_bwd("score", q, kv, sink, Dv, scale, dout, block_size, kv_lens, doc_start,
-                   doc_end, chunk=chunk, rows=rows)
+                   doc_end, chunk=chunk, rows=rows, dlse=dlse)
 
 
 def swa_bwd(q, kv, sink, Dv, scale, window, dout, block_size=64, kv_lens=None,
-            doc_start=None, doc_end=None, chunk=None, rows=None):
+            doc_start=None, doc_end=None, chunk=None, rows=None, dlse=None):
     """Gradients of the sliding-window attention."""
     return _op_bwd("swa", q, kv, sink, Dv, scale, dout, block_size, kv_lens, doc_start,
-                   doc_end, window=window, chunk=chunk, rows=rows)
+                   doc_end, window=window, chunk=chunk, rows=rows, dlse=dlse)
 
 
 def sparse_gather_bwd(q, kv, sink, Dv, scale, block_idx, dout, block_size=64, kv_lens=None,
-                      doc_start=None, doc_end=None, chunk=None, rows=None):
+                      doc_start=None, doc_end=None, chunk=None, rows=None, dlse=None):
     """Gradients of the block-sparse gather attention for a fixed selection."""
     bi = np.asarray(block_idx.cpu() if hasattr(block_idx, "cpu") else block_idx,
                     dtype=np.int64)
     return _op_bwd("gather", q, kv, sink, Dv, scale, dout, block_size, kv_lens, doc_start,
-                   doc_end, block_idx=bi, chunk=chunk, rows=rows)
+                   doc_end, block_idx=bi, chunk=chunk, rows=rows, dlse=dlse)
 
 
 def own_blocks(B, Sq, Skv, block_size, kv_lens=None, doc_start=None, doc_end=None,
@@ -445,3 +450,39 @@ def topk_blocks(block_logit, own, top_k: int) -> np.ndarray:
         chosen = sorted(chosen)
         res[r, :len(chosen)] = chosen
     return res.reshape(lead + (top_k,))
+
+
+def block_prob(block_logit, lse) -> np.ndarray:
+    """Normalised block scores (page "HySparse MQA sparse attention ...",
+    per-file overview row for pipeline.py: the block probabilities are
+    recovered as exp(block_logit - lse)).
+
+    Reading: block_logit is one value per (row, block) and lse one per (row,
+    head), so the row's normaliser is its largest per-head lse:
+        block_prob[b, r, j] = exp(block_logit[b, r, j] - max_h lse[b, r, h]),
+    and 0 where block_logit is -inf. With one head this is the page's formula
+    and the row sums to the mass the attention puts on keys.
+
+    block_logit [B, R, NB], lse [B, R, H] (natural log, sink included)."""
+    bl = np.asarray(block_logit.cpu() if hasattr(block_logit, "cpu") else block_logit,
+                    dtype=np.float64)
+    ls = np.asarray(lse.cpu() if hasattr(lse, "cpu") else lse, dtype=np.float64)
+    lmax = ls.max(axis=-1)[..., None]
+    with np.errstate(invalid="ignore", over="ignore"):
+        p = np.where(np.isfinite(bl), np.exp(bl - np.where(np.isfinite(lmax), lmax, 0.0)), 0.0)
+    return p
+
+
+def gated_combine(out_swa, out_sparse, gate_swa, gate_sparse) -> np.ndarray:
+    """Combination of the two branches of a sliding-window layer (reading: the
+    page "HySparse MQA sparse attention ..." calls the method NSA-style, section
+    "What", and does not state the rule; NSA combines branch outputs by a gated
+    sum with per-token, per-head gates):
+        out_mix[b, r, h, :] = gate_swa[b, r, h] * out_swa[b, r, h, :]
+                            + gate_sparse[b, r, h] * out_sparse[b, r, h, :].
+    out_* [B, R, H, Dv], gates [B, R, H]."""
+    a = _to64(out_swa)
+    b = _to64(out_sparse)
+    ga = _to64(gate_swa)[..., None]
+    gb = _to64(gate_sparse)[..., None]
+    return ga * a + gb * b

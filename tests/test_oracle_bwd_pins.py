@@ -203,3 +203,54 @@ def test_row_subset_matches_full_run():
     assert np.allclose(pb[0], full[0][:, b], atol=1e-14)
     assert np.allclose(pa[1] + pb[1], full[1], atol=1e-12)
     assert np.allclose(pa[2] + pb[2], full[2], atol=1e-12)
+
+
+def _loss_with_lse(kind, q, kv, sink, dout, dlse, Dv, scale, bs, kw):
+    kw = dict(kw)
+    if kind == "score":
+        out, lse, _ = ref.block_score(q, kv, sink, Dv, scale, block_size=bs, **kw)
+    elif kind == "swa":
+        out, lse = ref.swa(q, kv, sink, Dv, scale, kw.pop("window"), block_size=bs, **kw)
+    else:
+        out, lse = ref.sparse_gather(q, kv, sink, Dv, scale, kw.pop("block_idx"), block_size=bs,
+                                     **kw)
+    fin = np.isfinite(lse)
+    return float((out * dout).sum() + (np.where(fin, lse, 0.0) * dlse).sum())
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_lse_gradient_matches_finite_differences(name):
+    """A loss that also weights lse (as a combination of branches by their
+    log-sum-exp would): the gradients with dlse match central differences of
+    L = sum(dout * out) + sum(dlse * lse) in random directions, for q, kv and
+    the sink."""
+    kind, B, Sq, Skv, H, Dk, Dv, bs, with_sink, extra = CASES[name]
+    rng, q, kv, sink, dout = _problem(300 + list(CASES).index(name), B, Sq, Skv, H, Dk, Dv,
+                                      with_sink)
+    kw = _materialise(name, rng, B, Sq, Skv, bs, extra)
+    dlse = rng.standard_normal((B, Sq, H))
+    scale = 0.37
+    kw2 = dict(kw)
+    if kind == "score":
+        dq, dkv, dsink = ref.block_score_bwd(q, kv, sink, Dv, scale, dout, block_size=bs,
+                                             dlse=dlse, **kw2)
+    elif kind == "swa":
+        dq, dkv, dsink = ref.swa_bwd(q, kv, sink, Dv, scale, kw2.pop("window"), dout,
+                                     block_size=bs, dlse=dlse, **kw2)
+    else:
+        dq, dkv, dsink = ref.sparse_gather_bwd(q, kv, sink, Dv, scale, kw2.pop("block_idx"), dout,
+                                               block_size=bs, dlse=dlse, **kw2)
+    f = lambda q_, kv_, s_: _loss_with_lse(kind, q_, kv_, s_, dout, dlse, Dv, scale, bs, kw)
+    for trial in range(2):
+        uq = rng.standard_normal(q.shape)
+        ukv = rng.standard_normal(kv.shape)
+        fd = (f(q + EPS * uq, kv, sink) - f(q - EPS * uq, kv, sink)) / (2 * EPS)
+        assert math.isclose(fd, float((dq * uq).sum()), rel_tol=1e-6, abs_tol=1e-8), (trial, "q")
+        fd = (f(q, kv + EPS * ukv, sink) - f(q, kv - EPS * ukv, sink)) / (2 * EPS)
+        assert math.isclose(fd, float((dkv * ukv).sum()), rel_tol=1e-6, abs_tol=1e-8), (trial, "kv")
+    if sink is not None:
+        for h in range(H):
+            e = np.zeros(H)
+            e[h] = EPS
+            fd = (f(q, kv, sink + e) - f(q, kv, sink - e)) / (2 * EPS)
+            assert math.isclose(fd, dsink[h], rel_tol=1e-6, abs_tol=1e-9), h

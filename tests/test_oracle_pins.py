@@ -416,3 +416,58 @@ def test_block_table_documents():
     assert bt.end.tolist() == [64, 70, 71, 134, 198, 200]
     assert ref.num_blocks(1, 200, 64, None, [0, 70, 71, 134], [70, 71, 134, 200]) == 6
     assert ref.num_blocks(3, 300, 64, [1, 300, 129]) == 5
+
+
+def test_block_prob_one_head_is_key_mass():
+    """One head: exp(block_logit - lse) summed over the blocks is the
+    attention's mass on keys, 1 - exp(sink - lse) (all of it without a sink)."""
+    q, kv, sink = _rand(61, 2, 150, 1, 12)
+    scale = 0.3
+    for sk in (sink, None):
+        _, lse, bl = ref.block_score(q, kv, sk, 8, scale)
+        p = ref.block_prob(bl, lse)
+        mass = p.sum(axis=-1)
+        want = np.ones_like(mass) if sk is None else 1.0 - np.exp(sk[0] - lse[..., 0])
+        assert np.abs(mass - want).max() < 1e-12
+        assert (p >= 0).all() and (p <= 1 + 1e-15).all()
+
+
+def test_block_prob_many_heads_brute_force():
+    """Several heads: block_prob[j] is exp(max_h LSE_h(j) - max_h lse_h), with
+    the per-head block log-sum-exp and lse recomputed here key by key from
+    q . k (no oracle routine), and -inf blocks give 0."""
+    B, S, H, Dk, bs = 1, 70, 3, 5, 16
+    q, kv, sink = _rand(62, B, S, H, Dk)
+    scale = 0.7
+    _, lse, bl = ref.block_score(q, kv, sink, 4, scale, block_size=bs)
+    p = ref.block_prob(bl, lse)
+    for r in (0, 15, 16, 40, 69):
+        s = scale * np.einsum("hd,id->hi", q[0, r], kv[0, :r + 1])          # [H, r+1]
+        lse_h = [math.log(math.exp(sink[h]) + sum(math.exp(x) for x in s[h])) for h in range(H)]
+        for j in range((S + bs - 1) // bs):
+            keys = range(j * bs, min((j + 1) * bs, r + 1))
+            if len(keys) == 0:
+                assert p[0, r, j] == 0.0
+                continue
+            blk = max(math.log(sum(math.exp(s[h, i]) for i in keys)) for h in range(H))
+            assert abs(p[0, r, j] - math.exp(blk - max(lse_h))) < 1e-12
+
+
+def test_gated_combine_selects_and_is_linear():
+    """Gates (1, 0) and (0, 1) give back each branch; the sum is linear in the
+    gates and in each branch (checked against hand-written per-element sums
+    on a tiny case)."""
+    rng = np.random.default_rng(63)
+    a = rng.standard_normal((2, 3, 4, 5))
+    b = rng.standard_normal((2, 3, 4, 5))
+    one, zero = np.ones((2, 3, 4)), np.zeros((2, 3, 4))
+    assert np.array_equal(ref.gated_combine(a, b, one, zero), a)
+    assert np.array_equal(ref.gated_combine(a, b, zero, one), b)
+    g1 = rng.uniform(size=(2, 3, 4))
+    g2 = rng.uniform(size=(2, 3, 4))
+    m = ref.gated_combine(a, b, g1, g2)
+    for idx in [(0, 0, 0, 0), (1, 2, 3, 4), (0, 1, 2, 3)]:
+        want = g1[idx[:3]] * a[idx] + g2[idx[:3]] * b[idx]
+        assert abs(m[idx] - want) < 1e-15
+    # one branch's full output with equal gates of 1/2 each is its mean
+    assert np.allclose(ref.gated_combine(a, a, one / 2, one / 2), a, atol=0, rtol=1e-15)
