@@ -33,7 +33,8 @@ HS_OP_BLOCK_SCORE_BWD_STORE_DS, HS_OP_SWA_BWD_STORE_DS = 6, 7
 HS_OP_SWA_SPARSE = 8
 
 EXPORTS = ("hs_num_blocks", "hs_workspace_size", "hs_block_score_fwd", "hs_topk_blocks",
-           "hs_block_score_topk_fwd", "hs_sparse_gather_fwd", "hs_swa_fwd", "hs_swa_sparse_fwd",
+           "hs_block_score_topk_fwd", "hs_sparse_gather_fwd",
+           "hs_swa_fwd", "hs_swa_sparse_fwd",
            "hs_block_score_bwd", "hs_sparse_gather_bwd", "hs_swa_bwd", "hs_status_string",
            "hs_last_error", "hs_version")
 
@@ -48,7 +49,7 @@ class HsProblem(ctypes.Structure):
         ("doc_start", ctypes.POINTER(ctypes.c_int32)),
         ("doc_end", ctypes.POINTER(ctypes.c_int32)), ("n_docs", ctypes.c_int32),
         ("page_table", ctypes.c_void_p), ("max_pages", ctypes.c_int32),
-        ("kv_lens_device", ctypes.c_void_p),
+        ("kv_lens_device", ctypes.c_void_p), ("doc_bounds_device", ctypes.c_void_p),
     ]
 
 
@@ -75,20 +76,21 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hs_block_score_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hs_block_score_fwd.restype = i32
     lib.hs_topk_blocks.argtypes, lib.hs_topk_blocks.restype = [P, vp, i32, vp, vp], i32
-    lib.hs_block_score_topk_fwd.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.hs_block_score_topk_fwd.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hs_block_score_topk_fwd.restype = i32
     lib.hs_sparse_gather_fwd.argtypes = [P, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
     lib.hs_sparse_gather_fwd.restype = i32
     lib.hs_swa_fwd.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, sz, vp]
     lib.hs_swa_fwd.restype = i32
-    lib.hs_swa_sparse_fwd.argtypes = [P, vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.hs_swa_sparse_fwd.argtypes = [P, vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      sz, vp]
     lib.hs_swa_sparse_fwd.restype = i32
-    lib.hs_block_score_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hs_block_score_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hs_block_score_bwd.restype = i32
-    lib.hs_sparse_gather_bwd.argtypes = [P, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz,
-                                         vp]
+    lib.hs_sparse_gather_bwd.argtypes = [P, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         sz, vp]
     lib.hs_sparse_gather_bwd.restype = i32
-    lib.hs_swa_bwd.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hs_swa_bwd.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hs_swa_bwd.restype = i32
     lib.hs_status_string.argtypes, lib.hs_status_string.restype = [i32], ctypes.c_char_p
     lib.hs_last_error.argtypes, lib.hs_last_error.restype = [], ctypes.c_char_p
@@ -117,23 +119,34 @@ class Problem:
                  kv_lens: Optional[Sequence[int]] = None,
                  doc_start: Optional[Sequence[int]] = None,
                  doc_end: Optional[Sequence[int]] = None,
-                 page_table=None, kv_lens_device=None):
+                 page_table=None, kv_lens_device=None, doc_bounds_device=None):
         """page_table: optional int32 device tensor [B, max_pages] (paged KV: kv is
         then a pool [n_pages, block_size, Dk]); kv_lens_device: optional int32
-        device tensor [B] of lengths read at run time (paged KV only; Skv is
-        then the capacity). Both tensors must outlive the calls."""
+        device tensor [B] of lengths read at run time (bf16, in-place or paged; Skv is
+        then the capacity); doc_bounds_device: optional int32 device tensor
+        [n_docs + 1] of cumulative document starts read at run time (bf16 forward;
+        its length minus one is the document capacity). The tensors must outlive
+        the calls."""
         self.B, self.Sq, self.Skv, self.H, self.Dk, self.Dv = B, Sq, Skv, H, Dk, Dv
         self.page_table = page_table
         self.block_size = block_size
-        if page_table is not None or kv_lens_device is not None:
+        if page_table is not None or kv_lens_device is not None or doc_bounds_device is not None:
             import torch
             if page_table is not None and (page_table.dim() != 2 or page_table.shape[0] != B):
                 raise ValueError("page_table must be [B, max_pages]")
             _meta("page_table", page_table, torch.int32)
             _meta("kv_lens_device", kv_lens_device, torch.int32, (B,))
+            if doc_bounds_device is not None and doc_bounds_device.dim() != 1:
+                raise ValueError("doc_bounds_device must be [n_docs + 1]")
+            _meta("doc_bounds_device", doc_bounds_device, torch.int32)
             _dev("page_table", page_table)
             _dev("kv_lens_device", kv_lens_device)
+            _dev("doc_bounds_device", doc_bounds_device)
         self.kv_lens_device = kv_lens_device
+        self.doc_bounds_device = doc_bounds_device
+        n_docs = len(doc_start) if doc_start is not None else 0
+        if doc_bounds_device is not None:
+            n_docs = int(doc_bounds_device.shape[0]) - 1
         self.dtype = dtype
         self._kv = (ctypes.c_int32 * len(kv_lens))(*kv_lens) if kv_lens is not None else None
         self._ds = (ctypes.c_int32 * len(doc_start))(*doc_start) if doc_start is not None else None
@@ -146,10 +159,11 @@ class Problem:
             n_kv_lens=len(kv_lens) if kv_lens is not None else 0,
             doc_start=ctypes.cast(self._ds, ctypes.POINTER(ctypes.c_int32)) if self._ds else None,
             doc_end=ctypes.cast(self._de, ctypes.POINTER(ctypes.c_int32)) if self._de else None,
-            n_docs=len(doc_start) if doc_start is not None else 0,
+            n_docs=n_docs,
             page_table=None if page_table is None else page_table.data_ptr(),
             max_pages=0 if page_table is None else int(page_table.shape[1]),
-            kv_lens_device=None if kv_lens_device is None else kv_lens_device.data_ptr())
+            kv_lens_device=None if kv_lens_device is None else kv_lens_device.data_ptr(),
+            doc_bounds_device=None if doc_bounds_device is None else doc_bounds_device.data_ptr())
 
     @property
     def ref(self):
@@ -220,7 +234,7 @@ def _check_io(prob, **tensors):
             _meta(name, t, f32, (B, Sq, H))
         elif name in ("out", "dout", "out_swa", "out_sparse", "out_mix"):
             _meta(name, t, dt, (B, Sq, H, Dv))
-        elif name in ("lse", "lse_swa", "lse_sparse"):
+        elif name in ("lse", "lse_swa", "lse_sparse", "dlse"):
             _meta(name, t, f32, (B, Sq, H))
         elif name in ("block_logit", "block_prob"):
             _meta(name, t, f32, (B, Sq, hs_num_blocks(prob)))
@@ -266,12 +280,12 @@ def hs_topk_blocks(prob, block_logit, top_k, block_idx, stream=None):
 
 
 def hs_block_score_topk_fwd(prob, q, kv, sink, top_k, out, lse, block_logit, block_idx, ws=None,
-                            stream=None):
+                            stream=None, block_prob=None):
     _check_io(prob, q=q, kv=kv, sink=sink, out=out, lse=lse, block_logit=block_logit,
-              block_idx=block_idx, ws=ws, _top_k=int(top_k))
+              block_idx=block_idx, block_prob=block_prob, ws=ws, _top_k=int(top_k))
     _check(load_library().hs_block_score_topk_fwd(
         prob.ref, _ptr(q), _ptr(kv), _ptr(sink), int(top_k), _ptr(out), _ptr(lse),
-        _ptr(block_logit), _ptr(block_idx), _ptr(ws),
+        _ptr(block_logit), _ptr(block_idx), _ptr(block_prob), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
@@ -292,12 +306,15 @@ def hs_swa_fwd(prob, q, kv, sink, window, out, lse, ws=None, stream=None):
 
 
 def hs_swa_sparse_fwd(prob, q, kv, sink, window, block_idx, top_k, out_swa, lse_swa, out_sparse,
-                      lse_sparse, ws=None, stream=None):
+                      lse_sparse, ws=None, stream=None, gate_swa=None, gate_sparse=None,
+                      out_mix=None):
     _check_io(prob, q=q, kv=kv, sink=sink, block_idx=block_idx, out_swa=out_swa, lse_swa=lse_swa,
-              out_sparse=out_sparse, lse_sparse=lse_sparse, ws=ws, _top_k=int(top_k))
+              out_sparse=out_sparse, lse_sparse=lse_sparse, gate_swa=gate_swa,
+              gate_sparse=gate_sparse, out_mix=out_mix, ws=ws, _top_k=int(top_k))
     _check(load_library().hs_swa_sparse_fwd(
         prob.ref, _ptr(q), _ptr(kv), _ptr(sink), int(window), _ptr(block_idx), int(top_k),
-        _ptr(out_swa), _ptr(lse_swa), _ptr(out_sparse), _ptr(lse_sparse), _ptr(ws),
+        _ptr(out_swa), _ptr(lse_swa), _ptr(out_sparse), _ptr(lse_sparse), _ptr(gate_swa),
+        _ptr(gate_sparse), _ptr(out_mix), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
@@ -305,30 +322,32 @@ def _nbytes(ws) -> int:
     return 0 if ws is None else ws.numel() * ws.element_size()
 
 
-def hs_block_score_bwd(prob, q, kv, sink, out, lse, dout, dq, dkv, dsink, ws, stream=None):
-    _check_io(prob, q=q, kv=kv, sink=sink, out=out, lse=lse, dout=dout, dq=dq, dkv=dkv,
-              dsink=dsink, ws=ws)
+def hs_block_score_bwd(prob, q, kv, sink, out, lse, dout, dq, dkv, dsink, ws, stream=None,
+                       dlse=None):
+    _check_io(prob, q=q, kv=kv, sink=sink, out=out, lse=lse, dout=dout, dlse=dlse, dq=dq,
+              dkv=dkv, dsink=dsink, ws=ws)
     _check(load_library().hs_block_score_bwd(
-        prob.ref, _ptr(q), _ptr(kv), _ptr(sink), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
-        _ptr(dkv), _ptr(dsink), _ptr(ws), _nbytes(ws), _stream(stream)))
+        prob.ref, _ptr(q), _ptr(kv), _ptr(sink), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dlse),
+        _ptr(dq), _ptr(dkv), _ptr(dsink), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def hs_sparse_gather_bwd(prob, q, kv, sink, block_idx, top_k, out, lse, dout, dq, dkv, dsink,
-                         ws, stream=None):
+                         ws, stream=None, dlse=None):
     _check_io(prob, q=q, kv=kv, sink=sink, block_idx=block_idx, out=out, lse=lse, dout=dout,
-              dq=dq, dkv=dkv, dsink=dsink, ws=ws, _top_k=int(top_k))
+              dlse=dlse, dq=dq, dkv=dkv, dsink=dsink, ws=ws, _top_k=int(top_k))
     _check(load_library().hs_sparse_gather_bwd(
         prob.ref, _ptr(q), _ptr(kv), _ptr(sink), _ptr(block_idx), int(top_k), _ptr(out),
-        _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dkv), _ptr(dsink), _ptr(ws), _nbytes(ws),
-        _stream(stream)))
+        _ptr(lse), _ptr(dout), _ptr(dlse), _ptr(dq), _ptr(dkv), _ptr(dsink), _ptr(ws),
+        _nbytes(ws), _stream(stream)))
 
 
-def hs_swa_bwd(prob, q, kv, sink, window, out, lse, dout, dq, dkv, dsink, ws, stream=None):
-    _check_io(prob, q=q, kv=kv, sink=sink, out=out, lse=lse, dout=dout, dq=dq, dkv=dkv,
-              dsink=dsink, ws=ws)
+def hs_swa_bwd(prob, q, kv, sink, window, out, lse, dout, dq, dkv, dsink, ws, stream=None,
+               dlse=None):
+    _check_io(prob, q=q, kv=kv, sink=sink, out=out, lse=lse, dout=dout, dlse=dlse, dq=dq,
+              dkv=dkv, dsink=dsink, ws=ws)
     _check(load_library().hs_swa_bwd(
         prob.ref, _ptr(q), _ptr(kv), _ptr(sink), int(window), _ptr(out), _ptr(lse), _ptr(dout),
-        _ptr(dq), _ptr(dkv), _ptr(dsink), _ptr(ws), _nbytes(ws), _stream(stream)))
+        _ptr(dlse), _ptr(dq), _ptr(dkv), _ptr(dsink), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------
@@ -354,15 +373,19 @@ def block_score(prob, q, kv, sink=None, stream=None):
     return out, lse, bl
 
 
-def block_score_topk(prob, q, kv, sink, top_k, stream=None):
+def block_score_topk(prob, q, kv, sink, top_k, stream=None, with_prob=False):
+    """(out, lse, block_logit, block_idx[, block_prob]) of hs_block_score_topk_fwd;
+    block_prob (the normalised block scores) when with_prob."""
     import torch
     out = torch.empty((prob.B, prob.Sq, prob.H, prob.Dv), dtype=_torch_dtype(prob), device=q.device)
     lse = torch.empty((prob.B, prob.Sq, prob.H), dtype=torch.float32, device=q.device)
-    bl = torch.empty((prob.B, prob.Sq, hs_num_blocks(prob)), dtype=torch.float32, device=q.device)
+    NB = hs_num_blocks(prob)
+    bl = torch.empty((prob.B, prob.Sq, NB), dtype=torch.float32, device=q.device)
     idx = torch.empty((prob.B, prob.Sq, top_k), dtype=torch.int32, device=q.device)
+    pr = torch.empty((prob.B, prob.Sq, NB), dtype=torch.float32, device=q.device) if with_prob else None
     hs_block_score_topk_fwd(prob, q, kv, sink, top_k, out, lse, bl, idx,
-                            _workspace(prob, HS_OP_BLOCK_SCORE), stream)
-    return out, lse, bl, idx
+                            _workspace(prob, HS_OP_BLOCK_SCORE), stream, block_prob=pr)
+    return (out, lse, bl, idx, pr) if with_prob else (out, lse, bl, idx)
 
 
 def topk_blocks(prob, block_logit, top_k, stream=None):
@@ -390,10 +413,13 @@ def swa(prob, q, kv, sink, window, stream=None):
     return out, lse
 
 
-def swa_sparse(prob, q, kv, sink, window, block_idx, top_k, stream=None):
+def swa_sparse(prob, q, kv, sink, window, block_idx, top_k, stream=None, gate_swa=None,
+               gate_sparse=None):
     """Both branches of a sliding-window layer over the shared latent KV and a
     given block selection: (out_swa, lse_swa, out_sparse, lse_sparse), equal
-    to swa(...) and sparse_gather(...) for the same arguments."""
+    to swa(...) and sparse_gather(...) for the same arguments; with the gates
+    ([B, Sq, H] float32) also out_mix = gate_swa * out_swa + gate_sparse *
+    out_sparse as a fifth result."""
     import torch
     shape_o = (prob.B, prob.Sq, prob.H, prob.Dv)
     shape_l = (prob.B, prob.Sq, prob.H)
@@ -401,9 +427,11 @@ def swa_sparse(prob, q, kv, sink, window, block_idx, top_k, stream=None):
     lw = torch.empty(shape_l, dtype=torch.float32, device=q.device)
     og = torch.empty(shape_o, dtype=_torch_dtype(prob), device=q.device)
     lg = torch.empty(shape_l, dtype=torch.float32, device=q.device)
+    om = None if gate_swa is None else torch.empty(shape_o, dtype=_torch_dtype(prob), device=q.device)
     hs_swa_sparse_fwd(prob, q, kv, sink, window, block_idx, top_k, ow, lw, og, lg,
-                      _workspace(prob, HS_OP_SWA_SPARSE, top_k=top_k, window=window), stream)
-    return ow, lw, og, lg
+                      _workspace(prob, HS_OP_SWA_SPARSE, top_k=top_k, window=window), stream,
+                      gate_swa=gate_swa, gate_sparse=gate_sparse, out_mix=om)
+    return (ow, lw, og, lg) if om is None else (ow, lw, og, lg, om)
 
 
 def _grad_buffers(prob, q, sink):
@@ -433,28 +461,28 @@ def swa_bwd_workspace(prob, window, store_ds=False):
     return _stored_ds_workspace(prob, HS_OP_SWA_BWD, HS_OP_SWA_BWD_STORE_DS, store_ds, window)
 
 
-def block_score_bwd(prob, q, kv, sink, out, lse, dout, stream=None, store_ds=False):
+def block_score_bwd(prob, q, kv, sink, out, lse, dout, stream=None, store_ds=False, dlse=None):
     """Gradients (dq, dkv, dsink) of the causal attention of block_score;
     dsink is None without a sink. All float32. store_ds picks the workspace
     (score_bwd_workspace)."""
     dq, dkv, dsink = _grad_buffers(prob, q, sink)
     hs_block_score_bwd(prob, q, kv, sink, out, lse, dout, dq, dkv, dsink,
-                       score_bwd_workspace(prob, store_ds), stream)
+                       score_bwd_workspace(prob, store_ds), stream, dlse=dlse)
     return dq, dkv, dsink
 
 
-def sparse_gather_bwd(prob, q, kv, sink, block_idx, top_k, out, lse, dout, stream=None):
+def sparse_gather_bwd(prob, q, kv, sink, block_idx, top_k, out, lse, dout, stream=None, dlse=None):
     """Gradients (dq, dkv, dsink) of sparse_gather for the given selection."""
     dq, dkv, dsink = _grad_buffers(prob, q, sink)
     hs_sparse_gather_bwd(prob, q, kv, sink, block_idx, top_k, out, lse, dout, dq, dkv, dsink,
-                         _workspace(prob, HS_OP_SPARSE_GATHER_BWD, top_k=top_k), stream)
+                         _workspace(prob, HS_OP_SPARSE_GATHER_BWD, top_k=top_k), stream, dlse=dlse)
     return dq, dkv, dsink
 
 
-def swa_bwd(prob, q, kv, sink, window, out, lse, dout, stream=None, store_ds=False):
+def swa_bwd(prob, q, kv, sink, window, out, lse, dout, stream=None, store_ds=False, dlse=None):
     """Gradients (dq, dkv, dsink) of swa. store_ds picks the workspace
     (swa_bwd_workspace)."""
     dq, dkv, dsink = _grad_buffers(prob, q, sink)
     hs_swa_bwd(prob, q, kv, sink, window, out, lse, dout, dq, dkv, dsink,
-               swa_bwd_workspace(prob, window, store_ds), stream)
+               swa_bwd_workspace(prob, window, store_ds), stream, dlse=dlse)
     return dq, dkv, dsink

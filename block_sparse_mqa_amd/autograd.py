@@ -7,8 +7,10 @@ layers of the page "HySparse MQA sparse attention (FA4 block scoring + SWA
 MQA + block-sparse DSA gather)", section "Core": block scoring trained
 through its autograd layer, and the learnable sink's analytic gradient. As in
 the review of PaddleFleet PR 1453 (block-score PyLayer comments), gradients
-flow to q, the latent kv and the sink only. lse, the block scores and the
-block selection are outputs without gradient.
+flow to q, the latent kv and the sink only; the block scores and the block
+selection are outputs without gradient. lse is differentiable: a loss that
+uses it (for instance branches weighted by their log-sum-exp) passes its
+gradient to the kernels, which add it exactly (dlse in include/hs.h).
 
 The library computes gradients in fp32. Autograd needs each gradient in its
 input's dtype, so bf16 inputs receive the fp32 gradients rounded to bf16.
@@ -49,16 +51,16 @@ class BlockScoreTopk(torch.autograd.Function):
         out, lse, bl, idx = block_score_topk(prob, q, kv, sink, top_k)
         ctx.save_for_backward(q, kv, sink, out, lse)
         ctx.prob = prob
-        ctx.mark_non_differentiable(lse, bl, idx)
+        ctx.mark_non_differentiable(bl, idx)
         return out, lse, bl, idx
 
     @staticmethod
-    def backward(ctx, dout, _dlse, _dbl, _didx):
+    def backward(ctx, dout, dlse, _dbl, _didx):
         q, kv, sink, out, lse = ctx.saved_tensors
         prob = ctx.prob
         dq, dkv, dsink = _grads(prob, q, sink, ctx.needs_input_grad[2])
         hs_block_score_bwd(prob, q, kv, sink, out, lse, dout.contiguous(), dq, dkv, dsink,
-                           score_bwd_workspace(prob))
+                           score_bwd_workspace(prob), dlse=dlse.contiguous())
         return (*_finish(ctx, q, kv, sink, dq, dkv, dsink), None, None)
 
 
@@ -71,17 +73,17 @@ class SparseGather(torch.autograd.Function):
         out, lse = sparse_gather(prob, q, kv, sink, block_idx, top_k)
         ctx.save_for_backward(q, kv, sink, block_idx, out, lse)
         ctx.prob, ctx.top_k = prob, top_k
-        ctx.mark_non_differentiable(lse)
         return out, lse
 
     @staticmethod
-    def backward(ctx, dout, _dlse):
+    def backward(ctx, dout, dlse):
         q, kv, sink, block_idx, out, lse = ctx.saved_tensors
         prob = ctx.prob
         dq, dkv, dsink = _grads(prob, q, sink, ctx.needs_input_grad[2])
         hs_sparse_gather_bwd(prob, q, kv, sink, block_idx, ctx.top_k, out, lse,
                              dout.contiguous(), dq, dkv, dsink,
-                             _workspace(prob, HS_OP_SPARSE_GATHER_BWD, top_k=ctx.top_k))
+                             _workspace(prob, HS_OP_SPARSE_GATHER_BWD, top_k=ctx.top_k),
+                             dlse=dlse.contiguous())
         return (*_finish(ctx, q, kv, sink, dq, dkv, dsink), None, None, None)
 
 
@@ -93,16 +95,15 @@ class SlidingWindow(torch.autograd.Function):
         out, lse = swa(prob, q, kv, sink, window)
         ctx.save_for_backward(q, kv, sink, out, lse)
         ctx.prob, ctx.window = prob, window
-        ctx.mark_non_differentiable(lse)
         return out, lse
 
     @staticmethod
-    def backward(ctx, dout, _dlse):
+    def backward(ctx, dout, dlse):
         q, kv, sink, out, lse = ctx.saved_tensors
         prob = ctx.prob
         dq, dkv, dsink = _grads(prob, q, sink, ctx.needs_input_grad[2])
         hs_swa_bwd(prob, q, kv, sink, ctx.window, out, lse, dout.contiguous(), dq, dkv, dsink,
-                   swa_bwd_workspace(prob, ctx.window))
+                   swa_bwd_workspace(prob, ctx.window), dlse=dlse.contiguous())
         return (*_finish(ctx, q, kv, sink, dq, dkv, dsink), None, None)
 
 
@@ -110,8 +111,8 @@ class SlidingWindowLayer(torch.autograd.Function):
     """(out_swa, lse_swa, out_sparse, lse_sparse): both branches of a
     sliding-window layer over a full layer's KV and block selection
     (hs_swa_sparse_fwd). The gradient is the sum of the two branches'
-    (hs_swa_bwd and hs_sparse_gather_bwd); a branch whose output receives no
-    gradient is skipped."""
+    (hs_swa_bwd and hs_sparse_gather_bwd), each with the gradients its out and
+    lse receive; a branch whose outputs receive none is skipped."""
 
     @staticmethod
     def forward(ctx, q, kv, sink, block_idx, prob: Problem, window: int, top_k: int):
@@ -119,25 +120,25 @@ class SlidingWindowLayer(torch.autograd.Function):
         ctx.save_for_backward(q, kv, sink, block_idx, ow, lw, og, lg)
         ctx.prob, ctx.window, ctx.top_k = prob, window, top_k
         ctx.set_materialize_grads(False)
-        ctx.mark_non_differentiable(lw, lg)
         return ow, lw, og, lg
 
     @staticmethod
-    def backward(ctx, dout_swa, _dlw, dout_sparse, _dlg):
+    def backward(ctx, dout_swa, dlw, dout_sparse, dlg):
         q, kv, sink, block_idx, ow, lw, og, lg = ctx.saved_tensors
         prob = ctx.prob
         total = None
-        for dout, run in (
-                (dout_swa, lambda g, d: hs_swa_bwd(
+        for dout, dl, run in (
+                (dout_swa, dlw, lambda g, d, l_: hs_swa_bwd(
                     prob, q, kv, sink, ctx.window, ow, lw, d, *g,
-                    swa_bwd_workspace(prob, ctx.window))),
-                (dout_sparse, lambda g, d: hs_sparse_gather_bwd(
+                    swa_bwd_workspace(prob, ctx.window), dlse=l_)),
+                (dout_sparse, dlg, lambda g, d, l_: hs_sparse_gather_bwd(
                     prob, q, kv, sink, block_idx, ctx.top_k, og, lg, d, *g,
-                    _workspace(prob, HS_OP_SPARSE_GATHER_BWD, top_k=ctx.top_k)))):
-            if dout is None:
+                    _workspace(prob, HS_OP_SPARSE_GATHER_BWD, top_k=ctx.top_k), dlse=l_))):
+            if dout is None and dl is None:
                 continue
             g = _grads(prob, q, sink, ctx.needs_input_grad[2])
-            run(g, dout.contiguous())
+            d = torch.zeros_like(ow) if dout is None else dout.contiguous()
+            run(g, d, None if dl is None else dl.contiguous())
             total = g if total is None else tuple(
                 None if a is None else a + b for a, b in zip(total, g))
         if total is None:

@@ -18,7 +18,8 @@ LIB = os.path.join(HERE, "libhysparse.so")
 PROBE_LIB = os.path.join(HERE, "libhsprobe.so")
 PROBE_SOURCES = ["hs_probe.hip"]
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["hs_abi.hip", "hs_attn_bf16.hip", "hs_attn_f32.hip", "hs_topk.hip", "hs_bwd.hip"]
+SOURCES = ["hs_abi.hip", "hs_attn_bf16.hip", "hs_attn_f32.hip", "hs_topk.hip", "hs_bwd.hip",
+           "hs_bwd_plan.hip", "hs_mix.hip"]
 # Per-source extra flags. The bf16 engine keeps its MFMA accumulators in
 # VGPRs so that the O rescale and epilogue need no AGPR<->VGPR copies; Q and
 # other long-lived operands then go to AGPRs, which MFMA reads directly. Its

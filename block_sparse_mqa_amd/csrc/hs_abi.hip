@@ -14,6 +14,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdint>
 #include <cstring>
 #include <string>
 
@@ -96,7 +97,28 @@ hs_status prepare(const hs_problem* p, hs::Geom& g) {
     for (int b = 0; b < p->batch; ++b) g.kv_len[b] = p->seqlen_kv;
   }
 
-  if (p->n_docs != 0 || p->doc_start || p->doc_end) {
+  if (p->doc_bounds_device) {
+    // Packing read at run time; n_docs is the capacity (at most 64, one lane
+    // of the device lookup each).
+    if (p->dtype != HS_BF16)
+      return fail(HS_ERR_UNSUPPORTED, "device-resident document bounds are built for bf16 only");
+    if (p->doc_start || p->doc_end)
+      return fail(HS_ERR_INVALID_ARG, "doc_bounds_device and doc_start/doc_end are exclusive");
+    if (p->n_docs < 1)
+      return fail(HS_ERR_INVALID_ARG, "doc_bounds_device needs n_docs >= 1 (the capacity)");
+    if (p->n_docs > hs::kMaxDocs)
+      return fail(HS_ERR_UNSUPPORTED, "n_docs %d exceeds %d", p->n_docs, hs::kMaxDocs);
+    if (p->batch != 1 || p->kv_lens || p->kv_lens_device || p->page_table)
+      return fail(HS_ERR_INVALID_ARG,
+                  "documents require batch == 1 and no kv_lens, kv_lens_device or page_table");
+    if (p->seqlen_q != p->seqlen_kv)
+      return fail(HS_ERR_INVALID_ARG, "documents require seqlen_q == seqlen_kv");
+    if (reinterpret_cast<uintptr_t>(p->doc_bounds_device) % 4 != 0)
+      return fail(HS_ERR_INVALID_ARG, "doc_bounds_device is not 4-byte aligned");
+    g.n_docs = p->n_docs;
+    g.doc_dev = p->doc_bounds_device;
+    g.NB = (p->seqlen_q + g.BS - 1) / g.BS + p->n_docs - 1;
+  } else if (p->n_docs != 0 || p->doc_start || p->doc_end) {
     if (p->n_docs < 1 || !p->doc_start || !p->doc_end)
       return fail(HS_ERR_INVALID_ARG, "documents need doc_start, doc_end and n_docs >= 1");
     if (p->n_docs > hs::kMaxDocs)
@@ -130,8 +152,10 @@ hs_status prepare(const hs_problem* p, hs::Geom& g) {
   }
 
   if (p->kv_lens_device) {
-    if (!p->page_table)
-      return fail(HS_ERR_INVALID_ARG, "kv_lens_device needs paged KV (page_table)");
+    if (p->dtype != HS_BF16)
+      return fail(HS_ERR_UNSUPPORTED, "device-resident lengths are built for bf16 only");
+    if (g.n_docs != 0)
+      return fail(HS_ERR_INVALID_ARG, "kv_lens_device does not take documents");
     if (p->kv_lens)
       return fail(HS_ERR_INVALID_ARG, "kv_lens and kv_lens_device are exclusive");
     if (reinterpret_cast<uintptr_t>(p->kv_lens_device) % 4 != 0)
@@ -163,9 +187,12 @@ struct SplitPlan {
   int nsplit, tiles;
 };
 
-SplitPlan plan_split(const hs::Geom& g, int op, int top_k, int window) {
+// max_ws bounds the partials' workspace: past it, rows take fewer, longer
+// chunks.
+SplitPlan plan_split(const hs::Geom& g, int op, int top_k, int window,
+                     size_t max_ws = SIZE_MAX) {
   SplitPlan sp{1, 0};
-  if (g.Dk != 576) return sp;
+  if (g.Dk != 576 || g.doc_dev != nullptr) return sp;   // the host cannot see device documents
   const int items = g.B * g.Sq;
   if (items >= 512) return sp;
   long total = 0;
@@ -185,7 +212,15 @@ SplitPlan plan_split(const hs::Geom& g, int op, int top_k, int window) {
     }
   int tiles = (int)std::max<long>(4, (total + 511) / 512);
   tiles = std::max(tiles, (longest + 63) / 64);
-  const int ns = (longest + tiles - 1) / tiles;
+  int ns = (longest + tiles - 1) / tiles;
+  const size_t per_split = (size_t)g.B * g.Sq * g.H * (g.Dv + 2) * sizeof(float);
+  if (ns > 1 && (size_t)ns * per_split > max_ws) {
+    ns = (int)std::min<size_t>(max_ws / per_split, (size_t)ns);
+    if (ns > 1) {
+      tiles = (longest + ns - 1) / ns;
+      ns = (longest + tiles - 1) / tiles;
+    }
+  }
   if (ns > 1) sp = SplitPlan{ns, tiles};
   return sp;
 }
@@ -209,11 +244,12 @@ hs_status hip_status(int err, const char* what) {
   return HS_OK;
 }
 
-// sel_idx (score operation only): also select each row's top sel_k blocks.
+// sel_idx (score operation only): also select each row's top sel_k blocks,
+// and with sel_prob write the normalised block scores.
 hs_status launch_attn(int op, const hs_problem* p, const void* q, const void* kv, const float* sink,
                       const int32_t* block_idx, int32_t top_k, int32_t window, void* out,
                       float* lse, float* block_logit, void* ws, size_t ws_bytes, void* stream,
-                      int32_t* sel_idx = nullptr, int32_t sel_k = 0) {
+                      int32_t* sel_idx = nullptr, int32_t sel_k = 0, float* sel_prob = nullptr) {
   hs::Geom g;
   hs_status st = prepare(p, g);
   if (st != HS_OK) return st;
@@ -227,6 +263,7 @@ hs_status launch_attn(int op, const hs_problem* p, const void* q, const void* kv
     if (sel_k > 64) return fail(HS_ERR_UNSUPPORTED, "top_k %d exceeds 64", sel_k);
     if (g.NB > 4096) return fail(HS_ERR_UNSUPPORTED, "%d blocks exceed 4096", g.NB);
   }
+  if (sel_prob && (st = check_ptr(sel_prob, "block_prob", 4))) return st;
   if (op == HS_OP_SPARSE_GATHER) {
     if ((st = check_ptr(block_idx, "block_idx", 4))) return st;
     if (top_k < 1) return fail(HS_ERR_INVALID_ARG, "top_k must be >= 1 (got %d)", top_k);
@@ -270,6 +307,7 @@ hs_status launch_attn(int op, const hs_problem* p, const void* q, const void* kv
     a.max_pages = p->page_table ? p->max_pages : 0;
     a.topk_idx = sel_idx;
     a.topk_k = sel_k;
+    a.topk_prob = sel_prob;
     a.g = g;
     return hip_status(hs::attn_bf16_launch(op, a, s), "attention launch");
   }
@@ -292,6 +330,8 @@ hs_status launch_attn(int op, const hs_problem* p, const void* q, const void* kv
   t.block_logit = block_logit;
   t.block_idx = sel_idx;
   t.top_k = sel_k;
+  t.lse = lse;
+  t.block_prob = sel_prob;
   t.g = g;
   return hip_status(hs::topk_launch(t, s), "top-k launch");
 }
@@ -300,19 +340,23 @@ hs_status launch_attn(int op, const hs_problem* p, const void* q, const void* kv
 // or _SWA; the matching _BWD workspace).
 hs_status launch_bwd(int op, const hs_problem* p, const void* q, const void* kv,
                      const float* sink, const int32_t* block_idx, int32_t top_k, int32_t window,
-                     const void* out, const float* lse, const void* dout, float* dq, float* dkv,
-                     float* dsink, void* ws, size_t ws_bytes, void* stream) {
+                     const void* out, const float* lse, const void* dout, const float* dlse,
+                     float* dq, float* dkv, float* dsink, void* ws, size_t ws_bytes,
+                     void* stream) {
   hs::Geom g;
   hs_status st = prepare(p, g);
   if (st != HS_OK) return st;
-  if (p->page_table || p->kv_lens_device)
-    return fail(HS_ERR_UNSUPPORTED, "gradients take a contiguous kv with host lengths (no paged KV)");
+  if (p->page_table || p->kv_lens_device || p->doc_bounds_device)
+    return fail(HS_ERR_UNSUPPORTED,
+                "gradients take a contiguous kv with host lengths and documents (no paged KV)");
   if ((st = check_ptr(q, "q")) || (st = check_ptr(kv, "kv")) || (st = check_ptr(out, "out")) ||
       (st = check_ptr(lse, "lse", 4)) || (st = check_ptr(dout, "dout")) ||
       (st = check_ptr(dq, "dq")) || (st = check_ptr(dkv, "dkv")))
     return st;
   if (sink && reinterpret_cast<uintptr_t>(sink) % 4 != 0)
     return fail(HS_ERR_INVALID_ARG, "sink is not 4-byte aligned");
+  if (dlse && reinterpret_cast<uintptr_t>(dlse) % 4 != 0)
+    return fail(HS_ERR_INVALID_ARG, "dlse is not 4-byte aligned");
   if (dsink) {
     if (!sink) return fail(HS_ERR_INVALID_ARG, "dsink is set but there is no sink");
     if ((st = check_ptr(dsink, "dsink", 4))) return st;
@@ -350,6 +394,7 @@ hs_status launch_bwd(int op, const hs_problem* p, const void* q, const void* kv,
   a.out = out;
   a.lse = lse;
   a.dout = dout;
+  a.dlse = dlse;
   a.block_idx = block_idx;
   a.top_k = top_k;
   a.window = window;
@@ -391,7 +436,7 @@ hs_status launch_bwd(int op, const hs_problem* p, const void* q, const void* kv,
 
 extern "C" {
 
-int32_t hs_version(void) { return 106; }
+int32_t hs_version(void) { return 201; }
 
 const char* hs_status_string(int32_t status) {
   switch (status) {
@@ -433,6 +478,8 @@ hs_status hs_workspace_size(const hs_problem* p, int32_t op, int32_t top_k, int3
     return HS_OK;
   }
   if (op >= HS_OP_BLOCK_SCORE_BWD) {
+    if (p->doc_bounds_device)
+      return fail(HS_ERR_UNSUPPORTED, "gradients take host document bounds");
     const int kop = (op == HS_OP_SWA_BWD || op == HS_OP_SWA_BWD_STORE_DS) ? hs::kSwa
                     : op == HS_OP_SPARSE_GATHER_BWD                       ? hs::kGather
                                                                           : hs::kScore;
@@ -460,16 +507,17 @@ hs_status hs_block_score_fwd(const hs_problem* p, const void* q, const void* kv,
 
 hs_status hs_block_score_topk_fwd(const hs_problem* p, const void* q, const void* kv,
                                   const float* sink, int32_t top_k, void* out, float* lse,
-                                  float* block_logit, int32_t* block_idx, void* ws,
-                                  size_t ws_bytes, void* stream) {
+                                  float* block_logit, int32_t* block_idx, float* block_prob,
+                                  void* ws, size_t ws_bytes, void* stream) {
   return launch_attn(HS_OP_BLOCK_SCORE, p, q, kv, sink, nullptr, 0, 0, out, lse, block_logit, ws,
-                     ws_bytes, stream, block_idx, top_k);
+                     ws_bytes, stream, block_idx, top_k, block_prob);
 }
 
 hs_status hs_swa_sparse_fwd(const hs_problem* p, const void* q, const void* kv, const float* sink,
                             int32_t window, const int32_t* block_idx, int32_t top_k, void* out_swa,
-                            float* lse_swa, void* out_sparse, float* lse_sparse, void* ws,
-                            size_t ws_bytes, void* stream) {
+                            float* lse_swa, void* out_sparse, float* lse_sparse,
+                            const float* gate_swa, const float* gate_sparse, void* out_mix,
+                            void* ws, size_t ws_bytes, void* stream) {
   hs::Geom g;
   hs_status st = prepare(p, g);
   if (st != HS_OK) return st;
@@ -483,6 +531,10 @@ hs_status hs_swa_sparse_fwd(const hs_problem* p, const void* q, const void* kv, 
   if (window < 1) return fail(HS_ERR_INVALID_ARG, "window must be >= 1 (got %d)", window);
   if (sink && reinterpret_cast<uintptr_t>(sink) % 4 != 0)
     return fail(HS_ERR_INVALID_ARG, "sink is not 4-byte aligned");
+  const bool mix = gate_swa || gate_sparse || out_mix;
+  if (mix && ((st = check_ptr(gate_swa, "gate_swa", 4)) || (st = check_ptr(gate_sparse, "gate_sparse", 4)) ||
+              (st = check_ptr(out_mix, "out_mix"))))
+    return st;
   // One pass over both branches on the in-place bf16 path when neither splits
   // its key range; otherwise the two operations, one after the other.
   const bool one_pass = p->dtype == HS_BF16 && !p->page_table && !p->kv_lens_device &&
@@ -492,8 +544,19 @@ hs_status hs_swa_sparse_fwd(const hs_problem* p, const void* q, const void* kv, 
     st = launch_attn(HS_OP_SWA, p, q, kv, sink, nullptr, 0, window, out_swa, lse_swa, nullptr, ws,
                      ws_bytes, stream);
     if (st != HS_OK) return st;
-    return launch_attn(HS_OP_SPARSE_GATHER, p, q, kv, sink, block_idx, top_k, 0, out_sparse,
-                       lse_sparse, nullptr, ws, ws_bytes, stream);
+    st = launch_attn(HS_OP_SPARSE_GATHER, p, q, kv, sink, block_idx, top_k, 0, out_sparse,
+                     lse_sparse, nullptr, ws, ws_bytes, stream);
+    if (st != HS_OK || !mix) return st;
+    hs::MixArgs m;
+    m.a = out_swa;
+    m.b = out_sparse;
+    m.ga = gate_swa;
+    m.gb = gate_sparse;
+    m.out = out_mix;
+    m.rows = (long long)g.B * g.Sq * g.H;
+    m.dv = g.Dv;
+    m.bf16 = p->dtype == HS_BF16 ? 1 : 0;
+    return hip_status(hs::mix_launch(m, static_cast<hipStream_t>(stream)), "mix launch");
   }
   if (g.Sq * g.B == 0) return HS_OK;
   hs::AttnArgs a;
@@ -505,6 +568,9 @@ hs_status hs_swa_sparse_fwd(const hs_problem* p, const void* q, const void* kv, 
   a.lse = lse_sparse;
   a.out2 = static_cast<__bf16*>(out_swa);
   a.lse2 = lse_swa;
+  a.gate_a = gate_swa;
+  a.gate_b = gate_sparse;
+  a.out_mix = static_cast<__bf16*>(out_mix);
   a.block_idx = block_idx;
   a.top_k = top_k;
   a.window = window;
@@ -548,27 +614,28 @@ hs_status hs_topk_blocks(const hs_problem* p, const float* block_logit, int32_t 
 }
 
 hs_status hs_block_score_bwd(const hs_problem* p, const void* q, const void* kv, const float* sink,
-                             const void* out, const float* lse, const void* dout, float* dq,
-                             float* dkv, float* dsink, void* ws, size_t ws_bytes, void* stream) {
-  return launch_bwd(HS_OP_BLOCK_SCORE, p, q, kv, sink, nullptr, 0, 0, out, lse, dout, dq, dkv,
-                    dsink, ws, ws_bytes, stream);
+                             const void* out, const float* lse, const void* dout,
+                             const float* dlse, float* dq, float* dkv, float* dsink, void* ws,
+                             size_t ws_bytes, void* stream) {
+  return launch_bwd(HS_OP_BLOCK_SCORE, p, q, kv, sink, nullptr, 0, 0, out, lse, dout, dlse, dq,
+                    dkv, dsink, ws, ws_bytes, stream);
 }
 
 hs_status hs_sparse_gather_bwd(const hs_problem* p, const void* q, const void* kv,
                                const float* sink, const int32_t* block_idx, int32_t top_k,
-                               const void* out, const float* lse, const void* dout, float* dq,
-                               float* dkv, float* dsink, void* ws, size_t ws_bytes,
-                               void* stream) {
-  return launch_bwd(HS_OP_SPARSE_GATHER, p, q, kv, sink, block_idx, top_k, 0, out, lse, dout, dq,
-                    dkv, dsink, ws, ws_bytes, stream);
+                               const void* out, const float* lse, const void* dout,
+                               const float* dlse, float* dq, float* dkv, float* dsink, void* ws,
+                               size_t ws_bytes, void* stream) {
+  return launch_bwd(HS_OP_SPARSE_GATHER, p, q, kv, sink, block_idx, top_k, 0, out, lse, dout,
+                    dlse, dq, dkv, dsink, ws, ws_bytes, stream);
 }
 
 hs_status hs_swa_bwd(const hs_problem* p, const void* q, const void* kv, const float* sink,
                      int32_t window, const void* out, const float* lse, const void* dout,
-                     float* dq, float* dkv, float* dsink, void* ws, size_t ws_bytes,
-                     void* stream) {
-  return launch_bwd(HS_OP_SWA, p, q, kv, sink, nullptr, 0, window, out, lse, dout, dq, dkv, dsink,
-                    ws, ws_bytes, stream);
+                     const float* dlse, float* dq, float* dkv, float* dsink, void* ws,
+                     size_t ws_bytes, void* stream) {
+  return launch_bwd(HS_OP_SWA, p, q, kv, sink, nullptr, 0, window, out, lse, dout, dlse, dq, dkv,
+                    dsink, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -174,10 +174,11 @@ void attn_bf16_kernel(AttnArgs a) {
   const int r = g.Sq - 1 - (w % g.Sq);
   const size_t row = (size_t)b * g.Sq + r;
 
-  const RowRange rr = row_range<PAGED>(g, OP == kSwaSparse ? kGather : OP, b, r, a.window);
-  const int nb_b = nb_of_entry<PAGED>(g, b);
+  const RowRange rr = row_range<true>(g, OP == kSwaSparse ? kGather : OP, b, r, a.window);
+  const int nb_b = nb_of_entry<true>(g, b);
+  const Doc rdoc = rr.doc;   // every tile of the row lies in its document
   // window-and-sparse: the window branch's range; its n_w tiles come first
-  const RowRange rw = OP == kSwaSparse ? row_range<PAGED>(g, kSwa, b, r, a.window) : rr;
+  const RowRange rw = OP == kSwaSparse ? row_range<true>(g, kSwa, b, r, a.window) : rr;
   const int n_w = OP == kSwaSparse ? rw.j_last - rw.j_first + 1 : 0;
 
   // Tile sequence: a block range, or the listed blocks that intersect the
@@ -190,8 +191,8 @@ void attn_bf16_kernel(AttnArgs a) {
     bool ok = false;
     if (lane < a.top_k) {
       j = a.block_idx[row * a.top_k + lane];
-      if (j >= 0 && j < nb_b) {
-        const Blk bk = block_rows<PAGED>(g, b, j);
+      if (j >= 0 && j < nb_b && block_in_doc(g, rdoc, j)) {
+        const Blk bk = block_rows_in(g, rdoc, j);
         ok = !(bk.start > rr.hi || bk.start + bk.len - 1 < rr.lo);
       }
     }
@@ -239,7 +240,7 @@ void attn_bf16_kernel(AttnArgs a) {
   };
   if (t_begin < t_end) {
     const int j0 = tile_block(t_begin);
-    const Blk b0 = block_rows<PAGED>(g, b, j0);
+    const Blk b0 = block_rows_in(g, rdoc, j0);
     stage_tile(buf_a, block_base(j0), PAGED ? 0 : b0.start, b0.len, wave, lane);
   }
 
@@ -315,7 +316,7 @@ void attn_bf16_kernel(AttnArgs a) {
       }
     }
     const int j = tile_block(t);
-    const Blk blk = block_rows<PAGED>(g, b, j);
+    const Blk blk = block_rows_in(g, rdoc, j);
     const int rlo = (OP == kSwaSparse && t < n_w) ? rw.lo : rr.lo;
     const int rhi = (OP == kSwaSparse && t < n_w) ? rw.hi : rr.hi;
     const int klo = rlo - blk.start, khi = min(rhi - blk.start, blk.len - 1);
@@ -334,7 +335,7 @@ void attn_bf16_kernel(AttnArgs a) {
     const bool has_next = t + 1 < t_end;
     char* cp_dst = nxt + wave * 1024;
     const int jn = has_next ? tile_block(t + 1) : j;
-    const Blk nb = has_next ? block_rows<PAGED>(g, b, jn) : blk;
+    const Blk nb = has_next ? block_rows_in(g, rdoc, jn) : blk;
     const bf16* nbase = block_base(jn);
     const int nst = PAGED ? 0 : nb.start;
     const int ka = min(8 * wave + (lane >> 3), nb.len - 1);
@@ -558,6 +559,25 @@ void attn_bf16_kernel(AttnArgs a) {
     }
     if (grp == 0)
       a.lse[row * H + head] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
+    if constexpr (OP == kSwaSparse) {
+      // Gated sum of the two branches from their stored bf16 values (this lane
+      // wrote both rows of columns it now reads).
+      if (a.out_mix != nullptr) {
+        const float ga = a.gate_a[row * H + head], gb = a.gate_b[row * H + head];
+        const bf16* sw = a.out2 + (row * H + head) * DV + 4 * grp;
+        const bf16* sp = a.out + (row * H + head) * DV + 4 * grp;
+        bf16* mp = a.out_mix + (row * H + head) * DV + 4 * grp;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+          const bf16x4 x = *(const bf16x4*)(sw + 16 * db);
+          const bf16x4 y = *(const bf16x4*)(sp + 16 * db);
+          bf16x4 m;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) m[e] = (bf16)gated_mix(ga, (float)x[e], gb, (float)y[e]);
+          *(bf16x4*)(mp + 16 * db) = m;
+        }
+      }
+    }
   } else {
     // Unnormalised partial: O (fp32), reference max (log2) and denominator.
     const size_t slot = (size_t)w * a.nsplit + split;
@@ -579,8 +599,30 @@ __global__ __launch_bounds__(64) void merge_bf16_kernel(AttnArgs a) {
   using namespace mla;
   if constexpr (PER > 0) {
     if ((int)blockIdx.x >= a.g.B * a.g.Sq * H) {
-      topk_row<PER>(a.g, a.block_logit, a.topk_idx, a.topk_k, blockIdx.x - a.g.B * a.g.Sq * H,
-                    threadIdx.x);
+      const int rowi = blockIdx.x - a.g.B * a.g.Sq * H;
+      float lmax2 = 0.f;
+      if (a.topk_prob != nullptr) {
+        // the row's per-head lse in log2 units, formed from the partials as
+        // the merge waves of this launch form it (lane = head)
+        const int bb = rowi / a.g.Sq, rq = rowi % a.g.Sq;
+        const int item = bb * a.g.Sq + (a.g.Sq - 1 - rq);
+        const int head = threadIdx.x;
+        float M = -INFINITY;
+        for (int s = 0; s < a.nsplit; ++s) {
+          const size_t slot = (size_t)item * a.nsplit + s;
+          if (a.ws_ml[(slot * H + head) * 2 + 1] > 0.f) M = fmaxf(M, a.ws_ml[(slot * H + head) * 2]);
+        }
+        float L = 0.f;
+        if (M > -INFINITY)
+          for (int s = 0; s < a.nsplit; ++s) {
+            const size_t slot = (size_t)item * a.nsplit + s;
+            const float l = a.ws_ml[(slot * H + head) * 2 + 1];
+            if (l > 0.f) L += l * fast_exp2(a.ws_ml[(slot * H + head) * 2] - M);
+          }
+        lmax2 = wave_max_f(L > 0.f ? M + fast_log2(L) : -INFINITY);
+      }
+      topk_row<PER>(a.g, a.block_logit, a.topk_idx, a.topk_k, rowi, threadIdx.x, a.topk_prob,
+                    lmax2);
       return;
     }
   }
@@ -672,6 +714,8 @@ int attn_bf16_launch(int op, const AttnArgs& a, hipStream_t stream) {
     t.block_logit = a.block_logit;
     t.block_idx = a.topk_idx;
     t.top_k = a.topk_k;
+    t.lse = a.lse;
+    t.block_prob = a.topk_prob;
     t.g = a.g;
     const int err = (int)hipGetLastError();
     if (err != 0) return err;

@@ -54,6 +54,7 @@
 #include "hs_common.h"
 #include "hs_gfx950.h"
 #include "hs_bwd_args.h"
+#include "hs_bwd_plan.h"
 
 namespace hs {
 
@@ -106,82 +107,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Host-and-device forms of the block helpers of hs_common.h (the workspace
-// plan runs the same arithmetic on the host).
-__host__ __device__ inline int blocks_of_entry(const Geom& g, int b) {
-  if (g.n_docs == 0) return (g.kv_len[b] + g.BS - 1) / g.BS;
-  return g.doc_blk0[g.n_docs];
-}
-
-__host__ __device__ inline Blk block_span(const Geom& g, int b, int j) {
-  int s, e;
-  if (g.n_docs == 0) {
-    s = j * g.BS;
-    e = g.kv_len[b];
-  } else {
-    int lo = 0, hi = g.n_docs - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (g.doc_blk0[mid] <= j) lo = mid; else hi = mid - 1;
-    }
-    s = g.doc_start[lo] + (j - g.doc_blk0[lo]) * g.BS;
-    e = g.doc_end[lo];
-  }
-  return Blk{s, e - s < g.BS ? e - s : g.BS};
-}
-
-// Whether row rr of entry b gathers block j (the forward's tile rule: a valid
-// id whose block meets the row's allowed key range).
-__host__ __device__ inline bool gather_hit(const Geom& g, int b, int nb_b, const RowRange& rr,
-                                           int j) {
-  if (j < 0 || j >= nb_b) return false;
-  const Blk bk = block_span(g, b, j);
-  return !(bk.start > rr.hi || bk.start + bk.len - 1 < rr.lo);
-}
-
-// Rows of entry b whose allowed keys meet block j, for the causal and window
-// operations: a contiguous range [*first, *first + n) of row indices.
-__host__ __device__ inline int block_row_range(const Geom& g, int op, int b, int j, int window,
-                                               int* first) {
-  *first = 0;
-  if (j >= blocks_of_entry(g, b)) return 0;
-  const int L = g.kv_len[b];
-  const Blk blk = block_span(g, b, j);
-  const Doc d = doc_of_pos(g, b, blk.start);
-  const int p_lo = blk.start > L - g.Sq ? blk.start : L - g.Sq;
-  int p_hi = d.end - 1;
-  if (op == kSwa) {
-    const long reach = (long)blk.start + blk.len - 1 + window - 1;
-    if (reach < p_hi) p_hi = (int)reach;
-  }
-  if (p_hi < p_lo) return 0;
-  *first = p_lo - (L - g.Sq);
-  return p_hi - p_lo + 1;
-}
-
-// Sum over x = 0 .. n-1 of (x / bs + 1): the causal key blocks of the rows
-// at positions 0 .. n-1 of a document that starts at position 0.
-__host__ __device__ inline long long causal_tiles_upto(long long n, int bs) {
-  if (n <= 0) return 0;
-  const long long m = n / bs;
-  return n + (long long)bs * m * (m - 1) / 2 + (n - (long long)bs * m) * m;
-}
-
-// Causal key blocks of rows 0 .. r-1 of entry b: a row at position p of a
-// document starting at s walks (p - s) / bs + 1 blocks. Documents tile
-// [0, Sq) with rows at their positions; without documents the rows of entry
-// b sit at kv_len - Sq + r.
-__host__ __device__ inline long long causal_tiles_before(const Geom& g, int b, int r) {
-  if (g.n_docs == 0) {
-    const long long p0 = g.kv_len[b] - g.Sq;
-    return causal_tiles_upto(p0 + r, g.BS) - causal_tiles_upto(p0, g.BS);
-  }
-  long long t = 0;
-  for (int d = 0; d < g.n_docs && g.doc_start[d] < r; ++d)
-    t += causal_tiles_upto((g.doc_end[d] < r ? g.doc_end[d] : r) - g.doc_start[d], g.BS);
-  return t;
-}
-
 // ---------------------------------------------------------------------------
 // Dsum and the sink-gradient partials.
 // ---------------------------------------------------------------------------
@@ -225,7 +150,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
     const int h = p % H;
     if (row >= rows) break;
     const size_t off = (row * H + h) * (size_t)Dv;
-    const float d = wave_sum(dot_row<T>(out + off, dout + off, Dv, lane));
+    // An incoming gradient of lse enters every later formula as D - dlse.
+    float d = wave_sum(dot_row<T>(out + off, dout + off, Dv, lane));
+    if (a.dlse != nullptr) d -= a.dlse[row * H + h];
     if (lane == 0) {
       a.dsum[row * H + h] = d;
       if (a.sink != nullptr) {
@@ -297,27 +224,6 @@ __global__ __launch_bounds__(256) void bwd_gscan_kernel(BwdArgs a) {
     run += v;
   }
   a.g_total[f] = run;
-}
-
-// Rows of work item (b, c, j): a range [*first, *first + n) of row indices,
-// or (gather) a range of positions in block j's row list.
-__host__ __device__ inline int item_rows(const Geom& g, int op, int b, int c, int j, int window,
-                                         int R, int T, const int* g_cnt, const int* g_total,
-                                         const int* g_off, int* first) {
-  if (op == kGather) {
-    const int f = b * g.NB + j;
-    const int t0 = c * (R / 64), t1 = (c + 1) * (R / 64);
-    const int s0 = g_cnt[((size_t)b * T + t0) * g.NB + j];
-    const int s1 = t1 < T ? g_cnt[((size_t)b * T + t1) * g.NB + j] : g_total[f];
-    *first = g_off[f] + s0;
-    return s1 - s0;
-  }
-  int bf;
-  const int n = block_row_range(g, op, b, j, window, &bf);
-  const int lo = bf > c * R ? bf : c * R;
-  const int hi = bf + n < (c + 1) * R ? bf + n : (c + 1) * R;
-  *first = lo;
-  return hi > lo ? hi - lo : 0;
 }
 
 // Work items of the key-block gradient (one workgroup): the gather's list
@@ -1176,8 +1082,6 @@ __global__ __launch_bounds__(256) void bwd_reduce_f32_kernel(BwdArgs a) {
   }
 }
 
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
 template <int OP>
 void launch_bf16(const BwdArgs& a, hipStream_t s) {
   const Geom& g = a.g;
@@ -1223,87 +1127,6 @@ void launch_f32(const BwdArgs& a, hipStream_t s) {
 }
 
 }  // namespace
-
-BwdLayout bwd_layout(const Geom& g, int op, int top_k, int window, bool store_ds) {
-  BwdLayout L;
-  std::memset(&L, 0, sizeof(L));
-  const size_t rows = (size_t)g.B * g.Sq;
-  L.rows_per_pre = (int)std::max<size_t>(8, (rows + 2047) / 2048);
-  L.n_pre = (int)((rows + L.rows_per_pre - 1) / L.rows_per_pre);
-  size_t off = 0;
-  L.dsum = off;
-  off = align256(off + rows * g.H * sizeof(float));
-  L.sink_part = off;
-  off = align256(off + (size_t)L.n_pre * g.H * sizeof(float));
-  {
-    L.row_tiles = (g.Sq + 63) / 64;
-    // Row chunk R: the largest power of two from 512 down to 64 that still
-    // gives about 1024 work items (four per compute unit). At R = 512 the Q
-    // and dout rows of one chunk (71 MB) stay in the 256 MB last-level cache
-    // while the chunk's items run (1024 and 256 measured within 2 % of it).
-    // Longer sequences double R until at most 32768 items remain, which
-    // bounds the partials at 32768 x 64 x Dk fp32 (4.8 GB for Dk = 576).
-    auto items_for = [&](int R) -> long {
-      const int C = (g.Sq + R - 1) / R;
-      long it = 0;
-      const int oc = op == kSwa ? kSwa : kScore;  // gather rows lie in the causal ones
-      for (int b = 0; b < g.B; ++b)
-        for (int c = 0; c < C; ++c)
-          for (int j = 0; j < g.NB; ++j) {
-            int first;
-            it += item_rows(g, oc, b, c, j, window, R, 0, nullptr, nullptr, nullptr, &first) > 0;
-          }
-      return it;
-    };
-    int R = 512;
-    while (R > 64 && items_for(R) < 1024) R >>= 1;
-    while (R < g.Sq && items_for(R) > 32768) R <<= 1;
-    L.chunk_rows = R;
-    L.n_chunks = (g.Sq + R - 1) / R;
-    L.items = (int)items_for(R);
-    const size_t F = (size_t)g.B * L.n_chunks * g.NB;
-    L.first = off;
-    off = align256(off + F * sizeof(int));
-    L.nrows = off;
-    off = align256(off + F * sizeof(int));
-    L.pre = off;
-    off = align256(off + (F + 1) * sizeof(int));
-    if (op == kGather) {
-      const size_t FB = (size_t)g.B * g.NB;
-      L.cnt = off;
-      off = align256(off + (size_t)g.B * L.row_tiles * g.NB * sizeof(int));
-      L.total_g = off;
-      off = align256(off + FB * sizeof(int));
-      L.off_g = off;
-      off = align256(off + FB * sizeof(int));
-      L.rows = off;
-      off = align256(off + rows * std::max(top_k, 1) * sizeof(int));
-    }
-    L.part = off;
-    off = align256(off + (size_t)L.items * 64 * g.Dk * sizeof(float));
-  }
-  if (store_ds && op != kGather) {
-    // 64 heads x 64 keys of bf16 per (row, block of its range); a window of
-    // W keys meets at most ceil((W - 1) / BS) + 1 blocks
-    long long tiles = 0;
-    if (op == kScore) {
-      for (int b = 0; b < g.B; ++b) tiles += causal_tiles_before(g, b, g.Sq);
-    } else {
-      const long long per = std::min<long long>((window - 1 + (long long)g.BS - 1) / g.BS + 1, g.NB);
-      L.ds_stride = (int)per;
-      tiles = (long long)g.B * g.Sq * per;
-    }
-    L.store_ds = true;
-    L.ds_entry = off;
-    off = align256(off + (size_t)(g.B + 1) * sizeof(long long));
-    L.ds_dummy = off;
-    off = align256(off + 4096);
-    L.ds_tiles = off;
-    off = align256(off + (size_t)tiles * 64 * 64 * sizeof(bf16));
-  }
-  L.total = off;
-  return L;
-}
 
 int bwd_launch(int op, const BwdArgs& a, bool is_bf16, hipStream_t s) {
   if (is_bf16) hipLaunchKernelGGL(bwd_pre_kernel<bf16>, dim3(a.n_pre), dim3(256), 0, s, a);

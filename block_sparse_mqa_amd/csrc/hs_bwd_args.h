@@ -17,6 +17,7 @@ struct BwdArgs {
   const void* out;           // [B, Sq, H, Dv] dtype (forward output)
   const float* lse;          // [B, Sq, H] (forward output, natural log)
   const void* dout;          // [B, Sq, H, Dv] dtype
+  const float* dlse;         // [B, Sq, H] incoming gradient of lse, or nullptr
   const int* block_idx;      // gather: [B, Sq, top_k]
   int top_k;
   int window;

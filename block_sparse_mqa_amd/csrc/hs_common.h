@@ -28,8 +28,11 @@ struct Geom {
   int doc_start[kMaxDocs];
   int doc_end[kMaxDocs];
   int doc_blk0[kMaxDocs + 1];    // first global block id of each document
-  const int* kv_len_dev;         // device [B] valid KV rows (paged decode), or nullptr:
-                                 // then kv_len holds the capacity the host planned with
+  const int* kv_len_dev;         // device [B] valid KV rows, or nullptr: then kv_len
+                                 // holds the capacity the host planned with
+  const int* doc_dev;            // device [n_docs + 1] cumulative document starts, or
+                                 // nullptr; n_docs is then the capacity and the host
+                                 // arrays above are unused
 };
 
 // Valid KV rows of entry b. Launches given device lengths (DEV and
@@ -51,9 +54,38 @@ struct Blk {
   int start, len;
 };
 
-// Document holding position p of entry b.
+#if defined(__HIP_DEVICE_COMPILE__)
+// Document holding position p, from the device table of cumulative starts
+// (at most 64 documents: lane l holds document l). Every lane of the wave must
+// take part, with the same p. The holder is the last document starting at or
+// before p; it cannot be empty, since the next start is past p. Its first
+// block id is the sum of the block counts of the documents before it. Bounds
+// are clamped into [0, Sq], so a malformed table cannot send reads outside
+// the sequence.
+__device__ inline Doc doc_of_pos_wave(const Geom& g, int p) {
+  const int l = __lane_id();
+  const int nd = g.n_docs;
+  int s = 0x7fffffff, e = 0x7fffffff, nb = 0;
+  if (l < nd) {
+    s = min(max(g.doc_dev[l], 0), g.Sq);
+    e = min(max(g.doc_dev[l + 1], s), g.Sq);
+    nb = (e - s + g.BS - 1) / g.BS;
+  }
+  const unsigned long long m = __ballot(l < nd && s <= p);
+  const int d = m ? 63 - __clzll((long long)m) : 0;
+  int before = l < d ? nb : 0;
+  for (int o = 32; o >= 1; o >>= 1) before += __shfl_xor(before, o);
+  return Doc{__builtin_amdgcn_readlane(s, d), __builtin_amdgcn_readlane(e, d), before};
+}
+#endif
+
+// Document holding position p of entry b. With a device document table (DEV
+// launches only) every lane of the wave must call it with the same p.
 template <bool DEV = false>
 __host__ __device__ inline Doc doc_of_pos(const Geom& g, int b, int p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  if (DEV && g.doc_dev != nullptr) return doc_of_pos_wave(g, p);
+#endif
   if (g.n_docs == 0) return Doc{0, kv_len_of<DEV>(g, b), 0};
   int lo = 0, hi = g.n_docs - 1;
   while (lo < hi) {
@@ -63,11 +95,27 @@ __host__ __device__ inline Doc doc_of_pos(const Geom& g, int b, int p) {
   return Doc{g.doc_start[lo], g.doc_end[lo], g.doc_blk0[lo]};
 }
 
-// Number of key blocks of entry b.
+// Number of key blocks of entry b (with a device document table, the
+// capacity NB).
 template <bool DEV = false>
 __device__ __forceinline__ int nb_of_entry(const Geom& g, int b) {
   if (g.n_docs == 0) return (kv_len_of<DEV>(g, b) + g.BS - 1) / g.BS;
+  if (DEV && g.doc_dev != nullptr) return g.NB;
   return g.doc_blk0[g.n_docs];
+}
+
+// Rows [start, start + len) of block j of document d (j must be one of d's
+// blocks; without documents d is the whole entry). A row only ever attends
+// keys of its own document, so loops over a row's tiles use its document and
+// need no lookup.
+__device__ __forceinline__ Blk block_rows_in(const Geom& g, const Doc& d, int j) {
+  const int s = d.start + (j - d.blk0) * g.BS;
+  return Blk{s, min(g.BS, d.end - s)};
+}
+
+// Whether block j is one of document d's.
+__device__ __forceinline__ bool block_in_doc(const Geom& g, const Doc& d, int j) {
+  return j >= d.blk0 && j < d.blk0 + (d.end - d.start + g.BS - 1) / g.BS;
 }
 
 // Rows [start, start + len) of block j of entry b (j must be valid).
@@ -99,6 +147,7 @@ enum Op { kScore = 0, kGather = 1, kSwa = 2, kSwaSparse = 3 };
 
 struct RowRange {
   int pos, lo, hi, j_first, j_last;
+  Doc doc;   // the row's document (the whole entry without documents)
 };
 
 template <bool DEV = false>
@@ -106,6 +155,7 @@ __host__ __device__ inline RowRange row_range(const Geom& g, int op, int b, int 
   RowRange rr;
   rr.pos = kv_len_of<DEV>(g, b) - g.Sq + r;
   Doc d = doc_of_pos<DEV>(g, b, rr.pos);
+  rr.doc = d;
   rr.lo = d.start;
   rr.hi = rr.pos;
   if (op == kSwa && rr.pos - window + 1 > rr.lo) rr.lo = rr.pos - window + 1;

@@ -15,7 +15,13 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   const int lane = threadIdx.x & 63;
   const int rowi = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (rowi >= a.g.B * a.g.Sq) return;
-  topk_row<PER>(a.g, a.block_logit, a.block_idx, a.top_k, rowi, lane);
+  float lmax2 = 0.f;
+  if (a.block_prob != nullptr) {
+    float m = -INFINITY;
+    for (int h = lane; h < a.g.H; h += 64) m = fmaxf(m, a.lse[(size_t)rowi * a.g.H + h]);
+    lmax2 = wave_max_f(m) * kLog2e;
+  }
+  topk_row<PER>(a.g, a.block_logit, a.block_idx, a.top_k, rowi, lane, a.block_prob, lmax2);
 }
 
 int topk_launch(const TopkArgs& a, hipStream_t stream) {

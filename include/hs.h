@@ -53,13 +53,28 @@
  * logical. Paged KV needs HS_BF16, no documents, and
  * L_b <= max_pages * block_size for every entry (checked); the page ids must
  * lie in the pool (device data, not checked).
- * Device-resident lengths (paged KV only): with kv_lens_device set, L_b is
- * read from device memory when the kernels run, so one recorded launch (for
- * instance a captured HIP graph) serves changing cache lengths. The host
- * then plans with the capacity seqlen_kv (<= max_pages * block_size,
- * checked): hs_num_blocks and hs_workspace_size use it, block_logit has
+ * Device-resident lengths (bf16, in-place or paged KV, no documents): with
+ * kv_lens_device set, L_b is read from device memory when the kernels run,
+ * so one recorded launch (for instance a captured HIP graph) serves changing
+ * cache lengths. The host then plans with the capacity seqlen_kv (the row
+ * stride of an in-place kv; <= max_pages * block_size when paged, checked):
+ * hs_num_blocks and hs_workspace_size use it, block_logit has
  * ceil(seqlen_kv / block_size) columns (-inf past each entry's blocks), and
  * seqlen_q <= L_b <= seqlen_kv must hold (device data, not checked).
+ * Device-resident document bounds (bf16 forward calls; same pages, packed
+ * prefill replayed from a recorded launch): with doc_bounds_device set, the
+ * packing is read from device memory when the kernels run, as cumulative
+ * starts cu[0..n_docs] (document d is rows [cu[d], cu[d+1])), and n_docs is
+ * the capacity: a packing of fewer documents pads cu with empty documents
+ * (equal consecutive bounds; anywhere). cu[0] = 0, cu[n_docs] = seqlen_q and
+ * cu non-decreasing must hold (device data, not checked; kernels clamp every
+ * bound into [0, seqlen_q], so a bad table gives wrong results, not stray
+ * reads). The host plans with the capacity: hs_num_blocks returns
+ * ceil(seqlen / block_size) + n_docs - 1, the most blocks any such packing
+ * has; block ids are numbered in document order and block_logit columns past
+ * the packing's last block are -inf. Needs B == 1, seqlen_q == seqlen_kv, no
+ * kv_lens, kv_lens_device or page_table, and doc_start/doc_end NULL. Such
+ * launches never split the key range. The gradient calls reject it.
  * Streams: `stream` is a hipStream_t passed as void* (NULL = default stream).
  * Calls enqueue work and return without synchronising; a fault inside a
  * kernel surfaces at the caller's next synchronisation.
@@ -117,16 +132,21 @@ typedef struct {
   int32_t n_kv_lens;      /* must equal B when kv_lens is set (B <= 256)        */
   const int32_t* doc_start; /* HOST [n_docs] packed documents, or NULL          */
   const int32_t* doc_end;   /* HOST [n_docs]                                     */
-  int32_t n_docs;         /* 0, or 1..64 with B == 1 and kv_lens == NULL        */
+  int32_t n_docs;         /* 0, or 1..64 with B == 1 and kv_lens == NULL (with  */
+                          /* doc_bounds_device: the capacity)                   */
   const int32_t* page_table; /* DEVICE [B, max_pages] int32, or NULL: paged KV  */
   int32_t max_pages;      /* pages per entry in page_table (paged KV only)      */
   const int32_t* kv_lens_device; /* DEVICE [B] int32 valid KV lengths, read at  */
-                          /* run time (paged KV only; kv_lens must be NULL)     */
+                          /* run time (bf16; kv_lens must be NULL)              */
+  const int32_t* doc_bounds_device; /* DEVICE [n_docs + 1] int32 cumulative    */
+                          /* document starts, read at run time (bf16 forward;  */
+                          /* n_docs = capacity; doc_start/doc_end NULL)         */
 } hs_problem;
 
 /* Number of key blocks NB = columns of block_logit: the largest, over the
- * batch, of sum over documents of ceil(L_d / block_size). Returns NB >= 1, or
- * a negative hs_status if the problem is invalid. */
+ * batch, of sum over documents of ceil(L_d / block_size) (with
+ * doc_bounds_device, the capacity ceil(seqlen / block_size) + n_docs - 1).
+ * Returns NB >= 1, or a negative hs_status if the problem is invalid. */
 int32_t hs_num_blocks(const hs_problem* p);
 
 /* Workspace bytes the given operation needs for this problem (0 when it
@@ -173,11 +193,18 @@ hs_status hs_topk_blocks(const hs_problem* p, const float* block_logit, int32_t 
  * that merges the partial results, once every block score of the row is
  * final, so the call costs no separate launch; otherwise the top-k kernel
  * follows the attention kernel on the stream. 1 <= top_k <= 64, at most 4096
- * blocks; ws/ws_bytes as for hs_block_score_fwd. */
+ * blocks; ws/ws_bytes as for hs_block_score_fwd.
+ * block_prob (optional, NULL = not written) [B, Sq, NB] float32, 4-byte
+ * aligned: the normalised block scores (same page, per-file row for
+ * pipeline.py: the probabilities are recovered as exp(block_logit - lse)).
+ * With one lse per head, the row's normaliser is its largest per-head lse:
+ *   block_prob[b,r,j] = exp(block_logit[b,r,j] - max_h lse[b,r,h]),
+ * 0 where block_logit is -inf. Every value lies in [0, 1]; with one head the
+ * row sums to the mass the attention puts on keys (1 - exp(sink - lse)). */
 hs_status hs_block_score_topk_fwd(const hs_problem* p, const void* q, const void* kv,
                                   const float* sink, int32_t top_k, void* out, float* lse,
-                                  float* block_logit, int32_t* block_idx, void* ws,
-                                  size_t ws_bytes, void* stream);
+                                  float* block_logit, int32_t* block_idx, float* block_prob,
+                                  void* ws, size_t ws_bytes, void* stream);
 
 /* Block-sparse gather attention (same page, "Core", block-sparse DSA gather
  * bullet; per-file table row for block_sparse_mqa_dsa.py): attention with
@@ -203,19 +230,29 @@ hs_status hs_swa_fwd(const hs_problem* p, const void* q, const void* kv, const f
  * transformer_layer.py: KV shared across layers). One call returns the two
  * branch outputs separately, exactly as hs_swa_fwd (out_swa, lse_swa) and
  * hs_sparse_gather_fwd (out_sparse, lse_sparse) would for the same
- * arguments; how a layer combines them is not stated on the pages and is
- * left to the caller. On the bf16 path with an in-place cache, whenever
- * neither branch splits its key range across workgroups (few rows with long
- * ranges do, e.g. single-token decode or a short chunk over a long cache),
- * one launch walks each row's window blocks and then its selected blocks,
- * loading the row's queries once; otherwise the two operations run one
- * after the other. top_k < 1 and window < 1 are HS_ERR_INVALID_ARG, top_k >
- * 64 is HS_ERR_UNSUPPORTED (as for hs_sparse_gather_fwd). Workspace:
- * hs_workspace_size with HS_OP_SWA_SPARSE. */
+ * arguments. On the bf16 path with an in-place cache, whenever neither
+ * branch splits its key range across workgroups (few rows with long ranges
+ * do, e.g. single-token decode or a short chunk over a long cache), one
+ * launch walks each row's window blocks and then its selected blocks,
+ * loading the row's queries once; otherwise the two operations run one after
+ * the other. top_k < 1 and window < 1 are HS_ERR_INVALID_ARG, top_k > 64 is
+ * HS_ERR_UNSUPPORTED (as for hs_sparse_gather_fwd). Workspace:
+ * hs_workspace_size with HS_OP_SWA_SPARSE.
+ * Branch combination (optional; all three pointers or none): the pages do
+ * not state how a layer combines its branches; the method is NSA-style
+ * (same page, section "What"), and NSA combines its branches by a gated sum
+ * with gates the model computes per token and head. With gate_swa and
+ * gate_sparse ([B, Sq, H] float32, 4-byte aligned) the call also writes
+ *   out_mix[b,r,h,:] = gate_swa[b,r,h] * out_swa[b,r,h,:]
+ *                    + gate_sparse[b,r,h] * out_sparse[b,r,h,:]
+ * ([B, Sq, H, Dv], dtype, 16-byte aligned), formed in float32 from the two
+ * stored outputs and rounded to dtype; the one-pass launch forms it in its
+ * epilogue, otherwise a small elementwise launch follows (same values). */
 hs_status hs_swa_sparse_fwd(const hs_problem* p, const void* q, const void* kv, const float* sink,
                             int32_t window, const int32_t* block_idx, int32_t top_k, void* out_swa,
-                            float* lse_swa, void* out_sparse, float* lse_sparse, void* ws,
-                            size_t ws_bytes, void* stream);
+                            float* lse_swa, void* out_sparse, float* lse_sparse,
+                            const float* gate_swa, const float* gate_sparse, void* out_mix,
+                            void* ws, size_t ws_bytes, void* stream);
 
 /* Gradients (page "HySparse MQA sparse attention ...", section "Core": block
  * scoring trained through its autograd layer and the analytic gradient of
@@ -229,8 +266,12 @@ hs_status hs_swa_sparse_fwd(const hs_problem* p, const void* q, const void* kv, 
  *   dsink [H] float32   = dL/dsink = -sum over rows of exp(sink - lse) *
  *                       (dout . out); NULL skips it; needs a sink.
  * out and lse are the forward's outputs for the same inputs (out: dtype,
- * [B, Sq, H, Dv]; lse: [B, Sq, H]); dout has out's layout and dtype. lse is
- * a saved statistic and takes no gradient; the block scores take none either
+ * [B, Sq, H, Dv]; lse: [B, Sq, H]); dout has out's layout and dtype. dlse
+ * (optional, NULL = zero) [B, Sq, H] float32 is an incoming gradient of lse,
+ * for losses that use it (for instance a combination of branches weighted by
+ * their log-sum-exp): the loss is then L = sum(dout * out) + sum(dlse * lse),
+ * and since d lse / d s_i is the probability P_i, every formula above holds
+ * with dout . out replaced by dout . out - dlse. The block scores take none
  * (review of PaddleFleet PR 1453, block-score PyLayer comments: the backward
  * returns gradients for q, k and v only). The workspace is mandatory:
  * hs_workspace_size with HS_OP_*_BWD and the same top_k / window, 16-byte
@@ -244,16 +285,18 @@ hs_status hs_swa_sparse_fwd(const hs_problem* p, const void* q, const void* kv, 
  * smaller HS_OP_BLOCK_SCORE_BWD workspace dq recomputes them. Both give the
  * same gradients up to the rounding of dS. */
 hs_status hs_block_score_bwd(const hs_problem* p, const void* q, const void* kv, const float* sink,
-                             const void* out, const float* lse, const void* dout, float* dq,
-                             float* dkv, float* dsink, void* ws, size_t ws_bytes, void* stream);
+                             const void* out, const float* lse, const void* dout,
+                             const float* dlse, float* dq, float* dkv, float* dsink, void* ws,
+                             size_t ws_bytes, void* stream);
 
 /* Gradients of hs_sparse_gather_fwd for the given selection (block_idx and
  * top_k as in the forward; the selection itself takes no gradient). At most
  * 4096 blocks. */
 hs_status hs_sparse_gather_bwd(const hs_problem* p, const void* q, const void* kv,
                                const float* sink, const int32_t* block_idx, int32_t top_k,
-                               const void* out, const float* lse, const void* dout, float* dq,
-                               float* dkv, float* dsink, void* ws, size_t ws_bytes, void* stream);
+                               const void* out, const float* lse, const void* dout,
+                               const float* dlse, float* dq, float* dkv, float* dsink, void* ws,
+                               size_t ws_bytes, void* stream);
 
 /* Gradients of hs_swa_fwd (review of PaddleFleet PR 1453, the windowed
  * backward comments: a sequence length that is not a multiple of the tile
@@ -264,8 +307,8 @@ hs_status hs_sparse_gather_bwd(const hs_problem* p, const void* q, const void* k
  * key-block pass stores, as for hs_block_score_bwd. */
 hs_status hs_swa_bwd(const hs_problem* p, const void* q, const void* kv, const float* sink,
                      int32_t window, const void* out, const float* lse, const void* dout,
-                     float* dq, float* dkv, float* dsink, void* ws, size_t ws_bytes,
-                     void* stream);
+                     const float* dlse, float* dq, float* dkv, float* dsink, void* ws,
+                     size_t ws_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* hs_status_string(int32_t status);

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(hs.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.hs_version() == 106
+    assert lib.hs_version() == 201
 
 
 def _mla(**kw):
@@ -91,12 +91,14 @@ def test_fused_score_topk_rejects_before_launch():
     lib = hs.load_library()
     p = _mla()
     fake = ctypes.c_void_p(4096)
-    call = lambda k, idx, prob=p: lib.hs_block_score_topk_fwd(
-        prob.ref, fake, fake, None, k, fake, fake, fake, idx, None, 0, None)
+    call = lambda k, idx, prob=p, bp=None: lib.hs_block_score_topk_fwd(
+        prob.ref, fake, fake, None, k, fake, fake, fake, idx, bp, None, 0, None)
     assert call(0, fake) == hs.HS_ERR_INVALID_ARG and b"top_k" in lib.hs_last_error()
     assert call(65, fake) == hs.HS_ERR_UNSUPPORTED
     assert call(4, None) == hs.HS_ERR_INVALID_ARG and b"block_idx is NULL" in lib.hs_last_error()
     assert call(4, ctypes.c_void_p(4098)) == hs.HS_ERR_INVALID_ARG
+    assert call(4, fake, bp=ctypes.c_void_p(4098)) == hs.HS_ERR_INVALID_ARG and \
+        b"block_prob" in lib.hs_last_error()
     # more than 4096 blocks cannot be selected from
     big = _mla(B=1, Sq=1, Skv=4097 * 64, kv_lens=[4097 * 64])
     assert call(4, fake, big) == hs.HS_ERR_UNSUPPORTED and b"4096" in lib.hs_last_error()
@@ -113,25 +115,30 @@ def test_gradient_calls_reject_before_launch():
     assert n > 0
     big = ctypes.c_size_t(n)
 
-    def score(prob=p, q=f, sink=None, dout=f, dsink=None, ws=f, nbytes=big):
-        return lib.hs_block_score_bwd(prob.ref, q, f, sink, f, f, dout, f, f, dsink, ws, nbytes,
-                                      None)
+    def score(prob=p, q=f, sink=None, dout=f, dlse=None, dsink=None, ws=f, nbytes=big):
+        return lib.hs_block_score_bwd(prob.ref, q, f, sink, f, f, dout, dlse, f, f, dsink, ws,
+                                      nbytes, None)
     assert score(q=None) == hs.HS_ERR_INVALID_ARG and b"q is NULL" in lib.hs_last_error()
     assert score(dout=ctypes.c_void_p(4100)) == hs.HS_ERR_INVALID_ARG
+    assert score(dlse=ctypes.c_void_p(4098)) == hs.HS_ERR_INVALID_ARG and \
+        b"dlse" in lib.hs_last_error()
     assert score(dsink=f) == hs.HS_ERR_INVALID_ARG and b"no sink" in lib.hs_last_error()
     assert score(ws=None) == hs.HS_ERR_WORKSPACE
     assert score(nbytes=ctypes.c_size_t(n - 1)) == hs.HS_ERR_WORKSPACE
     assert score(ws=ctypes.c_void_p(4104)) == hs.HS_ERR_WORKSPACE
     # paged KV has no gradient path
     paged = _raw_problem()
-    st = lib.hs_block_score_bwd(ctypes.byref(paged), f, f, None, f, f, f, f, f, None, f, big, None)
+    st = lib.hs_block_score_bwd(ctypes.byref(paged), f, f, None, f, f, f, None, f, f, None, f,
+                                big, None)
     assert st == hs.HS_ERR_UNSUPPORTED and b"paged" in lib.hs_last_error()
     # window and top_k
-    st = lib.hs_swa_bwd(p.ref, f, f, None, 0, f, f, f, f, f, None, f, big, None)
+    st = lib.hs_swa_bwd(p.ref, f, f, None, 0, f, f, f, None, f, f, None, f, big, None)
     assert st == hs.HS_ERR_INVALID_ARG and b"window" in lib.hs_last_error()
-    st = lib.hs_sparse_gather_bwd(p.ref, f, f, None, f, 65, f, f, f, f, f, None, f, big, None)
+    st = lib.hs_sparse_gather_bwd(p.ref, f, f, None, f, 65, f, f, f, None, f, f, None, f, big,
+                                  None)
     assert st == hs.HS_ERR_UNSUPPORTED
-    st = lib.hs_sparse_gather_bwd(p.ref, f, f, None, None, 4, f, f, f, f, f, None, f, big, None)
+    st = lib.hs_sparse_gather_bwd(p.ref, f, f, None, None, 4, f, f, f, None, f, f, None, f,
+                                  big, None)
     assert st == hs.HS_ERR_INVALID_ARG and b"block_idx" in lib.hs_last_error()
     with pytest.raises(ValueError):
         hs.hs_workspace_size(p, hs.HS_OP_SWA_BWD, window=0)
@@ -225,8 +232,17 @@ def test_device_lengths_validation():
     lib = hs.load_library()
     ok = _raw_problem(batch=2, kv_lens_device=512)
     assert lib.hs_num_blocks(ctypes.byref(ok)) == 10            # capacity 640 -> 10 blocks
+    # in-place caches take device lengths too (bf16, no documents)
     assert lib.hs_num_blocks(ctypes.byref(_raw_problem(page_table=None, max_pages=0,
-                                                       kv_lens_device=512))) == hs.HS_ERR_INVALID_ARG
+                                                       kv_lens_device=512))) == 10
+    assert lib.hs_num_blocks(ctypes.byref(_raw_problem(
+        page_table=None, max_pages=0, kv_lens_device=512, dtype=hs.HS_F32, num_heads=8,
+        head_dim_qk=96, head_dim_v=64))) == hs.HS_ERR_UNSUPPORTED
+    ds = (ctypes.c_int32 * 1)(0)
+    de = (ctypes.c_int32 * 1)(640)
+    assert lib.hs_num_blocks(ctypes.byref(_raw_problem(
+        page_table=None, max_pages=0, seqlen_q=640, doc_start=ds, doc_end=de, n_docs=1,
+        kv_lens_device=512))) == hs.HS_ERR_INVALID_ARG
     lens = (ctypes.c_int32 * 1)(100)
     assert lib.hs_num_blocks(ctypes.byref(_raw_problem(kv_lens=lens, n_kv_lens=1,
                                                        kv_lens_device=512))) == hs.HS_ERR_INVALID_ARG
@@ -234,6 +250,48 @@ def test_device_lengths_validation():
     n = ctypes.c_size_t(0)
     assert lib.hs_workspace_size(ctypes.byref(ok), hs.HS_OP_BLOCK_SCORE, 0, 0, ctypes.byref(n)) == 0
     assert n.value > 0                                          # decode split planned at capacity
+
+
+def test_device_document_bounds_validation():
+    """Device-resident document bounds: NB is the capacity bound
+    ceil(S / 64) + n_docs - 1; host-only checks before any launch."""
+    lib = hs.load_library()
+
+    def prob(**kw):
+        f = dict(seqlen_q=1000, seqlen_kv=1000, page_table=None, max_pages=0, n_docs=8,
+                 doc_bounds_device=512)
+        f.update(kw)
+        return ctypes.byref(_raw_problem(**f))
+    assert lib.hs_num_blocks(prob()) == 16 + 7
+    assert lib.hs_num_blocks(prob(n_docs=1)) == 16
+    assert lib.hs_num_blocks(prob(n_docs=64)) == 16 + 63
+    assert lib.hs_num_blocks(prob(n_docs=0)) == hs.HS_ERR_INVALID_ARG
+    assert lib.hs_num_blocks(prob(n_docs=65)) == hs.HS_ERR_UNSUPPORTED
+    assert lib.hs_num_blocks(prob(doc_bounds_device=514)) == hs.HS_ERR_INVALID_ARG
+    assert lib.hs_num_blocks(prob(seqlen_q=999)) == hs.HS_ERR_INVALID_ARG
+    assert lib.hs_num_blocks(prob(batch=2, seqlen_q=1000)) == hs.HS_ERR_INVALID_ARG
+    assert lib.hs_num_blocks(prob(page_table=256, max_pages=16)) == hs.HS_ERR_INVALID_ARG
+    assert lib.hs_num_blocks(prob(kv_lens_device=256)) == hs.HS_ERR_INVALID_ARG
+    lens = (ctypes.c_int32 * 1)(1000)
+    assert lib.hs_num_blocks(prob(kv_lens=lens, n_kv_lens=1)) == hs.HS_ERR_INVALID_ARG
+    ds = (ctypes.c_int32 * 1)(0)
+    de = (ctypes.c_int32 * 1)(1000)
+    assert lib.hs_num_blocks(prob(doc_start=ds, doc_end=de, n_docs=1)) == hs.HS_ERR_INVALID_ARG
+    assert lib.hs_num_blocks(prob(dtype=hs.HS_F32, num_heads=8, head_dim_qk=96,
+                                  head_dim_v=64)) == hs.HS_ERR_UNSUPPORTED
+    # forward workspaces: never split (the host cannot see the packing)
+    n = ctypes.c_size_t(1)
+    for op in (hs.HS_OP_BLOCK_SCORE, hs.HS_OP_SWA, hs.HS_OP_SPARSE_GATHER):
+        assert lib.hs_workspace_size(prob(seqlen_q=256, seqlen_kv=256), op, 8, 64,
+                                     ctypes.byref(n)) == 0
+        assert n.value == 0
+    # gradients take host bounds only
+    for op in (hs.HS_OP_BLOCK_SCORE_BWD, hs.HS_OP_SWA_BWD, hs.HS_OP_SPARSE_GATHER_BWD):
+        assert lib.hs_workspace_size(prob(), op, 8, 64, ctypes.byref(n)) == hs.HS_ERR_UNSUPPORTED
+    f = ctypes.c_void_p(4096)
+    st = lib.hs_block_score_bwd(prob(), f, f, None, f, f, f, None, f, f, None, f,
+                                ctypes.c_size_t(1 << 30), None)
+    assert st == hs.HS_ERR_UNSUPPORTED and b"document" in lib.hs_last_error()
 
 
 def test_gradient_workspace_bounded_for_long_sequences():
@@ -402,15 +460,21 @@ def test_window_and_sparse_call_rejects_before_launch():
     p = _mla()
     f = ctypes.c_void_p(4096)
 
-    def call(top_k=4, window=16, out_swa=f, lse_swa=f, out_sparse=f, lse_sparse=f, idx=f):
+    def call(top_k=4, window=16, out_swa=f, lse_swa=f, out_sparse=f, lse_sparse=f, idx=f,
+             ga=None, gb=None, om=None):
         return lib.hs_swa_sparse_fwd(p.ref, f, f, None, window, idx, top_k, out_swa, lse_swa,
-                                     out_sparse, lse_sparse, None, 0, None)
+                                     out_sparse, lse_sparse, ga, gb, om, None, 0, None)
     assert call(out_swa=None) == hs.HS_ERR_INVALID_ARG and b"out_swa" in lib.hs_last_error()
     assert call(lse_sparse=None) == hs.HS_ERR_INVALID_ARG and b"lse_sparse" in lib.hs_last_error()
     assert call(idx=None) == hs.HS_ERR_INVALID_ARG and b"block_idx" in lib.hs_last_error()
     assert call(top_k=0) == hs.HS_ERR_INVALID_ARG
     assert call(top_k=65) == hs.HS_ERR_UNSUPPORTED
     assert call(window=0) == hs.HS_ERR_INVALID_ARG and b"window" in lib.hs_last_error()
+    # the gated combination takes both gates and the output, or none of them
+    assert call(ga=f) == hs.HS_ERR_INVALID_ARG and b"gate_sparse" in lib.hs_last_error()
+    assert call(ga=f, gb=f) == hs.HS_ERR_INVALID_ARG and b"out_mix" in lib.hs_last_error()
+    assert call(ga=f, gb=ctypes.c_void_p(4098), om=f) == hs.HS_ERR_INVALID_ARG
+    assert call(om=f) == hs.HS_ERR_INVALID_ARG and b"gate_swa" in lib.hs_last_error()
     n = ctypes.c_size_t(0)
     ws = lambda k, w: lib.hs_workspace_size(p.ref, hs.HS_OP_SWA_SPARSE, k, w, ctypes.byref(n))
     assert ws(4, 16) == hs.HS_OK and n.value == 0

@@ -1,7 +1,8 @@
 """GPU checks of the autograd functions (block_sparse_mqa_amd.autograd): a
 backward pass through them must deliver exactly the library's gradients
-(rounded to the inputs' dtype), the block scores, lse and selection must not
-require gradients, and gradients of two calls sharing q and kv must add."""
+(rounded to the inputs' dtype), the block scores and selection must not
+require gradients, lse carries its gradient into the kernels, and gradients
+of two calls sharing q and kv must add."""
 import pytest
 import torch
 
@@ -9,7 +10,7 @@ import block_sparse_mqa_amd as hs
 from block_sparse_mqa_amd import autograd as hsa
 from block_sparse_mqa_amd import inputs
 
-from gpu_common import say
+from gpu_common import np64, say
 from test_gpu_parity import MLA
 
 pytestmark = pytest.mark.gpu
@@ -30,7 +31,7 @@ def test_autograd_matches_library_gradients():
     q, kv, sink = _leaves(p)
 
     out, lse, bl, idx = hsa.block_score_attention(q, kv, sink, prob, p.top_k)
-    assert out.requires_grad and not lse.requires_grad and not bl.requires_grad
+    assert out.requires_grad and lse.requires_grad and not bl.requires_grad
     assert not idx.requires_grad and idx.dtype == torch.int32
     (gq, gkv, gs) = torch.autograd.grad(out, (q, kv, sink), dout)
     with torch.no_grad():
@@ -109,3 +110,47 @@ def test_sliding_window_layer_gradients():
     gq1, = torch.autograd.grad(ow, (q,), d1)
     assert torch.equal(gq1, a[0].to(q.dtype))
     say("[gpu] sliding-window layer function: gradients of both branches")
+
+
+def test_loss_using_lse_gets_its_gradient():
+    """A loss that uses lse (a log-sum-exp weighting of branches would):
+    autograd passes dlse to the kernels, giving exactly the library's
+    gradients with dlse, and those match the float64 oracle's gradient of
+    sum(dout * out) + sum(w * lse) for all three operations."""
+    from oracle import hysparse_ref as ref
+    from test_gpu_bwd import _grad_close
+    p = inputs.make(1, 130, 130, MLA["H"], MLA["Dk"], MLA["Dv"], seed=83, top_k=2, window=70,
+                    name="autograd_lse")
+    prob = hs.Problem(1, 130, 130, p.H, p.Dk, p.Dv, scale=p.scale)
+    dout = inputs.make_dout(p, seed=84).cuda()
+    w = torch.randn((1, 130, p.H), generator=torch.Generator().manual_seed(85)).cuda()
+    q, kv, sink = _leaves(p)
+    out, lse, bl, idx = hsa.block_score_attention(q, kv, sink, prob, p.top_k)
+    ow, lw = hsa.sliding_window_attention(q, kv, sink, prob, p.window)
+    og, lg = hsa.sparse_gather_attention(q, kv, sink, idx, prob, p.top_k)
+    kw = dict(block_size=64)
+    cases = (("score", out, lse, lambda d: ref.block_score_bwd(p.q, p.kv, p.sink, p.Dv, p.scale,
+                                                               d, dlse=w.cpu(), **kw)),
+             ("swa", ow, lw, lambda d: ref.swa_bwd(p.q, p.kv, p.sink, p.Dv, p.scale, p.window, d,
+                                                   dlse=w.cpu(), **kw)),
+             ("gather", og, lg, lambda d: ref.sparse_gather_bwd(p.q, p.kv, p.sink, p.Dv, p.scale,
+                                                                idx.cpu().numpy(), d,
+                                                                dlse=w.cpu(), **kw)))
+    errs = {}
+    for name, o, l, oracle_fn in cases:
+        loss = (o.float() * dout.float()).sum() + (l * w).sum()
+        gq, gkv, gs = torch.autograd.grad(loss, (q, kv, sink))
+        with torch.no_grad():
+            if name == "score":
+                lib = hs.block_score_bwd(prob, q, kv, sink, o, l, dout, dlse=w)
+            elif name == "swa":
+                lib = hs.swa_bwd(prob, q, kv, sink, p.window, o, l, dout, dlse=w)
+            else:
+                lib = hs.sparse_gather_bwd(prob, q, kv, sink, idx, p.top_k, o, l, dout, dlse=w)
+        torch.cuda.synchronize()
+        assert torch.equal(gq, lib[0].to(q.dtype)) and torch.equal(gkv, lib[1].to(kv.dtype))
+        assert torch.equal(gs, lib[2])
+        want = oracle_fn(dout.cpu())
+        errs[name] = [_grad_close(np64(a), b, "bf16", f"{name} {n}")
+                      for a, b, n in zip(lib, want, ("dq", "dkv", "dsink"))]
+    say(f"[gpu] gradients with dlse vs oracle: {errs}")

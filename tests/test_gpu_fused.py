@@ -109,3 +109,39 @@ def test_fused_paged_device_lengths_in_graph():
         own = ref.own_blocks(B, 1, cap, 64, kv_lens=lens)
         _check_same(got, (o2, l2, b2, i2), own, K, f"replay {rep}")
         say(f"[gpu] fused graph replay {rep} lengths {min(lens)}..{max(lens)}: identical")
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_normalised_block_scores(name):
+    """The optional block_prob output: equal to the oracle's block_prob on the
+    GPU's own block scores and lse (same inputs, rounding of exp only), and to
+    the oracle's from its own float64 scores within the block-score and lse
+    tolerances; the fused call's other outputs are unchanged by it."""
+    B, Sq, Skv, lens, K, dtype = CASES[name]
+    say(f"[gpu] normalised block scores {name}")
+    if lens == "rand":
+        lens = [int(x) for x in np.random.default_rng(53).integers(1, Skv + 1, size=B)]
+    if dtype == "f32":
+        p = inputs.make(B, Sq, Skv, 8, 96, 64, dtype="f32", seed=54, kv_lens=lens, top_k=K,
+                        name=name)
+    else:
+        p = inputs.make(B, Sq, Skv, MLA["H"], MLA["Dk"], MLA["Dv"], seed=54, kv_lens=lens,
+                        top_k=K, name=name)
+    d = Dev(p)
+    plain = hs.block_score_topk(d.prob, d.q, d.kv, d.sink, K)
+    out, lse, bl, idx, pr = hs.block_score_topk(d.prob, d.q, d.kv, d.sink, K, with_prob=True)
+    torch.cuda.synchronize()
+    for n, a, b in zip(("out", "lse", "block_logit", "block_idx"), (out, lse, bl, idx), plain):
+        assert torch.equal(a, b), f"{name}: {n} changed by the block_prob output"
+    got = pr.cpu().numpy().astype(np.float64)
+    same = ref.block_prob(bl.cpu().numpy(), lse.cpu().numpy())
+    e_same = float(np.abs(got - same).max())
+    assert e_same <= 1e-5, e_same
+    rows = None if p.B * p.Sq <= 4096 else np.arange(0, p.Sq, 7)
+    _, l_ref, b_ref = ref.block_score(p.q, p.kv, d.sink_cpu, p.Dv, p.scale, rows=rows, **d.kw())
+    want = ref.block_prob(b_ref, l_ref)
+    sel = slice(None) if rows is None else rows
+    e_ref = float(np.abs(got[:, sel] - want).max())
+    assert e_ref <= 1e-3, e_ref
+    assert (got >= 0).all() and (got <= 1 + 1e-6).all()
+    say(f"[gpu] block_prob {name}: vs own scores {e_same:.2e}, vs oracle {e_ref:.2e}")

@@ -82,20 +82,26 @@ def _decode_reference(p, lens, NB):
     return o, l, b, os_, ls
 
 
-def test_paged_device_lengths_and_graph_replay():
+@pytest.mark.parametrize("layout", ["paged", "in_place"])
+def test_device_lengths_and_graph_replay(layout):
     """Lengths in device memory, read at run time: one captured graph of the
-    decode calls replayed with different lengths matches the oracle each time."""
-    say("[gpu] paged KV with device lengths, captured graph")
+    decode calls replayed with different lengths matches the oracle each time,
+    for a paged pool and for an in-place cache [B, capacity, Dk]."""
+    say(f"[gpu] {layout} KV with device lengths, captured graph")
     B, cap = 8, 2048
     rng = np.random.default_rng(44)
     full = [cap] * B
     p = inputs.make(B, 1, cap, MLA["H"], MLA["Dk"], MLA["Dv"], seed=44, kv_lens=full, top_k=4,
                     window=200, name="paged_devlen")
-    pool, pt = _paged(p, seed=45)
-    pool, pt = pool.cuda(), pt.cuda()
     q, sink = p.q.cuda(), p.sink.cuda()
     lens_dev = torch.full((B,), cap, dtype=torch.int32, device="cuda")
-    prob = hs.Problem(B, 1, cap, p.H, p.Dk, p.Dv, page_table=pt, kv_lens_device=lens_dev)
+    if layout == "paged":
+        pool, pt = _paged(p, seed=45)
+        pool, pt = pool.cuda(), pt.cuda()
+        prob = hs.Problem(B, 1, cap, p.H, p.Dk, p.Dv, page_table=pt, kv_lens_device=lens_dev)
+    else:
+        pool = p.kv.cuda()
+        prob = hs.Problem(B, 1, cap, p.H, p.Dk, p.Dv, kv_lens_device=lens_dev)
     NB = hs.hs_num_blocks(prob)
     assert NB == cap // 64
     out = torch.empty((B, 1, p.H, p.Dv), dtype=torch.bfloat16, device="cuda")

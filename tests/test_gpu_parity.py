@@ -152,3 +152,39 @@ def test_topk_exact_synthetic():
         own = ref.own_blocks(B, 1, Skv, 64, lens)
         want = ref.topk_blocks(bl, own, K)
         assert np.array_equal(idx.cpu().numpy(), want), K
+
+
+def test_topk_exact_adversarial():
+    """Top-k on scores built to stress the radix select: neighbours one ulp
+    apart (keys that differ only in their lowest bits), +0 and -0 mixed with
+    denormals, negative and positive values (the sign bit differs, so every
+    digit is searched), long runs of equal values at the cut, one value
+    everywhere, and 4096 columns with k = 64. The selection must equal the
+    oracle's on the same fp32 scores."""
+    say("[gpu] top-k adversarial")
+    rng = np.random.default_rng(23)
+    B, Skv = 6, 4096 * 64
+    prob = hs.Problem(B, 1, Skv, 64, 576, 512)
+    NB = hs.hs_num_blocks(prob)
+    assert NB == 4096
+    one = np.float32(1.0)
+    steps = rng.integers(0, 3000, size=NB)
+    bl = np.empty((B, 1, NB), np.float32)
+    bl[0, 0] = (one + steps.astype(np.float32) * np.finfo(np.float32).eps).astype(np.float32)
+    tiny = np.finfo(np.float32).smallest_subnormal
+    bl[1, 0] = rng.choice(np.array([0.0, -0.0, tiny, -tiny, 2 * tiny], np.float32), size=NB)
+    bl[2, 0] = rng.standard_normal(NB).astype(np.float32) * np.float32(1e3)
+    bl[3, 0] = np.where(rng.random(NB) < 0.5, np.float32(3.0), np.float32(-3.0))
+    bl[3, 0, rng.choice(NB, 40, replace=False)] = np.float32(5.0)   # 40 above a long tie run
+    bl[4, 0] = np.float32(0.75)
+    bl[5, 0] = rng.standard_normal(NB).astype(np.float32)
+    bl[5, 0, rng.random(NB) < 0.7] = -np.inf
+    own = ref.own_blocks(B, 1, Skv, 64, None)
+    for K in (1, 2, 33, 64):
+        idx = hs.topk_blocks(prob, torch.from_numpy(bl).cuda(), K)
+        torch.cuda.synchronize()
+        want = ref.topk_blocks(bl, own, K)
+        got = idx.cpu().numpy()
+        for b in range(B):
+            assert np.array_equal(got[b], want[b]), (K, b, got[b], want[b])
+    say("[gpu] top-k adversarial: exact")

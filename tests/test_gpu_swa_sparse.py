@@ -111,3 +111,51 @@ def test_long_context_full_size():
     got, want = _both(d, p, idx)
     _equal(got, want, "long context")
     say("[gpu] swa+sparse long context: identical")
+
+
+def _gates(p, seed):
+    g = torch.Generator().manual_seed(seed)
+    shape = (p.B, p.Sq, p.H)
+    return torch.rand(shape, generator=g), torch.rand(shape, generator=g)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_gated_combination(name):
+    """The optional gated sum out_mix = g_swa * out_swa + g_sparse * out_sparse
+    (per token and head): within the rounding bound of an fp32 sum and a bf16
+    store of the call's own branch outputs, combined in float64, and within the bf16 tolerance of the oracle's
+    gated combination of its own branch outputs; the branch outputs are the
+    ones the call returns without gates. One-pass shapes form it in the
+    kernel's epilogue, split decode and fp32 in a separate launch."""
+    p = CASES[name]()
+    say(f"[gpu] gated combination {name}")
+    d = Dev(p)
+    _, _, bl = hs.block_score(d.prob, d.q, d.kv, d.sink)
+    idx = hs.topk_blocks(d.prob, bl, p.top_k)
+    g1, g2 = _gates(p, 81)
+    ow, lw, og, lg, om = hs.swa_sparse(d.prob, d.q, d.kv, d.sink, p.window, idx, p.top_k,
+                                       gate_swa=g1.cuda(), gate_sparse=g2.cuda())
+    plain = hs.swa_sparse(d.prob, d.q, d.kv, d.sink, p.window, idx, p.top_k)
+    torch.cuda.synchronize()
+    for n, a, b in zip(("out_swa", "lse_swa", "out_sparse", "lse_sparse"), (ow, lw, og, lg), plain):
+        assert torch.equal(a, b), f"{name}: {n} changed by the gates"
+    ga, gb = g1.double().numpy()[..., None], g2.double().numpy()[..., None]
+    ta, tb = ga * np64(ow), gb * np64(og)
+    own = ta + tb
+    got = np64(om)
+    # fp32 sum fl(gb*b + fl(ga*a)): at most 2^-24 of |ga*a| and of the result
+    # each (under 2^-22 of |ga*a| + |gb*b| together, which matters only where
+    # the branches cancel), then one rounding to bf16 (at most 2^-8 relative)
+    bound = 2.0 ** -22 * (np.abs(ta) + np.abs(tb))
+    if p.dtype == "bf16":
+        bound = bound + 2.0 ** -8 * np.abs(own) * (1 + 2.0 ** -20)
+    e_own = float((np.abs(got - own) / (bound + 1e-30)).max())
+    assert e_own <= 1.0, f"{name}: error {e_own} of the rounding bound from its own branches"
+    idx_np = idx.cpu().numpy()
+    os_ref, _ = ref.swa(p.q, p.kv, d.sink_cpu, p.Dv, p.scale, p.window, **d.kw())
+    og_ref, _ = ref.sparse_gather(p.q, p.kv, d.sink_cpu, p.Dv, p.scale, idx_np, **d.kw())
+    want = ref.gated_combine(os_ref, og_ref, g1, g2)
+    tol = BF16_TOL if p.dtype == "bf16" else 1e-4
+    e = assert_close(got, want, 2 * tol, f"{name} out_mix")
+    say(f"[gpu] gated combination {name}: {e_own:.2f} of the rounding bound from its branches, "
+        f"oracle {e:.2e}")
