@@ -33,7 +33,7 @@ HS_OP_BLOCK_SCORE_BWD_STORE_DS, HS_OP_SWA_BWD_STORE_DS = 6, 7
 HS_OP_SWA_SPARSE = 8
 
 EXPORTS = ("hs_num_blocks", "hs_workspace_size", "hs_block_score_fwd", "hs_topk_blocks",
-           "hs_block_score_topk_fwd", "hs_sparse_gather_fwd",
+           "hs_block_score_topk_fwd", "hs_block_score_topk_fwd_noalloc", "hs_sparse_gather_fwd",
            "hs_swa_fwd", "hs_swa_sparse_fwd",
            "hs_block_score_bwd", "hs_sparse_gather_bwd", "hs_swa_bwd", "hs_status_string",
            "hs_last_error", "hs_version")
@@ -78,6 +78,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hs_topk_blocks.argtypes, lib.hs_topk_blocks.restype = [P, vp, i32, vp, vp], i32
     lib.hs_block_score_topk_fwd.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hs_block_score_topk_fwd.restype = i32
+    lib.hs_block_score_topk_fwd_noalloc.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
+    lib.hs_block_score_topk_fwd_noalloc.restype = i32
     lib.hs_sparse_gather_fwd.argtypes = [P, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
     lib.hs_sparse_gather_fwd.restype = i32
     lib.hs_swa_fwd.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, sz, vp]
@@ -287,6 +289,15 @@ def hs_block_score_topk_fwd(prob, q, kv, sink, top_k, out, lse, block_logit, blo
         prob.ref, _ptr(q), _ptr(kv), _ptr(sink), int(top_k), _ptr(out), _ptr(lse),
         _ptr(block_logit), _ptr(block_idx), _ptr(block_prob), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def hs_block_score_topk_fwd_noalloc(prob, q, kv, sink, top_k, out, lse, block_logit, block_idx,
+                                    stream=None, block_prob=None):
+    _check_io(prob, q=q, kv=kv, sink=sink, out=out, lse=lse, block_logit=block_logit,
+              block_idx=block_idx, block_prob=block_prob, _top_k=int(top_k))
+    _check(load_library().hs_block_score_topk_fwd_noalloc(
+        prob.ref, _ptr(q), _ptr(kv), _ptr(sink), int(top_k), _ptr(out), _ptr(lse),
+        _ptr(block_logit), _ptr(block_idx), _ptr(block_prob), _stream(stream)))
 
 
 def hs_sparse_gather_fwd(prob, q, kv, sink, block_idx, top_k, out, lse, ws=None, stream=None):

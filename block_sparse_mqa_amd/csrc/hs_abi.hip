@@ -16,6 +16,7 @@
 #include <cstdio>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/hs.h"
@@ -244,12 +245,45 @@ hs_status hip_status(int err, const char* what) {
   return HS_OK;
 }
 
+// Library-owned workspace of the no-allocation entry point: the split-decode
+// partials of hs_block_score_topk_fwd_noalloc live here. Every GPU the library
+// runs on holds its own copy until the process ends; host code uses the
+// device address hipGetSymbolAddress returns, never the array's name.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+// Device address of this device's scratch array, looked up once per device
+// (with that device current) and kept; nullptr and a message on failure.
+void* scratch_ptr() {
+  static std::mutex mu;
+  static void* ptrs[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    fail(HS_ERR_HIP, "hipGetDevice failed or device index out of range");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      fail(HS_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+      return nullptr;
+    }
+    ptrs[dev] = ptr;
+  }
+  return ptrs[dev];
+}
+
 // sel_idx (score operation only): also select each row's top sel_k blocks,
 // and with sel_prob write the normalised block scores.
+// use_scratch: plan the split within kScratchBytes and take the partials'
+// workspace from the library's scratch array (ws and ws_bytes are ignored).
 hs_status launch_attn(int op, const hs_problem* p, const void* q, const void* kv, const float* sink,
                       const int32_t* block_idx, int32_t top_k, int32_t window, void* out,
                       float* lse, float* block_logit, void* ws, size_t ws_bytes, void* stream,
-                      int32_t* sel_idx = nullptr, int32_t sel_k = 0, float* sel_prob = nullptr) {
+                      int32_t* sel_idx = nullptr, int32_t sel_k = 0, float* sel_prob = nullptr,
+                      bool use_scratch = false) {
   hs::Geom g;
   hs_status st = prepare(p, g);
   if (st != HS_OK) return st;
@@ -277,9 +311,18 @@ hs_status launch_attn(int op, const hs_problem* p, const void* q, const void* kv
   if (g.Sq * g.B == 0) return HS_OK;
 
   if (p->dtype == HS_BF16) {
-    const SplitPlan sp = plan_split(g, op, top_k, window);
+    const SplitPlan sp =
+        plan_split(g, op, top_k, window, use_scratch ? kScratchBytes : SIZE_MAX);
     const int nsplit = sp.nsplit;
     const size_t need = split_ws_bytes(g, nsplit);
+    if (use_scratch) {
+      if (need > kScratchBytes)
+        return fail(HS_ERR_UNSUPPORTED, "partials of %zu bytes exceed the %zu-byte scratch array",
+                    need, kScratchBytes);
+      ws = need > 0 ? scratch_ptr() : nullptr;
+      if (need > 0 && !ws) return HS_ERR_HIP;
+      ws_bytes = kScratchBytes;
+    }
     if (need > 0 && (!ws || ws_bytes < need))
       return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
                   ws ? ws_bytes : (size_t)0);
@@ -511,6 +554,14 @@ hs_status hs_block_score_topk_fwd(const hs_problem* p, const void* q, const void
                                   void* ws, size_t ws_bytes, void* stream) {
   return launch_attn(HS_OP_BLOCK_SCORE, p, q, kv, sink, nullptr, 0, 0, out, lse, block_logit, ws,
                      ws_bytes, stream, block_idx, top_k, block_prob);
+}
+
+hs_status hs_block_score_topk_fwd_noalloc(const hs_problem* p, const void* q, const void* kv,
+                                          const float* sink, int32_t top_k, void* out, float* lse,
+                                          float* block_logit, int32_t* block_idx,
+                                          float* block_prob, void* stream) {
+  return launch_attn(HS_OP_BLOCK_SCORE, p, q, kv, sink, nullptr, 0, 0, out, lse, block_logit,
+                     nullptr, 0, stream, block_idx, top_k, block_prob, true);
 }
 
 hs_status hs_swa_sparse_fwd(const hs_problem* p, const void* q, const void* kv, const float* sink,

@@ -206,6 +206,22 @@ hs_status hs_block_score_topk_fwd(const hs_problem* p, const void* q, const void
                                   float* block_logit, int32_t* block_idx, float* block_prob,
                                   void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * outputs as hs_block_score_topk_fwd, but the partial results of a split key
+ * range (single-token decode) live in a library-owned device array of 64 MiB
+ * per GPU instead of a caller workspace, and the call allocates nothing.
+ * The split is planned to fit that array (rows then take fewer, longer
+ * chunks), so results agree with hs_block_score_topk_fwd up to the rounding
+ * of the partial merge; HS_ERR_UNSUPPORTED if the partials could not fit.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (each call writes every partial it later reads, so nothing needs
+ * clearing): calls that overlap on one GPU (concurrent streams) race. */
+hs_status hs_block_score_topk_fwd_noalloc(const hs_problem* p, const void* q, const void* kv,
+                                          const float* sink, int32_t top_k, void* out, float* lse,
+                                          float* block_logit, int32_t* block_idx,
+                                          float* block_prob, void* stream);
+
 /* Block-sparse gather attention (same page, "Core", block-sparse DSA gather
  * bullet; per-file table row for block_sparse_mqa_dsa.py): attention with
  * sink over the union of the listed blocks intersected with the allowed keys.
