@@ -725,6 +725,14 @@ def main():
         grads["flop_per_pair"] = fpb
         grads["block_score_bwd_tflop_s"] = round(f_bwd / (t * 1e-3) / 1e12, 2)
         grads["block_score_bwd_frac"] = round(f_bwd / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        # the gather and the window over the same (head, key) pairs as their
+        # forward calls (forward flops / (2 Dk + 2 Dv) pairs)
+        for name, f_fwd in (("sparse_gather_bwd", f_gather), ("swa_bwd", f_swa)):
+            if f_fwd and name in grads["ms"]:
+                fb = f_fwd / (2 * (p.Dk + p.Dv)) * fpb
+                rate = fb / (grads["ms"][name] * 1e-3) / 1e12
+                grads[name + "_tflop_s"] = round(rate, 2)
+                grads[name + "_frac"] = round(rate / PEAK_BF16_TFLOPS, 4)
         res["gradients"] = grads
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(p, args.cpu_budget)

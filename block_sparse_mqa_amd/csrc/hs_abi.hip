@@ -468,6 +468,7 @@ hs_status launch_bwd(int op, const hs_problem* p, const void* q, const void* kv,
     a.chunk_rows = L.chunk_rows;
     a.n_chunks = L.n_chunks;
     a.items = L.items;
+    a.split_rows = L.split_rows;
     a.row_tiles = L.row_tiles;
   }
   a.g = g;

@@ -621,8 +621,9 @@ __global__ __launch_bounds__(64) void merge_bf16_kernel(AttnArgs a) {
           }
         lmax2 = wave_max_f(L > 0.f ? M + fast_log2(L) : -INFINITY);
       }
-      topk_row<PER>(a.g, a.block_logit, a.topk_idx, a.topk_k, rowi, threadIdx.x, a.topk_prob,
-                    lmax2);
+      __shared__ unsigned pack[192];
+      topk_row<PER>(a.g, a.block_logit, a.topk_idx, a.topk_k, rowi, threadIdx.x, pack,
+                    a.topk_prob, lmax2);
       return;
     }
   }

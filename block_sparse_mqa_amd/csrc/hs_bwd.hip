@@ -272,12 +272,12 @@ __global__ __launch_bounds__(256) void bwd_plan_kernel(BwdArgs a, int op) {
                             a.g_total, a.g_off, &first);
     a.plan_first[f] = first;
     a.plan_nrows[f] = n;
-    cnt += n > 0;
+    cnt += items_of(n, a.split_rows);
   }
   int run = seg_scan(cnt);
   for (int f = f0; f < f1; ++f) {
     a.plan_pre[f] = min(run, a.items);
-    run += a.plan_nrows[f] > 0;
+    run += items_of(a.plan_nrows[f], a.split_rows);
   }
   if (tid == 255) a.plan_pre[F] = min(run, a.items);
 }
@@ -646,8 +646,12 @@ void bwd_dkv_bf16_kernel(BwdArgs a) {
   }
   const int f = lo;
   const int j = f % g.NB, b = f / (g.NB * C);
-  const int n = a.plan_nrows[f];
-  const int base_i = a.plan_first[f];
+  // the item's share of (b, c, j)'s rows: all of them, or split_rows from
+  // sub-item (item - plan_pre[f]) onwards
+  const int sub = item - a.plan_pre[f];
+  const int n = a.split_rows > 0 ? min(a.split_rows, a.plan_nrows[f] - sub * a.split_rows)
+                                 : a.plan_nrows[f];
+  const int base_i = a.plan_first[f] + sub * a.split_rows;
   auto row_at = [&](int i) -> int {
     const int rr = OP == kGather ? a.g_rows[base_i + i] : base_i + i;
     return min(max(rr, 0), g.Sq - 1);
@@ -848,8 +852,8 @@ __global__ __launch_bounds__(256) void bwd_reduce_bf16_kernel(BwdArgs a) {
       const int k = i - (d.start + (j - d.blk0) * g.BS);
       for (int c = 0; c < a.n_chunks; ++c) {
         const int f = (b * a.n_chunks + c) * g.NB + j;
-        const int it = a.plan_pre[f];
-        if (a.plan_pre[f + 1] > it) v += *(const f32x4*)(a.part + ((size_t)it * BS + k) * DK + 4 * c4);
+        for (int it = a.plan_pre[f]; it < a.plan_pre[f + 1]; ++it)
+          v += *(const f32x4*)(a.part + ((size_t)it * BS + k) * DK + 4 * c4);
       }
     }
     *(f32x4*)(a.dkv + ((size_t)b * g.Skv + i) * DK + 4 * c4) = v;
@@ -967,8 +971,12 @@ __global__ __launch_bounds__(f32b::NT) void bwd_dkv_f32_kernel(BwdArgs a) {
   }
   const int f = lo;
   const int j = f % g.NB, b = f / (g.NB * C);
-  const int n = a.plan_nrows[f];
-  const int base_i = a.plan_first[f];
+  // the item's share of (b, c, j)'s rows: all of them, or split_rows from
+  // sub-item (item - plan_pre[f]) onwards
+  const int sub = item - a.plan_pre[f];
+  const int n = a.split_rows > 0 ? min(a.split_rows, a.plan_nrows[f] - sub * a.split_rows)
+                                 : a.plan_nrows[f];
+  const int base_i = a.plan_first[f] + sub * a.split_rows;
   auto row_at = [&](int i) -> int {
     const int rr = OP == kGather ? a.g_rows[base_i + i] : base_i + i;
     return min(max(rr, 0), g.Sq - 1);
@@ -1074,8 +1082,8 @@ __global__ __launch_bounds__(256) void bwd_reduce_f32_kernel(BwdArgs a) {
       const int k = i - (dc.start + (j - dc.blk0) * g.BS);
       for (int cc = 0; cc < a.n_chunks; ++cc) {
         const int f = (b * a.n_chunks + cc) * g.NB + j;
-        const int it = a.plan_pre[f];
-        if (a.plan_pre[f + 1] > it) v += a.part[((size_t)it * 64 + k) * Dk + d];
+        for (int it = a.plan_pre[f]; it < a.plan_pre[f + 1]; ++it)
+          v += a.part[((size_t)it * 64 + k) * Dk + d];
       }
     }
     a.dkv[((size_t)b * g.Skv + i) * Dk + d] = v;

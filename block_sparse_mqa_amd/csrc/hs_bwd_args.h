@@ -52,6 +52,8 @@ struct BwdArgs {
   int chunk_rows;            // R: rows per chunk (multiple of 64)
   int n_chunks;              // C = ceil(Sq / R)
   int items;                 // work items launched (exact or an upper bound)
+  int split_rows;            // gather: rows per work item at most (a (b, c, j) with more
+                             // rows becomes several items); 0: one item per (b, c, j)
   int row_tiles;             // T = ceil(Sq / 64)
   Geom g;
 };
@@ -61,7 +63,7 @@ struct BwdArgs {
 struct BwdLayout {
   size_t dsum, sink_part, first, nrows, pre, cnt, total_g, off_g, rows, part, ds_entry, ds_dummy,
       ds_tiles, total;
-  int n_pre, rows_per_pre, chunk_rows, n_chunks, items, row_tiles, ds_stride;
+  int n_pre, rows_per_pre, chunk_rows, n_chunks, items, row_tiles, ds_stride, split_rows;
   bool store_ds;
 };
 

@@ -89,6 +89,13 @@ __host__ __device__ inline long long causal_tiles_before(const Geom& g, int b, i
   return t;
 }
 
+// Work items of a (b, c, j) with n rows: one if it has rows, or with a split
+// of m rows per item, ceil(n / m).
+__host__ __device__ inline int items_of(int n, int m) {
+  if (n <= 0) return 0;
+  return m > 0 ? (n + m - 1) / m : 1;
+}
+
 // Rows of work item (b, c, j): a range [*first, *first + n) of row indices,
 // or (gather) a range of positions in block j's row list.
 __host__ __device__ inline int item_rows(const Geom& g, int op, int b, int c, int j, int window,

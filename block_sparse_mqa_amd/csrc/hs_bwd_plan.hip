@@ -55,6 +55,16 @@ BwdLayout bwd_layout(const Geom& g, int op, int top_k, int window, bool store_ds
     L.chunk_rows = R;
     L.n_chunks = (g.Sq + R - 1) / R;
     L.items = (int)items_for(R);
+    if (op == kGather) {
+      // A block that many rows of a chunk selected (the rows' own and recent
+      // blocks) would make one long item among short ones; such an item is
+      // split into items of at most split_rows rows, whose partials the
+      // reduction adds in order. Each extra item takes split_rows rows, so
+      // at most B * Sq * top_k / split_rows are added (capped near 8192).
+      const long sel = (long)g.B * g.Sq * std::max(top_k, 1);
+      L.split_rows = (int)std::max<long>(128, (sel + 8191) / 8192);
+      L.items += (int)((sel + L.split_rows - 1) / L.split_rows);
+    }
     const size_t F = (size_t)g.B * L.n_chunks * g.NB;
     L.first = off;
     off = align256(off + F * sizeof(int));

@@ -12,8 +12,10 @@ namespace hs {
 
 template <int PER>
 __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
+  __shared__ unsigned pack[4][192];   // one packing buffer per wave
   const int lane = threadIdx.x & 63;
-  const int rowi = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wave = threadIdx.x >> 6;
+  const int rowi = blockIdx.x * 4 + wave;
   if (rowi >= a.g.B * a.g.Sq) return;
   float lmax2 = 0.f;
   if (a.block_prob != nullptr) {
@@ -21,7 +23,8 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
     for (int h = lane; h < a.g.H; h += 64) m = fmaxf(m, a.lse[(size_t)rowi * a.g.H + h]);
     lmax2 = wave_max_f(m) * kLog2e;
   }
-  topk_row<PER>(a.g, a.block_logit, a.block_idx, a.top_k, rowi, lane, a.block_prob, lmax2);
+  topk_row<PER>(a.g, a.block_logit, a.block_idx, a.top_k, rowi, lane, pack[wave], a.block_prob,
+                lmax2);
 }
 
 int topk_launch(const TopkArgs& a, hipStream_t stream) {

@@ -8,9 +8,10 @@
 // own block is kept and the other top_k-1 (or top_k if the own block is not a
 // candidate) are the best by (score descending, index ascending). The k-th
 // best value is found exactly by a bitwise search over order-preserving
-// uint32 keys of the fp32 scores: bits shared by every candidate are taken as
-// they are, and each remaining bit (from the highest that differs) is one
-// step that counts the keys at or above a trial threshold. Counts are wave
+// uint32 keys of the fp32 scores, after the keys that cannot be selected are
+// pruned (below): bits shared by every remaining candidate are taken as they
+// are, and each remaining bit (from the highest that differs) is one step
+// that counts the keys at or above a trial threshold. Counts are wave
 // ballots added with scalar popcounts, so a step needs no cross-lane
 // shuffle. Entries above the k-th value are taken, and ties at it are taken
 // in ascending index order until the count is reached. The final scan runs
@@ -32,13 +33,32 @@ __device__ __forceinline__ unsigned ord_key(float v) {
   return u ^ ((unsigned)((int)u >> 31) | 0x80000000u);
 }
 
+// AND / OR over the wave, returned in a scalar register. DPP moves: row
+// shifts by 1, 2, 4 and 8 leave each 16-lane row's total in its last lane,
+// then two row broadcasts carry rows 0 and 0-1 into the rows above, so lane
+// 63 holds the total. Lanes whose source is outside the row keep the
+// identity. No LDS round trip (a shuffle costs one per step).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ unsigned dpp_u(unsigned ident, unsigned v) {
+  return (unsigned)__builtin_amdgcn_update_dpp((int)ident, (int)v, CTRL, ROWS, 0xf, false);
+}
 __device__ __forceinline__ unsigned wave_and_u(unsigned v) {
-  for (int o = 32; o >= 1; o >>= 1) v &= (unsigned)__shfl_xor((int)v, o);
-  return v;
+  v &= dpp_u<0x111, 0xf>(~0u, v);   // row_shr:1
+  v &= dpp_u<0x112, 0xf>(~0u, v);   // row_shr:2
+  v &= dpp_u<0x114, 0xf>(~0u, v);   // row_shr:4
+  v &= dpp_u<0x118, 0xf>(~0u, v);   // row_shr:8
+  v &= dpp_u<0x142, 0xa>(~0u, v);   // row_bcast:15
+  v &= dpp_u<0x143, 0xc>(~0u, v);   // row_bcast:31
+  return (unsigned)__builtin_amdgcn_readlane((int)v, 63);
 }
 __device__ __forceinline__ unsigned wave_or_u(unsigned v) {
-  for (int o = 32; o >= 1; o >>= 1) v |= (unsigned)__shfl_xor((int)v, o);
-  return v;
+  v |= dpp_u<0x111, 0xf>(0u, v);
+  v |= dpp_u<0x112, 0xf>(0u, v);
+  v |= dpp_u<0x114, 0xf>(0u, v);
+  v |= dpp_u<0x118, 0xf>(0u, v);
+  v |= dpp_u<0x142, 0xa>(0u, v);
+  v |= dpp_u<0x143, 0xc>(0u, v);
+  return (unsigned)__builtin_amdgcn_readlane((int)v, 63);
 }
 // Number of (lane, i) with pred(i) true, by ballots and scalar popcounts.
 template <int PER, typename F>
@@ -64,23 +84,30 @@ __device__ __forceinline__ float wave_max_f(float v) {
 // attention (FA4 block scoring + SWA MQA + block-sparse DSA gather)", per-file
 // row for pipeline.py: the block probabilities are recovered as
 // exp(block_logit - lse)).
+// pack: this wave's 192-entry LDS buffer (128 packed keys, a spare slot per
+// lane).
 template <int PER>
 __device__ __forceinline__ void topk_row(const Geom& g, const float* block_logit, int* block_idx,
-                                         int top_k, int rowi, int lane,
+                                         int top_k, int rowi, int lane, unsigned* pack,
                                          float* block_prob = nullptr, float lmax2 = 0.f) {
   rowi = __builtin_amdgcn_readfirstlane(rowi);
   const float* bl = block_logit + (size_t)rowi * g.NB;
   // The row's scores first, so that their loads overlap the geometry below.
+  // (a clamped index and a select instead of a guarded load: no divergent
+  // branch, whose exec-mask bookkeeping runs on the scalar unit)
   float v[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int j = lane + 64 * i;
-    v[i] = j < g.NB ? bl[j] : -INFINITY;
+    const float x = bl[min(j, g.NB - 1)];
+    v[i] = j < g.NB ? x : -INFINITY;
   }
   const int b = rowi / g.Sq, r = rowi % g.Sq;
   const int pos = __builtin_amdgcn_readfirstlane(kv_len_of<true>(g, b)) - g.Sq + r;
   const Doc d = doc_of_pos<true>(g, b, pos);
-  const int own = block_of_pos(g, d, pos);
+  // row-uniform values are pinned to scalar registers, so that the branches
+  // that test them stay scalar branches (not exec-mask bookkeeping)
+  const int own = __builtin_amdgcn_readfirstlane(block_of_pos(g, d, pos));
   const int K = top_k;
   if (block_prob != nullptr) {
     float* pr = block_prob + (size_t)rowi * g.NB;
@@ -116,25 +143,114 @@ __device__ __forceinline__ void topk_row(const Geom& g, const float* block_logit
         if (lane + 64 * i == own) key[i] = 0u;
     }
     const int need = force_own ? K - 1 : K;
-    // Bits common to every remaining candidate, and the highest that differs.
-    unsigned kand = ~0u, kor = 0u;
+    // Pruning: at least need lanes hold a key at or above the need-th largest
+    // lane maximum, so no key below it can be selected. A short search over
+    // the lane maxima gives a bound B no larger than that value (its bits
+    // below the 8 highest that differ among the maxima are left 0); keys
+    // under B are dropped, and when at most 128 remain they are packed into
+    // two registers per lane (through this wave's LDS buffer, whose
+    // operations complete in order), so each step of the exact search
+    // compares 2 values per lane instead of PER.
+    bool packed = false, c1_empty = false;
+    unsigned c[2] = {0u, 0u};
+    if (PER >= 2 && need >= 1) {
+      unsigned lm = 0u;
 #pragma unroll
-    for (int i = 0; i < PER; ++i)
-      if (key[i] > 0u) {
-        kand &= key[i];
-        kor |= key[i];
+      for (int i = 0; i < PER; ++i) lm = max(lm, key[i]);
+      if (__popcll(__ballot(lm > 0u)) >= need) {
+        const unsigned land = __builtin_amdgcn_readfirstlane(wave_and_u(lm > 0u ? lm : ~0u));
+        const unsigned lor = __builtin_amdgcn_readfirstlane(wave_or_u(lm));
+        unsigned B = land;   // every lane maximum equal
+        if (land != lor) {
+          const int ltop = 31 - __clz(land ^ lor);
+          B = ltop == 31 ? 0u : land & ~((2u << ltop) - 1u);
+          for (int bit = ltop; bit >= 0 && bit > ltop - 8; --bit) {
+            const unsigned Bc = B | (1u << bit);
+            if (__popcll(__ballot(lm >= Bc)) >= need) B = Bc;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+          if (key[i] < B) key[i] = 0u;
+        const int C = wave_count<PER>([&](int i) { return key[i] > 0u; });
+        if (C <= 128) {
+          const unsigned long long ltm = (1ull << lane) - 1ull;
+          int base = 0;
+#pragma unroll
+          for (int i = 0; i < PER; ++i) {
+            // non-survivors write to their lane's spare slot (no branch)
+            const unsigned long long m = __ballot(key[i] > 0u);
+            pack[key[i] > 0u ? base + __popcll(m & ltm) : 128 + lane] = key[i];
+            base += __popcll(m);
+          }
+          c[0] = lane < C ? pack[lane] : 0u;
+          c[1] = lane + 64 < C ? pack[lane + 64] : 0u;
+          packed = true;
+          c1_empty = C <= 64;
+        }
       }
-    kand = __builtin_amdgcn_readfirstlane(wave_and_u(kand));
-    kor = __builtin_amdgcn_readfirstlane(wave_or_u(kor));
-    const unsigned diff = kand ^ kor;
-    const int top = diff ? 31 - __clz(diff) : -1;
-    T = top >= 0 ? kand & ~((2u << top) - 1u) : kand;   // 2u << 31 wraps to 0: all bits
-    if (top == 31) T = 0u;
-    for (int bit = top; bit >= 0; --bit) {
-      const unsigned Tc = T | (1u << bit);
-      if (wave_count<PER>([&](int i) { return key[i] >= Tc; }) >= need) T = Tc;
     }
-    take_ties = need - wave_count<PER>([&](int i) { return key[i] > T; });
+    // Bits common to every remaining candidate (or packed value), then the
+    // threshold with them set and the highest bit that differs.
+    auto common_prefix = [&](int& top_out) -> unsigned {
+      unsigned kand = ~0u, kor = 0u;
+      if (packed) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          if (c[i] > 0u) {
+            kand &= c[i];
+            kor |= c[i];
+          }
+      } else {
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+          if (key[i] > 0u) {
+            kand &= key[i];
+            kor |= key[i];
+          }
+      }
+      kand = wave_and_u(kand);
+      kor = wave_or_u(kor);
+      const unsigned diff = kand ^ kor;
+      const int top = diff ? 31 - __clz(diff) : -1;
+      top_out = top;
+      if (top == 31) return 0u;
+      return top >= 0 ? kand & ~((2u << top) - 1u) : kand;   // 2u << 31 wraps to 0: all bits
+    };
+    if (packed && c1_empty) {
+      // At most 64 candidates left, one per lane: a bitonic sort across the
+      // lanes (descending; vector work only) puts the need-th largest key in
+      // lane need - 1.
+      unsigned v = c[0];
+#pragma unroll
+      for (int k = 2; k <= 64; k <<= 1)
+#pragma unroll
+        for (int jj = k >> 1; jj > 0; jj >>= 1) {
+          const unsigned o = (unsigned)__shfl_xor((int)v, jj);
+          const bool keep_max = ((lane & jj) == 0) == ((lane & k) == 0);
+          v = keep_max ? max(v, o) : min(v, o);
+        }
+      T = (unsigned)__builtin_amdgcn_readlane((int)v, need - 1);
+      take_ties = need - wave_count<1>([&](int) { return c[0] > T; });
+    } else if (packed) {
+      int top;
+      T = common_prefix(top);
+      for (int bit = top; bit >= 0; --bit) {
+        const unsigned Tc = T | (1u << bit);
+        if (wave_count<2>([&](int i) { return c[i] >= Tc; }) >= need) T = Tc;
+      }
+      take_ties = need - wave_count<2>([&](int i) { return c[i] > T; });
+    } else {
+      int top;
+      T = common_prefix(top);
+      for (int bit = top; bit >= 0; --bit) {
+        const unsigned Tc = T | (1u << bit);
+        if (wave_count<PER>([&](int i) { return key[i] >= Tc; }) >= need) T = Tc;
+      }
+      take_ties = need - wave_count<PER>([&](int i) { return key[i] > T; });
+    }
+    T = __builtin_amdgcn_readfirstlane(T);
+    take_ties = __builtin_amdgcn_readfirstlane(take_ties);
   }
 
   const unsigned long long lt = (1ull << lane) - 1ull;
@@ -142,6 +258,9 @@ __device__ __forceinline__ void topk_row(const Geom& g, const float* block_logit
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int j = lane + 64 * i;
+    // a slot with no key left (after pruning most are empty) selects nothing
+    // unless it holds the row's own block
+    if (PER > 1 && !(force_own && own >> 6 == i) && __ballot(key[i] > 0u) == 0ull) continue;
     bool s;
     if (all) {
       s = key[i] > 0u;

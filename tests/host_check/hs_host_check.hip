@@ -286,6 +286,15 @@ void check_problem(const Spec& s, std::mt19937& rng) {
             items += n > 0;
             ++g_items_checked;
           }
+      if (op == hs::kGather) {
+        // the gather's rows lie within the causal ones; items of more than
+        // split_rows rows split, adding at most ceil(B Sq top_k / split_rows)
+        const long sel = (long)s.B * s.Sq * top_k;
+        CHECK(L.split_rows >= 128 && sel / L.split_rows <= 8192, "split_rows %d", L.split_rows);
+        items += (sel + L.split_rows - 1) / L.split_rows;
+      } else {
+        CHECK(L.split_rows == 0, "split_rows %d outside the gather", L.split_rows);
+      }
       CHECK(L.items == items, "items %d, brute force %ld", L.items, items);
       const size_t offs[] = {L.dsum, L.sink_part, L.first, L.nrows, L.pre, L.part, L.total};
       for (size_t i = 0; i + 1 < sizeof(offs) / sizeof(offs[0]); ++i)
