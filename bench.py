@@ -188,7 +188,7 @@ def row_key_counts(p, idx_cpu=None):
     the gather over the selected blocks (when indices are given), and the
     distinct KV rows each operation touches per batch entry."""
     causal, window, gather = [], [], []
-    kv_rows = {"score": 0, "swa": 0}
+    kv_rows = {"score": 0, "swa": 0, "gather": 0}
     for b, (L, docs, blocks) in enumerate(host_blocks(p)):
         pos = np.arange(L - p.Sq, L)
         lo = np.zeros_like(pos)
@@ -203,13 +203,18 @@ def row_key_counts(p, idx_cpu=None):
         if idx_cpu is not None:
             st = np.array([x[0] for x in blocks]); en = np.array([x[1] for x in blocks])
             g = np.zeros(p.Sq, dtype=np.int64)
+            used = np.zeros(len(blocks), dtype=bool)   # blocks some row gathers from
             for k in range(idx_cpu.shape[-1]):
                 j = idx_cpu[b, :, k].astype(np.int64)
                 ok = (j >= 0) & (j < len(blocks))
                 jj = np.where(ok, j, 0)
                 a = np.maximum(st[jj], lo); e = np.minimum(en[jj] - 1, pos)
-                g += np.where(ok, np.clip(e - a + 1, 0, None), 0)
+                n = np.where(ok, np.clip(e - a + 1, 0, None), 0)
+                g += n
+                used[jj[n > 0]] = True
             gather.append(g)
+            # distinct KV rows of the gathered blocks (each block's rows at most once)
+            kv_rows["gather"] += int((en - st)[used].sum())
     cat = lambda x: np.concatenate(x) if x else None
     return cat(causal), cat(window), cat(gather), kv_rows
 
@@ -355,15 +360,16 @@ def suite_config(c, dev, stream, peaks, oracle_budget):
         "topk": (0, p.B * p.Sq * (NB + p.top_k) * 4),
         "score_topk_fused": (int(causal.sum()) * H * fpp,
                              qb + kv_rows["score"] * p.Dk * es + ob + lb + p.B * p.Sq * NB * 4),
-        # compulsory bytes: every KV row at most once (the per-token selected rows,
-        # reported separately, are served largely from L2 and the MALL)
+        # compulsory bytes: every gathered KV row at most once (the per-token
+        # selected rows, reported separately, are served largely from L2 and
+        # the MALL)
         "sparse_gather": (int(gather.sum()) * H * fpp,
-                          qb + ob + lb + p.B * p.Sq * p.top_k * 4 + kv_rows["score"] * p.Dk * es),
+                          qb + ob + lb + p.B * p.Sq * p.top_k * 4 + kv_rows["gather"] * p.Dk * es),
         "swa": (int(window.sum()) * H * fpp, qb + kv_rows["swa"] * p.Dk * es + ob + lb),
     }
     work["swa_sparse"] = (int(window.sum()) * H * fpp + int(gather.sum()) * H * fpp,
-                          qb + kv_rows["score"] * p.Dk * es + 2 * (ob + lb) +
-                          p.B * p.Sq * p.top_k * 4)
+                          qb + max(kv_rows["swa"], kv_rows["gather"]) * p.Dk * es +
+                          2 * (ob + lb) + p.B * p.Sq * p.top_k * 4)
     l2_served = {"sparse_gather": qb + ob + lb + int(gather.sum()) * p.Dk * es}
     # Gradients: five contractions per pair (S recomputed, dP, dQ, dK, dV), i.e.
     # 2 (3 Dk + 2 Dv) flops; bytes: q, kv rows, out, dout, lse, dq and dkv in fp32.
@@ -372,7 +378,7 @@ def suite_config(c, dev, stream, peaks, oracle_budget):
     work["block_score_bwd"] = (int(causal.sum()) * H * fpb,
                                gb + kv_rows["score"] * p.Dk * (es + 4))
     work["sparse_gather_bwd"] = (int(gather.sum()) * H * fpb,
-                                 gb + p.B * p.Sq * p.top_k * 4 + kv_rows["score"] * p.Dk * (es + 4))
+                                 gb + p.B * p.Sq * p.top_k * 4 + kv_rows["gather"] * p.Dk * (es + 4))
     work["swa_bwd"] = (int(window.sum()) * H * fpb, gb + kv_rows["swa"] * p.Dk * (es + 4))
     peak_f = PEAK_BF16_TFLOPS if p.dtype == "bf16" else PEAK_F32_TFLOPS
     meas_f = peaks["mfma_bf16_tflop_s"] if p.dtype == "bf16" else None

@@ -183,14 +183,27 @@ void attn_bf16_kernel(AttnArgs a) {
 
   // Tile sequence: a block range, or the listed blocks that intersect the
   // allowed key range (compacted in order of the list).
+  // The selection's load first, then the Q loads, so that the Q loads are
+  // in flight while the tile list waits for the selection.
+  int jsel = -1;
+  if (OP == kGather || OP == kSwaSparse) {
+    if (lane < a.top_k) jsel = a.block_idx[row * a.top_k + lane];
+  }
+  // Q rows of this wave as MFMA B operands: lane holds q[row, head, 32ks + 8grp .. +8].
+  bf16x8 qreg[KSTEPS];
+  {
+    const bf16* qp = a.q + (row * H + head) * DK + 8 * grp;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) qreg[ks] = *(const bf16x8*)(qp + 32 * ks);
+  }
+
   int ntiles;
   if (OP == kGather || OP == kSwaSparse) {
     // Every wave builds its own copy of the list (same indices, same result),
-    // so no workgroup barrier separates it from the first copy and Q loads.
-    int j = -1;
+    // so no workgroup barrier separates it from the first copy.
+    const int j = jsel;
     bool ok = false;
     if (lane < a.top_k) {
-      j = a.block_idx[row * a.top_k + lane];
       if (j >= 0 && j < nb_b && block_in_doc(g, rdoc, j)) {
         const Blk bk = block_rows_in(g, rdoc, j);
         ok = !(bk.start > rr.hi || bk.start + bk.len - 1 < rr.lo);
@@ -242,14 +255,6 @@ void attn_bf16_kernel(AttnArgs a) {
     const int j0 = tile_block(t_begin);
     const Blk b0 = block_rows_in(g, rdoc, j0);
     stage_tile(buf_a, block_base(j0), PAGED ? 0 : b0.start, b0.len, wave, lane);
-  }
-
-  // Q rows of this wave as MFMA B operands: lane holds q[row, head, 32ks + 8grp .. +8].
-  bf16x8 qreg[KSTEPS];
-  {
-    const bf16* qp = a.q + (row * H + head) * DK + 8 * grp;
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) qreg[ks] = *(const bf16x8*)(qp + 32 * ks);
   }
 
   const float sk = (a.sink != nullptr && split == 0) ? a.sink[head] * kLog2e : -INFINITY;

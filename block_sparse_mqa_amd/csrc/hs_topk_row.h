@@ -143,10 +143,10 @@ __device__ __forceinline__ void topk_row(const Geom& g, const float* block_logit
         if (lane + 64 * i == own) key[i] = 0u;
     }
     const int need = force_own ? K - 1 : K;
-    // Pruning: at least need lanes hold a key at or above the need-th largest
-    // lane maximum, so no key below it can be selected. A short search over
-    // the lane maxima gives a bound B no larger than that value (its bits
-    // below the 8 highest that differ among the maxima are left 0); keys
+    // Pruning: at least need keys lie at or above the need-th largest of the
+    // lanes' two largest keys, so no key below it can be selected. A short
+    // search over those 128 values gives a bound B no larger than that value
+    // (its bits below the 8 highest that differ among them are left 0); keys
     // under B are dropped, and when at most 128 remain they are packed into
     // two registers per lane (through this wave's LDS buffer, whose
     // operations complete in order), so each step of the exact search
@@ -154,19 +154,25 @@ __device__ __forceinline__ void topk_row(const Geom& g, const float* block_logit
     bool packed = false, c1_empty = false;
     unsigned c[2] = {0u, 0u};
     if (PER >= 2 && need >= 1) {
-      unsigned lm = 0u;
+      // each lane's two largest keys: at least need keys lie at or above the
+      // need-th largest of these 128 values, a tighter bound than the lane
+      // maxima alone
+      unsigned lm = 0u, lm2 = 0u;
 #pragma unroll
-      for (int i = 0; i < PER; ++i) lm = max(lm, key[i]);
-      if (__popcll(__ballot(lm > 0u)) >= need) {
-        const unsigned land = __builtin_amdgcn_readfirstlane(wave_and_u(lm > 0u ? lm : ~0u));
-        const unsigned lor = __builtin_amdgcn_readfirstlane(wave_or_u(lm));
-        unsigned B = land;   // every lane maximum equal
+      for (int i = 0; i < PER; ++i) {
+        lm2 = max(lm2, min(lm, key[i]));
+        lm = max(lm, key[i]);
+      }
+      if (__popcll(__ballot(lm > 0u)) + __popcll(__ballot(lm2 > 0u)) >= need) {
+        const unsigned land = wave_and_u((lm > 0u ? lm : ~0u) & (lm2 > 0u ? lm2 : ~0u));
+        const unsigned lor = wave_or_u(lm | lm2);
+        unsigned B = land;   // every value equal
         if (land != lor) {
           const int ltop = 31 - __clz(land ^ lor);
           B = ltop == 31 ? 0u : land & ~((2u << ltop) - 1u);
           for (int bit = ltop; bit >= 0 && bit > ltop - 8; --bit) {
             const unsigned Bc = B | (1u << bit);
-            if (__popcll(__ballot(lm >= Bc)) >= need) B = Bc;
+            if (__popcll(__ballot(lm >= Bc)) + __popcll(__ballot(lm2 >= Bc)) >= need) B = Bc;
           }
         }
 #pragma unroll
