@@ -538,19 +538,44 @@ void attn_bf16_kernel(AttnArgs a) {
     }
   }
 
-  if (OP == kScore) {
-    __syncthreads();
-    if (j_prev >= 0 && threadIdx.x == 0) {
-      float v = bl_slot[par ^ 1][0];
+  // every wave is past the last tile and every copy has landed: the tile
+  // buffers are free for the output transpose below
+  __syncthreads();
+  if (OP == kScore && j_prev >= 0 && threadIdx.x == 0) {
+    float v = bl_slot[par ^ 1][0];
 #pragma unroll
-      for (int k = 1; k < NW; ++k) v = fmaxf(v, bl_slot[par ^ 1][k]);
-      a.block_logit[row * g.NB + j_prev] = v * kLn2;
-    }
+    for (int k = 1; k < NW; ++k) v = fmaxf(v, bl_slot[par ^ 1][k]);
+    a.block_logit[row * g.NB + j_prev] = v * kLn2;
   }
 
   const float l_tot = sum_xor32(sum_xor16(l_run));
   // oacc[db][i] is O[row l16][dim 16db + 4grp + i].
-  if (!SPLIT) {
+  if (!SPLIT && (OP != kSwaSparse || a.out_mix == nullptr)) {
+    // The wave's 16 x 512 bf16 outputs go through LDS (its own 16.25 KB of
+    // the free tile buffer, head rows 1040 B apart against bank conflicts)
+    // so that each store writes one head's whole 1 KB row: a lane's own
+    // values are 8 B pieces of 16 different rows, which stored directly cost
+    // 16 memory segments per store instruction.
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    constexpr int OROW = 2 * DV + 16;
+    HS_LDS char* ob = (HS_LDS char*)buf_a + wave * (RW * OROW);
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+      bf16x4 v;
+      v[0] = (bf16)(oacc[db][0] * inv);
+      v[1] = (bf16)(oacc[db][1] * inv);
+      v[2] = (bf16)(oacc[db][2] * inv);
+      v[3] = (bf16)(oacc[db][3] * inv);
+      *(HS_LDS bf16x4*)(ob + l16 * OROW + 2 * (16 * db + 4 * grp)) = v;
+    }
+    // (LDS operations of one wave complete in order)
+    bf16* orow = a.out + (row * H + wave * RW) * DV + 8 * lane;
+#pragma unroll
+    for (int h = 0; h < RW; ++h)
+      *(bf16x8*)(orow + h * DV) = *(const HS_LDS bf16x8*)(ob + h * OROW + 16 * lane);
+    if (grp == 0)
+      a.lse[row * H + head] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
+  } else if (!SPLIT) {
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     bf16* op = a.out + (row * H + head) * DV + 4 * grp;
 #pragma unroll
