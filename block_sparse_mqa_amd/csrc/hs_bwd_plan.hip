@@ -55,13 +55,20 @@ BwdLayout bwd_layout(const Geom& g, int op, int top_k, int window, bool store_ds
     L.chunk_rows = R;
     L.n_chunks = (g.Sq + R - 1) / R;
     L.items = (int)items_for(R);
-    if (op == kGather) {
-      // A block that many rows of a chunk selected (the rows' own and recent
-      // blocks) would make one long item among short ones; such an item is
-      // split into items of at most split_rows rows, whose partials the
-      // reduction adds in order. Each extra item takes split_rows rows, so
-      // at most B * Sq * top_k / split_rows are added (capped near 8192).
-      const long sel = (long)g.B * g.Sq * std::max(top_k, 1);
+    if (op == kGather || op == kSwa) {
+      // Items differ in length: a gather block that many rows of a chunk
+      // selected (the rows' own and recent blocks) against one that a few
+      // did; a window block whose rows fill a chunk against one at a chunk's
+      // edge. Long items among short ones leave compute units idle at the
+      // end of the launch, so items are split into items of at most
+      // split_rows rows, whose partials the reduction adds in order. Each
+      // extra item takes split_rows of the B * Sq * per (row, block) pairs,
+      // per = top_k, or for the window the most blocks W keys can meet, so
+      // at most that many / split_rows are added (capped near 8192).
+      const long per = op == kGather
+                           ? std::max(top_k, 1)
+                           : std::min<long>((window - 1 + (long)g.BS - 1) / g.BS + 1, g.NB);
+      const long sel = (long)g.B * g.Sq * per;
       L.split_rows = (int)std::max<long>(128, (sel + 8191) / 8192);
       L.items += (int)((sel + L.split_rows - 1) / L.split_rows);
     }

@@ -269,7 +269,7 @@ void check_problem(const Spec& s, std::mt19937& rng) {
       CHECK(L.chunk_rows >= 64 && (L.chunk_rows & (L.chunk_rows - 1)) == 0, "chunk_rows %d",
             L.chunk_rows);
       const int oc = op == hs::kSwa ? hs::kSwa : hs::kScore;
-      long items = 0;
+      long items = 0, split_items = 0;
       for (int b = 0; b < s.B; ++b)
         for (int c = 0; c < L.n_chunks; ++c)
           for (int j = 0; j < g.NB; ++j) {
@@ -284,6 +284,7 @@ void check_problem(const Spec& s, std::mt19937& rng) {
             CHECK(n == 0 || (first >= c * L.chunk_rows && first + n <= std::min(s.Sq, (c + 1) * L.chunk_rows)),
                   "item rows outside its chunk");
             items += n > 0;
+            split_items += hs::items_of(n, L.split_rows);
             ++g_items_checked;
           }
       if (op == hs::kGather) {
@@ -292,8 +293,18 @@ void check_problem(const Spec& s, std::mt19937& rng) {
         const long sel = (long)s.B * s.Sq * top_k;
         CHECK(L.split_rows >= 128 && sel / L.split_rows <= 8192, "split_rows %d", L.split_rows);
         items += (sel + L.split_rows - 1) / L.split_rows;
+      } else if (op == hs::kSwa) {
+        // window items split the same way: at most ceil(B Sq per / split_rows)
+        // more, per = the most blocks a window meets; the exact split count
+        // must fit the layout
+        const long per = std::min<long>((window - 1 + 63) / 64 + 1, g.NB);
+        const long sel = (long)s.B * s.Sq * per;
+        CHECK(L.split_rows >= 128 && sel / L.split_rows <= 8192, "split_rows %d", L.split_rows);
+        items += (sel + L.split_rows - 1) / L.split_rows;
+        CHECK(split_items <= items, "window items after the split %ld, layout %ld", split_items,
+              items);
       } else {
-        CHECK(L.split_rows == 0, "split_rows %d outside the gather", L.split_rows);
+        CHECK(L.split_rows == 0, "split_rows %d for the causal gradient", L.split_rows);
       }
       CHECK(L.items == items, "items %d, brute force %ld", L.items, items);
       const size_t offs[] = {L.dsum, L.sink_part, L.first, L.nrows, L.pre, L.part, L.total};

@@ -195,6 +195,53 @@ def test_long_context_sampled():
     say("[gpu] gradients long context: ok")
 
 
+def test_split_work_items_against_oracle():
+    """Key-block work items longer than split_rows (128) rows are split and
+    their partials added in order. At B = 4, S = 4096 the rows are chunked by
+    512 for the gather and by 256 for the window (about 1024 items each), so:
+    - rows 0 .. 511 all select block 0 (the rest their own and previous
+      blocks): the gather's item of block 0 has 512 rows, four parts; dq of
+      those rows and block 0's dkv, which only they reach, are compared with
+      the oracle;
+    - a window of 1024 gives middle blocks 256-row items (two parts each);
+      block 20's dkv is compared from every row that attends it (1280 to
+      2366), with dq of those rows, for both workspaces."""
+    p = _mla("split_items", 4096, 905, 2, 1024, B=4)
+    d = Dev(p)
+    dout_cpu = inputs.make_dout(p, seed=906)
+    dout = dout_cpu.cuda()
+    S = p.Sq
+    own = np.arange(S) // 64
+    sel = np.stack([np.where(np.arange(S) < 512, 0, own - 1), own], axis=1)
+    sel[sel[:, 0] == sel[:, 1], 0] = -1          # distinct ids, -1 for the rest
+    sel[sel < 0] = -1
+    idx_cpu = np.broadcast_to(sel, (p.B, S, 2)).astype(np.int32).copy()
+    idx = torch.from_numpy(idx_cpu).cuda()
+    g = _gpu_grads(d, "gather", dout, idx, 2)
+    torch.cuda.synchronize()
+    rows = np.arange(512)
+    got_dq = np64(g[0][:, :512])
+    got_dkv = np64(g[1][:, :64])
+    del g
+    say("[gpu] split items: gather on the GPU done, oracle on rows 0 .. 511")
+    w = _oracle_grads(d, "gather", dout_cpu[:, rows], idx_cpu, rows=rows)
+    e = [_grad_close(got_dq, w[0], "bf16", "gather dq"),
+         _grad_close(got_dkv, w[1][:, :64], "bf16", "gather dkv block 0")]
+    rows = np.arange(1280, 1280 + 64 + p.window - 1)
+    for v in ("swa", "swa_recompute"):
+        gw = _gpu_grads(d, v, dout)
+        torch.cuda.synchronize()
+        got_dq = np64(gw[0][:, torch.from_numpy(rows).cuda()])
+        got_dkv = np64(gw[1][:, 1280:1344])
+        del gw
+        if v == "swa":
+            say(f"[gpu] split items: window on the GPU done, oracle on {len(rows)} rows")
+            ww = _oracle_grads(d, "swa", dout_cpu[:, rows], rows=rows)
+        e += [_grad_close(got_dq, ww[0], "bf16", f"{v} dq"),
+              _grad_close(got_dkv, ww[1][:, 1280:1344], "bf16", f"{v} dkv block 20")]
+    say(f"[gpu] split work items: worst {max(e):.2e}")
+
+
 def test_gradients_in_captured_graph():
     """The gradient calls allocate nothing and write every workspace word before
     reading it, so one captured graph replays correctly with new upstream
