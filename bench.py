@@ -344,7 +344,8 @@ def suite_config(c, dev, stream, peaks, oracle_budget):
     dkv = torch.empty((p.B, p.Skv, p.Dk), dtype=torch.float32, device=dev)
     dsink = torch.empty((p.H,), dtype=torch.float32, device=dev)
     wb1, wb3, wb4 = hs.score_bwd_workspace(prob, store_ds=True), \
-        ws(hs.HS_OP_SPARSE_GATHER_BWD, top_k=p.top_k), hs.swa_bwd_workspace(prob, p.window, store_ds=True)
+        hs.sparse_gather_bwd_workspace(prob, p.top_k, store_ds=True), \
+        hs.swa_bwd_workspace(prob, p.window, store_ds=True)
     calls["block_score_bwd"] = lambda: hs.hs_block_score_bwd(
         prob, q, kv, sink, *fwd["block_score"], dout, dq, dkv, dsink, wb1, stream)
     calls["sparse_gather_bwd"] = lambda: hs.hs_sparse_gather_bwd(
@@ -474,10 +475,10 @@ def write_suite_md(path, peaks, results, args):
     L.append("`*_bwd` are the gradient calls (dq, dkv and the sink gradient) of the three attention "
              "operations, each fed its own forward outputs; their flops are 2 (3 Dk + 2 Dv) per "
              "(query-head, key) pair (score recomputed, dP, dQ, dK, dV) and their bytes count q, the "
-             "KV rows, out, dout, lse and the fp32 dq and dkv. With the larger workspaces (chosen "
-             "when they fit in half the free memory) the causal and window calls store the score "
-             "gradients and execute exactly the counted flops; the gather call and the fp32 shapes "
-             "recompute the scores and dP in both of their kernels, 1.4 times the counted flops.\n")
+             "KV rows, out, dout, lse and the fp32 dq and dkv. With the larger workspaces used here "
+             "the bf16 calls store the score gradients and execute exactly the counted flops; the "
+             "fp32 shapes recompute the scores and dP in both of their kernels, 1.4 times the "
+             "counted flops.\n")
     L.append("`swa_sparse` is `hs_swa_sparse_fwd`: the window and the selected-block branches of a "
              "sliding-window layer in one call (separate outputs), its work the sum of `swa` and "
              "`sparse_gather`.\n")
@@ -623,7 +624,9 @@ def main():
         dsink = torch.empty((p.H,), dtype=torch.float32, device=dev)
         wb1 = hs.score_bwd_workspace(prob, store_ds=True)
         stored = wb1.numel() * 4 >= hs.hs_workspace_size(prob, hs.HS_OP_BLOCK_SCORE_BWD_STORE_DS)
-        wb3 = ws_for(hs.HS_OP_SPARSE_GATHER_BWD, top_k=p.top_k)
+        wb3 = hs.sparse_gather_bwd_workspace(prob, p.top_k, store_ds=True)
+        stored3 = wb3.numel() * 4 >= hs.hs_workspace_size(prob, hs.HS_OP_SPARSE_GATHER_BWD_STORE_DS,
+                                                          top_k=p.top_k)
         wb4 = hs.swa_bwd_workspace(prob, p.window, store_ds=True)
         stored4 = wb4.numel() * 4 >= hs.hs_workspace_size(prob, hs.HS_OP_SWA_BWD_STORE_DS,
                                                           window=p.window)
@@ -635,6 +638,7 @@ def main():
             "swa_bwd": lambda: hs.hs_swa_bwd(
                 prob, q, kv, sink, p.window, osw, lsw, dout, dq, dkv, dsink, wb4, stream)}
         grads = {"ms": {}, "block_score_bwd_dq": "stored dS" if stored else "recomputed dS",
+                 "sparse_gather_bwd_dq": "stored dS" if stored3 else "recomputed dS",
                  "swa_bwd_dq": "stored dS" if stored4 else "recomputed dS"}
         for k, fn in gcalls.items():
             fn()

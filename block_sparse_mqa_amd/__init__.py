@@ -31,6 +31,7 @@ HS_OP_BLOCK_SCORE, HS_OP_SPARSE_GATHER, HS_OP_SWA = 0, 1, 2
 HS_OP_BLOCK_SCORE_BWD, HS_OP_SPARSE_GATHER_BWD, HS_OP_SWA_BWD = 3, 4, 5
 HS_OP_BLOCK_SCORE_BWD_STORE_DS, HS_OP_SWA_BWD_STORE_DS = 6, 7
 HS_OP_SWA_SPARSE = 8
+HS_OP_SPARSE_GATHER_BWD_STORE_DS = 9
 
 EXPORTS = ("hs_num_blocks", "hs_workspace_size", "hs_block_score_fwd", "hs_topk_blocks",
            "hs_block_score_topk_fwd", "hs_block_score_topk_fwd_noalloc", "hs_sparse_gather_fwd",
@@ -472,6 +473,13 @@ def swa_bwd_workspace(prob, window, store_ds=False):
     return _stored_ds_workspace(prob, HS_OP_SWA_BWD, HS_OP_SWA_BWD_STORE_DS, store_ds, window)
 
 
+def sparse_gather_bwd_workspace(prob, top_k, store_ds=False):
+    """Workspace of hs_sparse_gather_bwd, chosen as for score_bwd_workspace
+    (the stored form is 8 KB per row and per selection entry)."""
+    return _workspace(prob, HS_OP_SPARSE_GATHER_BWD_STORE_DS if store_ds else HS_OP_SPARSE_GATHER_BWD,
+                      top_k=top_k)
+
+
 def block_score_bwd(prob, q, kv, sink, out, lse, dout, stream=None, store_ds=False, dlse=None):
     """Gradients (dq, dkv, dsink) of the causal attention of block_score;
     dsink is None without a sink. All float32. store_ds picks the workspace
@@ -482,11 +490,13 @@ def block_score_bwd(prob, q, kv, sink, out, lse, dout, stream=None, store_ds=Fal
     return dq, dkv, dsink
 
 
-def sparse_gather_bwd(prob, q, kv, sink, block_idx, top_k, out, lse, dout, stream=None, dlse=None):
-    """Gradients (dq, dkv, dsink) of sparse_gather for the given selection."""
+def sparse_gather_bwd(prob, q, kv, sink, block_idx, top_k, out, lse, dout, stream=None, dlse=None,
+                      store_ds=False):
+    """Gradients (dq, dkv, dsink) of sparse_gather for the given selection.
+    store_ds picks the workspace (sparse_gather_bwd_workspace)."""
     dq, dkv, dsink = _grad_buffers(prob, q, sink)
     hs_sparse_gather_bwd(prob, q, kv, sink, block_idx, top_k, out, lse, dout, dq, dkv, dsink,
-                         _workspace(prob, HS_OP_SPARSE_GATHER_BWD, top_k=top_k), stream, dlse=dlse)
+                         sparse_gather_bwd_workspace(prob, top_k, store_ds), stream, dlse=dlse)
     return dq, dkv, dsink
 
 

@@ -416,10 +416,10 @@ hs_status launch_bwd(int op, const hs_problem* p, const void* q, const void* kv,
     return fail(HS_ERR_INVALID_ARG, "window must be >= 1 (got %d)", window);
   const bool bf16 = p->dtype == HS_BF16;
   const int kop = op == HS_OP_SWA ? hs::kSwa : op == HS_OP_SPARSE_GATHER ? hs::kGather : hs::kScore;
-  // The stored-score path (causal and window, bf16) runs when the workspace
-  // also holds the score gradients; otherwise dq recomputes them.
+  // The stored-score path (bf16) runs when the workspace also holds the score
+  // gradients; otherwise dq recomputes them.
   hs::BwdLayout L = hs::bwd_layout(g, kop, top_k, window, false);
-  if (bf16 && kop != hs::kGather && ws) {
+  if (bf16 && ws) {
     const hs::BwdLayout Ls = hs::bwd_layout(g, kop, top_k, window, true);
     if (ws_bytes >= Ls.total) L = Ls;
   }
@@ -457,6 +457,7 @@ hs_status launch_bwd(int op, const hs_problem* p, const void* q, const void* kv,
       a.g_total = reinterpret_cast<int*>(w + L.total_g);
       a.g_off = reinterpret_cast<int*>(w + L.off_g);
       a.g_rows = reinterpret_cast<int*>(w + L.rows);
+      if (L.store_ds) a.g_pos = reinterpret_cast<int*>(w + L.pos);
     }
     a.part = reinterpret_cast<float*>(w + L.part);
     if (L.store_ds) {
@@ -480,7 +481,7 @@ hs_status launch_bwd(int op, const hs_problem* p, const void* q, const void* kv,
 
 extern "C" {
 
-int32_t hs_version(void) { return 201; }
+int32_t hs_version(void) { return 202; }
 
 const char* hs_status_string(int32_t status) {
   switch (status) {
@@ -507,7 +508,7 @@ hs_status hs_workspace_size(const hs_problem* p, int32_t op, int32_t top_k, int3
   hs_status st = prepare(p, g);
   if (st != HS_OK) return st;
   if (!bytes) return fail(HS_ERR_INVALID_ARG, "bytes is NULL");
-  if (op < HS_OP_BLOCK_SCORE || op > HS_OP_SWA_SPARSE)
+  if (op < HS_OP_BLOCK_SCORE || op > HS_OP_SPARSE_GATHER_BWD_STORE_DS)
     return fail(HS_ERR_INVALID_ARG, "unknown op %d", op);
   if (op == HS_OP_SWA_SPARSE) {
     // the two branches run one after the other when they do not run as one
@@ -525,15 +526,17 @@ hs_status hs_workspace_size(const hs_problem* p, int32_t op, int32_t top_k, int3
     if (p->doc_bounds_device)
       return fail(HS_ERR_UNSUPPORTED, "gradients take host document bounds");
     const int kop = (op == HS_OP_SWA_BWD || op == HS_OP_SWA_BWD_STORE_DS) ? hs::kSwa
-                    : op == HS_OP_SPARSE_GATHER_BWD                       ? hs::kGather
-                                                                          : hs::kScore;
+                    : (op == HS_OP_SPARSE_GATHER_BWD || op == HS_OP_SPARSE_GATHER_BWD_STORE_DS)
+                        ? hs::kGather
+                        : hs::kScore;
     if (kop == hs::kGather && top_k < 1)
       return fail(HS_ERR_INVALID_ARG, "top_k must be >= 1 (got %d)", top_k);
     if (kop == hs::kGather && top_k > 64)
       return fail(HS_ERR_UNSUPPORTED, "top_k %d exceeds 64", top_k);
     if (kop == hs::kSwa && window < 1)
       return fail(HS_ERR_INVALID_ARG, "window must be >= 1 (got %d)", window);
-    const bool store = (op == HS_OP_BLOCK_SCORE_BWD_STORE_DS || op == HS_OP_SWA_BWD_STORE_DS) &&
+    const bool store = (op == HS_OP_BLOCK_SCORE_BWD_STORE_DS || op == HS_OP_SWA_BWD_STORE_DS ||
+                        op == HS_OP_SPARSE_GATHER_BWD_STORE_DS) &&
                        p->dtype == HS_BF16;
     *bytes = hs::bwd_layout(g, kop, top_k, window, store).total;
     return HS_OK;

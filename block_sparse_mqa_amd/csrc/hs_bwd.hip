@@ -302,7 +302,11 @@ __global__ __launch_bounds__(256) void bwd_gfill_kernel(BwdArgs a) {
     if (lane < a.top_k) {
       const int j = a.block_idx[((size_t)b * g.Sq + r) * a.top_k + lane];
       const RowRange rr = row_range(g, kGather, b, r, 0);
-      if (gather_hit(g, b, nb_b, rr, j)) a.g_rows[atomicAdd(&next[j], 1)] = r;
+      if (gather_hit(g, b, nb_b, rr, j)) {
+        const int at = atomicAdd(&next[j], 1);
+        a.g_rows[at] = r;
+        if (a.g_pos != nullptr) a.g_pos[at] = lane;  // the row's stored tile
+      }
     }
   }
 }
@@ -373,19 +377,24 @@ __device__ __forceinline__ bf16x8 frag_t(const char* base, int gs, int kk, int d
   return v;
 }
 
-// dq from the stored score gradients (causal or window): one workgroup per
-// pair of consecutive query rows (heaviest first), 8 waves, two per SIMD: wave w
-// owns heads 16 (w & 3) .. +15 of row r_hi - (w >> 2). Per tile only
-// dQ^T += K^T . dS^T remains, with dS^T read from the stored tile in operand
-// order (16 B per lane and k-step, the next tile's prefetched during the
-// current one). Both rows walk the union of their block ranges; a row takes
-// zero dS on a block outside its own range. Each copied K tile serves both
-// rows.
+// dq from the stored score gradients: one workgroup per pair of consecutive
+// query rows (heaviest first), 8 waves, two per SIMD: wave w owns heads
+// 16 (w & 3) .. +15 of row r_hi - (w >> 2). Per tile only dQ^T += K^T . dS^T
+// remains, with dS^T read from the stored tile in operand order (16 B per
+// lane and k-step, the next tile's prefetched during the current one). Both
+// rows walk one tile sequence and each copied K tile serves both; a row takes
+// zero dS on a tile it does not have. Causal and window: the union of the two
+// rows' block ranges. Gather: the union of their selections (the first row's
+// usable entries in list order, then the second row's other ones), built by
+// every wave in its own LDS list; a row's stored tile is its selection entry.
 template <int OP>
 __global__ __launch_bounds__(2 * bw::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_ds_bf16_kernel(BwdArgs a) {
   using namespace bw;
   __shared__ __attribute__((aligned(16))) char buf[2][TILE];
+  // gather: per wave, the union's blocks and each row's entry (-1: none)
+  __shared__ int ulist[OP == kGather ? 2 * NT / 64 : 1][128];
+  __shared__ int upos[OP == kGather ? 2 * NT / 64 : 1][2][128];
 
   const Geom& g = a.g;
   const int lane = threadIdx.x & 63;
@@ -399,8 +408,46 @@ void bwd_dq_ds_bf16_kernel(BwdArgs a) {
   const int r_lo = r_hi - 1;                       // -1: no second row
   const RowRange ra = row_range(g, OP, b, r_hi, a.window);
   const RowRange rb = r_lo >= 0 ? row_range(g, OP, b, r_lo, a.window) : ra;
-  const int jf = min(ra.j_first, rb.j_first), jl = max(ra.j_last, rb.j_last);
-  const int ntiles = jl - jf + 1;
+  int jf = min(ra.j_first, rb.j_first), jl = max(ra.j_last, rb.j_last);
+  int ntiles = jl - jf + 1;
+  if constexpr (OP == kGather) {
+    const int K = a.top_k;
+    const int nb_b = nb_of_entry(g, b);
+    int ja = -1, jb = -1;
+    if (lane < K) {
+      ja = a.block_idx[((size_t)b * g.Sq + r_hi) * K + lane];
+      if (r_lo >= 0) jb = a.block_idx[((size_t)b * g.Sq + r_lo) * K + lane];
+    }
+    const bool oka = lane < K && gather_hit(g, b, nb_b, ra, ja);
+    const bool okb = lane < K && r_lo >= 0 && gather_hit(g, b, nb_b, rb, jb);
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    const unsigned long long ma = __ballot(oka);
+    const int na = __popcll(ma);
+    if (oka) {
+      const int at = __popcll(ma & lt);
+      ulist[wave][at] = ja;
+      upos[wave][0][at] = lane;
+      upos[wave][1][at] = -1;
+    }
+    // the second row's entry that the first row also selected
+    const int jam = oka ? ja : -2;
+    int found = -1;
+    for (int k = 0; k < K; ++k)
+      if (okb && jb == __builtin_amdgcn_readlane(jam, k)) found = k;
+    // (LDS operations of one wave complete in order)
+    if (found >= 0) upos[wave][1][__popcll(ma & ((1ull << found) - 1ull))] = lane;
+    const bool only_b = okb && found < 0;
+    const unsigned long long mb = __ballot(only_b);
+    if (only_b) {
+      const int at = na + __popcll(mb & lt);
+      ulist[wave][at] = jb;
+      upos[wave][0][at] = -1;
+      upos[wave][1][at] = lane;
+    }
+    ntiles = na + __popcll(mb);
+    __builtin_amdgcn_wave_barrier();
+  }
+  auto tile_block = [&](int t) -> int { return OP == kGather ? ulist[wave][t] : jf + t; };
   // this wave's row
   const int r = rsel ? r_lo : r_hi;
   const bool has_row = r >= 0;
@@ -415,16 +462,25 @@ void bwd_dq_ds_bf16_kernel(BwdArgs a) {
     const char* src = (const char*)(kv_entry + (size_t)(bk.start + k) * DK) + 16 * cp_c8;
     issue(src, dst + wave * 1024);
   };
-  copy_tile(buf[0], block_rows(g, b, jf), [&](const char* src, char* dst) __attribute__((always_inline)) {
+  if (ntiles > 0)
+    copy_tile(buf[0], block_rows(g, b, tile_block(0)), [&](const char* src, char* dst) __attribute__((always_inline)) {
 #pragma unroll
-    for (int G = 0; G < 9; ++G) dma16(src + 128 * G, dst + G * GR);
-  });
+      for (int G = 0; G < 9; ++G) dma16(src + 128 * G, dst + G * GR);
+    });
   const long long base = has_row ? ds_row_base(a, b, r) : 0;
   const bf16* dsp = a.ds_tiles + (base * 4 + hw) * 2 * 512 + lane * 8;  // row tile t: + 4096 t
   const bf16x8 zero8 = {};
-  auto ds_load = [&](int j, bf16x8* d) __attribute__((always_inline)) {
-    if (has_row && j >= rr.j_first && j <= rr.j_last) {
-      const bf16* q = dsp + (size_t)(j - rr.j_first) * 4096;
+  // dS of tile t of the walk for this wave's row
+  auto ds_load = [&](int t, bf16x8* d) __attribute__((always_inline)) {
+    int e = -1;
+    if (OP == kGather) {
+      e = has_row ? upos[wave][rsel][t] : -1;
+    } else {
+      const int j = jf + t;
+      if (has_row && j >= rr.j_first && j <= rr.j_last) e = j - rr.j_first;
+    }
+    if (e >= 0) {
+      const bf16* q = dsp + (size_t)e * 4096;
       d[0] = *(const bf16x8*)q;
       d[1] = *(const bf16x8*)(q + 512);
     } else {
@@ -433,7 +489,7 @@ void bwd_dq_ds_bf16_kernel(BwdArgs a) {
     }
   };
   bf16x8 dnext[2], dcur[2];
-  ds_load(jf, dnext);
+  if (ntiles > 0) ds_load(0, dnext);
 
   f32x4 acc[DBK];
 #pragma unroll
@@ -441,15 +497,15 @@ void bwd_dq_ds_bf16_kernel(BwdArgs a) {
 
   for (int t = 0; t < ntiles; ++t) {
     char* cur = buf[t & 1];
-    const int j = jf + t;
+    const int tn = min(t + 1, ntiles - 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // tile t and its dS resident; tile t-1 consumed by every wave
     dcur[0] = dnext[0];
     dcur[1] = dnext[1];
-    ds_load(min(j + 1, jl), dnext);
+    ds_load(tn, dnext);
     // The copy of the next tile (on the last tile the current one again, into
     // the idle buffer) is spread over the stream.
-    const Blk nbk = block_rows(g, b, min(j + 1, jl));
+    const Blk nbk = block_rows(g, b, tile_block(tn));
     const int ck = min(8 * wave + (lane >> 3), nbk.len - 1);
     const char* cp_src = (const char*)(kv_entry + (size_t)(nbk.start + ck) * DK) + 16 * cp_c8;
     char* cp_dst = buf[(t + 1) & 1] + wave * 1024;
@@ -696,7 +752,7 @@ void bwd_dkv_bf16_kernel(BwdArgs a) {
   bf16* st_prev = nullptr;
   const int tr_off = (32 * (wave & 1) + 4 * grp + (l16 >> 2)) * 64 + 32 * (wave >> 1) + 8 * (l16 & 3);
   if (STORE) {
-    rbase = ds_row_base(a, b, row_at(0));
+    if (OP != kGather) rbase = ds_row_base(a, b, row_at(0));
     st_prev = a.ds_dummy + wave * 512 + lane * 8;
   }
 
@@ -708,9 +764,15 @@ void bwd_dkv_bf16_kernel(BwdArgs a) {
     const RowRange rr = row_range(g, OP, b, r, a.window);
     bf16* st_cur = nullptr;
     if (STORE) {
-      if (s > 0 && (s & 1) == 0) rbase += a.ds_stride > 0 ? a.ds_stride : prev_nt;
-      prev_nt = rr.j_last - rr.j_first + 1;
-      const long long slot = rbase + (j - rr.j_first);
+      long long slot;
+      if (OP == kGather) {
+        // the row's tile of this selection entry
+        slot = ((long long)b * g.Sq + r) * a.ds_stride + a.g_pos[base_i + (s >> 1)];
+      } else {
+        if (s > 0 && (s & 1) == 0) rbase += a.ds_stride > 0 ? a.ds_stride : prev_nt;
+        prev_nt = rr.j_last - rr.j_first + 1;
+        slot = rbase + (j - rr.j_first);
+      }
       st_cur = a.ds_tiles + ((slot * 4 + 2 * (s & 1) + (wave >> 1)) * 2 + (wave & 1)) * 512 + lane * 8;
     }
     const bool valid = kloc < blk.len && key >= rr.lo && key <= rr.hi;
@@ -834,14 +896,50 @@ void bwd_dkv_bf16_kernel(BwdArgs a) {
 }
 
 // dkv rows of entry b, 64 at a time: each row sums its block's partials in
-// chunk order; rows past the entry's valid length are zero.
+// chunk order; rows past the entry's valid length are zero. Without documents
+// the 64 rows are exactly one block (key k of block c is row 64 c + k), so a
+// thread keeps its 36 elements in registers and walks the block's items once:
+// per item 36 independent loads, and the workgroup reads each item's partial
+// as one contiguous 147 KB run. With documents a row's block is looked up per
+// element. Both add the partials in the same order.
 __global__ __launch_bounds__(256) void bwd_reduce_bf16_kernel(BwdArgs a) {
   using namespace bw;
   const Geom& g = a.g;
   const int chunks = (g.Skv + 63) / 64;
   const int b = blockIdx.x / chunks, c = blockIdx.x % chunks;
   const int L = kv_len_of(g, b);
-  constexpr int V4 = DK / 4;  // 144 float4 per row
+  constexpr int V4 = DK / 4;           // 144 float4 per row
+  constexpr int PT = 64 * V4 / 256;    // 36 float4 per thread
+  if (g.n_docs == 0) {
+    f32x4 v[PT];
+#pragma unroll
+    for (int n = 0; n < PT; ++n) v[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (64 * c < L) {
+      for (int cc = 0; cc < a.n_chunks; ++cc) {
+        const int f = (b * a.n_chunks + cc) * g.NB + c;
+        const int it1 = a.plan_pre[f + 1];
+        for (int it = a.plan_pre[f]; it < it1; ++it) {
+          const f32x4* src = (const f32x4*)(a.part + (size_t)it * BS * DK) + threadIdx.x;
+          // all of the item's loads in flight before the first add
+          f32x4 t[PT];
+#pragma unroll
+          for (int n = 0; n < PT; ++n) t[n] = __builtin_nontemporal_load(src + 256 * n);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int n = 0; n < PT; ++n) v[n] += t[n];
+        }
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < PT; ++n) {
+      const int e = threadIdx.x + 256 * n;
+      const int i = 64 * c + e / V4;
+      if (i < g.Skv)
+        *(f32x4*)(a.dkv + ((size_t)b * g.Skv + i) * DK + 4 * (e % V4)) =
+            i < L ? v[n] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    return;
+  }
   for (int e = threadIdx.x; e < 64 * V4; e += 256) {
     const int i = 64 * c + e / V4, c4 = e % V4;
     if (i >= g.Skv) break;
@@ -850,8 +948,8 @@ __global__ __launch_bounds__(256) void bwd_reduce_bf16_kernel(BwdArgs a) {
       const Doc d = doc_of_pos(g, b, i);
       const int j = block_of_pos(g, d, i);
       const int k = i - (d.start + (j - d.blk0) * g.BS);
-      for (int c = 0; c < a.n_chunks; ++c) {
-        const int f = (b * a.n_chunks + c) * g.NB + j;
+      for (int cc = 0; cc < a.n_chunks; ++cc) {
+        const int f = (b * a.n_chunks + cc) * g.NB + j;
         for (int it = a.plan_pre[f]; it < a.plan_pre[f + 1]; ++it)
           v += *(const f32x4*)(a.part + ((size_t)it * BS + k) * DK + 4 * c4);
       }
@@ -1101,14 +1199,13 @@ void launch_bf16(const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(bwd_plan_kernel, dim3(1), dim3(256), 0, s, a, OP);
   if (OP == kGather)
     hipLaunchKernelGGL(bwd_gfill_kernel, dim3(g.B * a.row_tiles), dim3(256), 0, s, a);
-  if (OP != kGather && a.ds_tiles != nullptr) {
+  if (a.ds_tiles != nullptr) {
     // stored score gradients: the key-block pass writes dS, dq reads it
     if (a.ds_stride == 0) hipLaunchKernelGGL(bwd_ds_entry_kernel, dim3(1), dim3(256), 0, s, a);
     if (a.items > 0)
-      hipLaunchKernelGGL((bwd_dkv_bf16_kernel<OP == kGather ? kScore : OP, true>), dim3(a.items),
-                         dim3(bw::NT), 0, s, a);
-    hipLaunchKernelGGL(bwd_dq_ds_bf16_kernel<OP == kGather ? kScore : OP>,
-                       dim3(g.B * ((g.Sq + 1) / 2)), dim3(2 * bw::NT), 0, s, a);
+      hipLaunchKernelGGL((bwd_dkv_bf16_kernel<OP, true>), dim3(a.items), dim3(bw::NT), 0, s, a);
+    hipLaunchKernelGGL(bwd_dq_ds_bf16_kernel<OP>, dim3(g.B * ((g.Sq + 1) / 2)), dim3(2 * bw::NT),
+                       0, s, a);
   } else {
     hipLaunchKernelGGL(bwd_dq_bf16_kernel<OP>, dim3(g.B * g.Sq), dim3(bw::NT), 0, s, a);
     if (a.items > 0)

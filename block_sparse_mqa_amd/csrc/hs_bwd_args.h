@@ -38,13 +38,16 @@ struct BwdArgs {
   int* g_total;              // gather: [B * NB] rows that selected each block
   int* g_off;                // gather: [B * NB] start of each block's row list
   int* g_rows;               // gather: row lists of all blocks, rows ascending
+  int* g_pos;                // gather with stored dS: each list entry's position in its
+                             // row's selection (the row's stored tile), or nullptr
   float* part;               // [items, 64, Dk] per-item key-block gradient partials
-  // Stored score gradients (causal and window, bf16; nullptr: dq recomputes
-  // them). Tile t of a row holds dS (scale included, bf16) of its 64 heads x
-  // the 64 keys of the row's t-th block, in the dq kernel's operand order
-  // [head block 4][k-step 2][lane 64][8]. Causal (ds_stride 0): row (b, r)
-  // owns tiles ds_entry[b] + tiles_before(b, r) .. + its block count; window:
-  // tiles (b Sq + r) ds_stride .. (ds_stride bounds a row's block count).
+  // Stored score gradients (bf16; nullptr: dq recomputes them). Tile t of a
+  // row holds dS (scale included, bf16) of its 64 heads x the 64 keys of the
+  // row's t-th block, in the dq kernel's operand order [head block 4][k-step
+  // 2][lane 64][8]. Causal (ds_stride 0): row (b, r) owns tiles ds_entry[b] +
+  // tiles_before(b, r) .. + its block count; window: tiles (b Sq + r)
+  // ds_stride .. (ds_stride bounds a row's block count); gather: ds_stride =
+  // top_k, tile t holding the block of selection entry t.
   __bf16* ds_tiles;
   int ds_stride;
   long long* ds_entry;       // causal: [B + 1] first tile of each entry; [B] = total
@@ -61,13 +64,13 @@ struct BwdArgs {
 // Workspace layout of one gradient call: byte offsets of each piece and the
 // total, plus the work split of the key-block gradient.
 struct BwdLayout {
-  size_t dsum, sink_part, first, nrows, pre, cnt, total_g, off_g, rows, part, ds_entry, ds_dummy,
-      ds_tiles, total;
+  size_t dsum, sink_part, first, nrows, pre, cnt, total_g, off_g, rows, pos, part, ds_entry,
+      ds_dummy, ds_tiles, total;
   int n_pre, rows_per_pre, chunk_rows, n_chunks, items, row_tiles, ds_stride, split_rows;
   bool store_ds;
 };
 
-// store_ds: also lay out the stored score gradients (causal and window).
+// store_ds: also lay out the stored score gradients.
 BwdLayout bwd_layout(const Geom& g, int op, int top_k, int window, bool store_ds);
 int bwd_launch(int op, const BwdArgs& a, bool bf16, hipStream_t stream);
 

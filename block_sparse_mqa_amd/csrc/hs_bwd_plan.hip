@@ -89,16 +89,24 @@ BwdLayout bwd_layout(const Geom& g, int op, int top_k, int window, bool store_ds
       off = align256(off + FB * sizeof(int));
       L.rows = off;
       off = align256(off + rows * std::max(top_k, 1) * sizeof(int));
+      if (store_ds) {
+        L.pos = off;
+        off = align256(off + rows * std::max(top_k, 1) * sizeof(int));
+      }
     }
     L.part = off;
     off = align256(off + (size_t)L.items * 64 * g.Dk * sizeof(float));
   }
-  if (store_ds && op != kGather) {
+  if (store_ds) {
     // 64 heads x 64 keys of bf16 per (row, block of its range); a window of
-    // W keys meets at most ceil((W - 1) / BS) + 1 blocks
+    // W keys meets at most ceil((W - 1) / BS) + 1 blocks; a gather row owns
+    // one tile per selection entry
     long long tiles = 0;
     if (op == kScore) {
       for (int b = 0; b < g.B; ++b) tiles += causal_tiles_before(g, b, g.Sq);
+    } else if (op == kGather) {
+      L.ds_stride = std::max(top_k, 1);
+      tiles = (long long)g.B * g.Sq * L.ds_stride;
     } else {
       const long long per = std::min<long long>((window - 1 + (long long)g.BS - 1) / g.BS + 1, g.NB);
       L.ds_stride = (int)per;

@@ -115,7 +115,8 @@ typedef enum {
   HS_OP_BLOCK_SCORE_BWD_STORE_DS = 6, /* larger workspace of hs_block_score_bwd
                                          that also holds the score gradients */
   HS_OP_SWA_BWD_STORE_DS = 7,   /* the same for hs_swa_bwd           */
-  HS_OP_SWA_SPARSE = 8          /* workspace of hs_swa_sparse_fwd    */
+  HS_OP_SWA_SPARSE = 8,         /* workspace of hs_swa_sparse_fwd    */
+  HS_OP_SPARSE_GATHER_BWD_STORE_DS = 9 /* the same for hs_sparse_gather_bwd */
 } hs_op;
 
 typedef struct {
@@ -307,7 +308,13 @@ hs_status hs_block_score_bwd(const hs_problem* p, const void* q, const void* kv,
 
 /* Gradients of hs_sparse_gather_fwd for the given selection (block_idx and
  * top_k as in the forward; the selection itself takes no gradient). At most
- * 4096 blocks. */
+ * 4096 blocks. Given at least the HS_OP_SPARSE_GATHER_BWD_STORE_DS workspace
+ * (bf16 only; 8 KB per row and per selection entry, 8.6 GB at one
+ * 32768-token sequence with top_k 32), the key-block pass stores the score
+ * gradients of every (row, selected block) pair and dq is computed from them,
+ * for two consecutive rows at a time over the union of their selections, as
+ * for hs_block_score_bwd; with the smaller HS_OP_SPARSE_GATHER_BWD workspace
+ * dq recomputes them. */
 hs_status hs_sparse_gather_bwd(const hs_problem* p, const void* q, const void* kv,
                                const float* sink, const int32_t* block_idx, int32_t top_k,
                                const void* out, const float* lse, const void* dout,

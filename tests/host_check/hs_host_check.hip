@@ -97,6 +97,12 @@ int bwd_launch(int op, const BwdArgs& a, bool, hipStream_t) {
     in_ws(a.g_total, (size_t)g.B * g.NB * sizeof(int), "gather totals");
     in_ws(a.g_off, (size_t)g.B * g.NB * sizeof(int), "gather offsets");
     in_ws(a.g_rows, rows * a.top_k * sizeof(int), "gather row lists");
+    if (a.ds_tiles != nullptr) {
+      in_ws(a.g_pos, rows * a.top_k * sizeof(int), "gather list positions");
+      CHECK(a.ds_stride == a.top_k, "gather dS stride %d, top_k %d", a.ds_stride, a.top_k);
+    } else {
+      CHECK(a.g_pos == nullptr, "gather list positions without stored dS");
+    }
   }
   in_ws(a.part, (size_t)a.items * 64 * g.Dk * sizeof(float), "dkv partials");
   if (a.ds_tiles != nullptr) {
@@ -352,7 +358,9 @@ void check_problem(const Spec& s, std::mt19937& rng) {
       {HS_OP_BLOCK_SCORE, HS_OP_BLOCK_SCORE_BWD_STORE_DS, s.f32 ? -1 : causal_tiles},
       {HS_OP_SWA, HS_OP_SWA_BWD, -1},
       {HS_OP_SWA, HS_OP_SWA_BWD_STORE_DS, s.f32 ? -1 : (long long)s.B * s.Sq * per},
-      {HS_OP_SPARSE_GATHER, HS_OP_SPARSE_GATHER_BWD, -1}};
+      {HS_OP_SPARSE_GATHER, HS_OP_SPARSE_GATHER_BWD, -1},
+      {HS_OP_SPARSE_GATHER, HS_OP_SPARSE_GATHER_BWD_STORE_DS,
+       s.f32 ? -1 : (long long)s.B * s.Sq * top_k}};
   for (const BwdCase& c : cases) {
     g_ds_tiles_expect = c.tiles;
     with_ws(c.ws_op, top_k, window, [&](void* ws, size_t n) {

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(hs.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.hs_version() == 201
+    assert lib.hs_version() == 202
 
 
 def _mla(**kw):
@@ -360,6 +360,8 @@ def test_stored_score_gradient_workspace_f32_unchanged():
     p = hs.Problem(1, 100, 100, 8, 96, 64, dtype="f32")
     assert hs.hs_workspace_size(p, hs.HS_OP_BLOCK_SCORE_BWD_STORE_DS) == \
         hs.hs_workspace_size(p, hs.HS_OP_BLOCK_SCORE_BWD)
+    assert hs.hs_workspace_size(p, hs.HS_OP_SPARSE_GATHER_BWD_STORE_DS, top_k=3) == \
+        hs.hs_workspace_size(p, hs.HS_OP_SPARSE_GATHER_BWD, top_k=3)
     assert hs.hs_workspace_size(p, hs.HS_OP_SWA_BWD_STORE_DS, window=30) == \
         hs.hs_workspace_size(p, hs.HS_OP_SWA_BWD, window=30)
 
@@ -369,9 +371,25 @@ def test_workspace_query_rejects_unknown_ops():
     gradient's larger workspace are errors."""
     p = _mla()
     with pytest.raises(ValueError):
-        hs.hs_workspace_size(p, hs.HS_OP_SWA_BWD_STORE_DS + 1)
+        hs.hs_workspace_size(p, hs.HS_OP_SPARSE_GATHER_BWD_STORE_DS + 1)
+    with pytest.raises(ValueError):
+        hs.hs_workspace_size(p, hs.HS_OP_SPARSE_GATHER_BWD_STORE_DS, top_k=0)
     with pytest.raises(ValueError):
         hs.hs_workspace_size(p, hs.HS_OP_SWA_BWD_STORE_DS, window=0)
+
+
+@pytest.mark.parametrize("B,Sq,Skv,top_k", [(1, 130, 130, 2), (1, 32768, 32768, 32),
+                                             (2, 70, 200, 64)])
+def test_stored_gather_gradient_workspace(B, Sq, Skv, top_k):
+    """The larger gather-gradient workspace adds 8 KB per row and per
+    selection entry, the list position of each row-list entry (4 B per row and
+    entry) and the same small pieces as the causal one."""
+    p = hs.Problem(B, Sq, Skv, 64, 576, 512)
+    n4 = hs.hs_workspace_size(p, hs.HS_OP_SPARSE_GATHER_BWD, top_k=top_k)
+    n9 = hs.hs_workspace_size(p, hs.HS_OP_SPARSE_GATHER_BWD_STORE_DS, top_k=top_k)
+    a256 = lambda x: (x + 255) // 256 * 256
+    assert n9 - n4 == (a256(B * Sq * top_k * 4) + a256((B + 1) * 8) + a256(4096) +
+                       a256(B * Sq * top_k * 8192)), (n4, n9)
 
 
 @pytest.mark.parametrize("B,Sq,Skv,window,kv_lens,per_row", [

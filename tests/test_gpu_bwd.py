@@ -54,8 +54,11 @@ def _gpu_grads(d, op, dout, idx=None, K=None):
         out, lse = hs.swa(d.prob, d.q, d.kv, d.sink, p.window)
         return hs.swa_bwd(d.prob, d.q, d.kv, d.sink, p.window, out, lse, dout,
                           store_ds=op == "swa")
+    # "gather": the smaller workspace (dq recomputes); "gather_ds": the larger
+    # one (bf16: the key-block pass stores dS, dq on row pairs reads it)
     out, lse = hs.sparse_gather(d.prob, d.q, d.kv, d.sink, idx, K)
-    return hs.sparse_gather_bwd(d.prob, d.q, d.kv, d.sink, idx, K, out, lse, dout)
+    return hs.sparse_gather_bwd(d.prob, d.q, d.kv, d.sink, idx, K, out, lse, dout,
+                                store_ds=op == "gather_ds")
 
 
 def _oracle_grads(d, op, dout_cpu, idx=None, rows=None):
@@ -104,7 +107,7 @@ def test_gradients_match_oracle(name):
     torch.cuda.synchronize()
     idx_cpu = idx.cpu().numpy()
     res = {}
-    for op in ("score", "score_recompute", "swa", "swa_recompute", "gather"):
+    for op in ("score", "score_recompute", "swa", "swa_recompute", "gather", "gather_ds"):
         g = _gpu_grads(d, op, dout, idx, p.top_k)
         torch.cuda.synchronize()
         w = _oracle_grads(d, op, dout_cpu, idx_cpu)
@@ -132,12 +135,13 @@ def test_gather_list_with_skipped_entries():
     idx[0, 5] = [-1, -1, -1, NB + 1]                     # nothing usable
     idx_dev = torch.from_numpy(idx).cuda()
     dout_cpu = inputs.make_dout(p, seed=40)
-    g = _gpu_grads(d, "gather", dout_cpu.cuda(), idx_dev, 4)
-    torch.cuda.synchronize()
     w = _oracle_grads(d, "gather", dout_cpu, idx)
-    for k, name in enumerate(("dq", "dkv", "dsink")):
-        _grad_close(np64(g[k]), w[k], "bf16", f"gather {name}")
-    assert not torch.any(g[0][0, 5]).item()
+    for v in ("gather", "gather_ds"):
+        g = _gpu_grads(d, v, dout_cpu.cuda(), idx_dev, 4)
+        torch.cuda.synchronize()
+        for k, name in enumerate(("dq", "dkv", "dsink")):
+            _grad_close(np64(g[k]), w[k], "bf16", f"{v} {name}")
+        assert not torch.any(g[0][0, 5]).item()
     say("[gpu] gather with skipped entries: ok")
 
 
@@ -149,7 +153,7 @@ def test_gradients_are_deterministic():
     dout = inputs.make_dout(p, seed=42).cuda()
     _, _, bl = hs.block_score(d.prob, d.q, d.kv, d.sink)
     idx = hs.topk_blocks(d.prob, bl, p.top_k)
-    for op in ("score", "score_recompute", "swa", "swa_recompute", "gather"):
+    for op in ("score", "score_recompute", "swa", "swa_recompute", "gather", "gather_ds"):
         a = _gpu_grads(d, op, dout, idx, p.top_k)
         b = _gpu_grads(d, op, dout, idx, p.top_k)
         torch.cuda.synchronize()
@@ -179,7 +183,7 @@ def test_long_context_sampled():
     # the causal and window calls through both workspaces (stored and
     # recomputed score gradients), against one oracle evaluation each
     for op, variants in (("score", ("score", "score_recompute")), ("swa", ("swa", "swa_recompute")),
-                         ("gather", ("gather",))):
+                         ("gather", ("gather", "gather_ds"))):
         got = []
         for v in variants:
             g = _gpu_grads(d, v, dout, idx, p.top_k)
@@ -217,16 +221,19 @@ def test_split_work_items_against_oracle():
     sel[sel < 0] = -1
     idx_cpu = np.broadcast_to(sel, (p.B, S, 2)).astype(np.int32).copy()
     idx = torch.from_numpy(idx_cpu).cuda()
-    g = _gpu_grads(d, "gather", dout, idx, 2)
-    torch.cuda.synchronize()
     rows = np.arange(512)
-    got_dq = np64(g[0][:, :512])
-    got_dkv = np64(g[1][:, :64])
-    del g
-    say("[gpu] split items: gather on the GPU done, oracle on rows 0 .. 511")
-    w = _oracle_grads(d, "gather", dout_cpu[:, rows], idx_cpu, rows=rows)
-    e = [_grad_close(got_dq, w[0], "bf16", "gather dq"),
-         _grad_close(got_dkv, w[1][:, :64], "bf16", "gather dkv block 0")]
+    e = []
+    for v in ("gather", "gather_ds"):
+        g = _gpu_grads(d, v, dout, idx, 2)
+        torch.cuda.synchronize()
+        got_dq = np64(g[0][:, :512])
+        got_dkv = np64(g[1][:, :64])
+        del g
+        if v == "gather":
+            say("[gpu] split items: gather on the GPU done, oracle on rows 0 .. 511")
+            w = _oracle_grads(d, "gather", dout_cpu[:, rows], idx_cpu, rows=rows)
+        e += [_grad_close(got_dq, w[0], "bf16", f"{v} dq"),
+              _grad_close(got_dkv, w[1][:, :64], "bf16", f"{v} dkv block 0")]
     rows = np.arange(1280, 1280 + 64 + p.window - 1)
     for v in ("swa", "swa_recompute"):
         gw = _gpu_grads(d, v, dout)
@@ -245,23 +252,23 @@ def test_split_work_items_against_oracle():
 def test_gradients_in_captured_graph():
     """The gradient calls allocate nothing and write every workspace word before
     reading it, so one captured graph replays correctly with new upstream
-    gradients. Each replay must equal an eager call bit for bit."""
+    gradients. Each replay must equal an eager call bit for bit (the gather
+    and the causal call, both with stored score gradients)."""
     p = _mla("graph", 333, 44, 3, 90)
     d = Dev(p)
     out, lse, bl = hs.block_score(d.prob, d.q, d.kv, d.sink)
     idx = hs.topk_blocks(d.prob, bl, p.top_k)
     og, lg = hs.sparse_gather(d.prob, d.q, d.kv, d.sink, idx, p.top_k)
     dout = inputs.make_dout(p, seed=45).cuda()
-    dq = torch.empty((1, p.Sq, p.H, p.Dk), dtype=torch.float32, device="cuda")
-    dkv = torch.empty((1, p.Skv, p.Dk), dtype=torch.float32, device="cuda")
-    dsink = torch.empty((p.H,), dtype=torch.float32, device="cuda")
-    ws = hs._workspace(d.prob, hs.HS_OP_SPARSE_GATHER_BWD, top_k=p.top_k)
+    bufs = [(torch.empty((1, p.Sq, p.H, p.Dk), dtype=torch.float32, device="cuda"),
+             torch.empty((1, p.Skv, p.Dk), dtype=torch.float32, device="cuda"),
+             torch.empty((p.H,), dtype=torch.float32, device="cuda")) for _ in range(2)]
+    ws = hs.sparse_gather_bwd_workspace(d.prob, p.top_k, store_ds=True)
     ws2 = hs.score_bwd_workspace(d.prob, store_ds=True)
 
     def calls():
-        hs.hs_sparse_gather_bwd(d.prob, d.q, d.kv, d.sink, idx, p.top_k, og, lg, dout, dq, dkv,
-                                dsink, ws)
-        hs.hs_block_score_bwd(d.prob, d.q, d.kv, d.sink, out, lse, dout, dq, dkv, dsink, ws2)
+        hs.hs_sparse_gather_bwd(d.prob, d.q, d.kv, d.sink, idx, p.top_k, og, lg, dout, *bufs[0], ws)
+        hs.hs_block_score_bwd(d.prob, d.q, d.kv, d.sink, out, lse, dout, *bufs[1], ws2)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -280,11 +287,14 @@ def test_gradients_in_captured_graph():
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        got = (dq.clone(), dkv.clone(), dsink.clone())
-        want = hs.block_score_bwd(d.prob, d.q, d.kv, d.sink, out, lse, dout, store_ds=True)
+        got = [tuple(x.clone() for x in b_) for b_ in bufs]
+        want = [hs.sparse_gather_bwd(d.prob, d.q, d.kv, d.sink, idx, p.top_k, og, lg, dout,
+                                     store_ds=True),
+                hs.block_score_bwd(d.prob, d.q, d.kv, d.sink, out, lse, dout, store_ds=True)]
         torch.cuda.synchronize()
-        for g_, w_, n in zip(got, want, ("dq", "dkv", "dsink")):
-            assert torch.equal(g_, w_), f"replay {rep}: {n} differs from the eager call"
+        for call, gg, ww in zip(("gather", "causal"), got, want):
+            for g_, w_, n in zip(gg, ww, ("dq", "dkv", "dsink")):
+                assert torch.equal(g_, w_), f"replay {rep}: {call} {n} differs from the eager call"
     say("[gpu] gradient graph replays: identical")
 
 
@@ -308,21 +318,25 @@ def test_sink_without_its_gradient():
 
 
 def test_stored_and_recomputed_score_gradients_agree():
-    """The two workspaces of the causal and window gradients: the key-block
-    pass is the same arithmetic in both (dkv and dsink bit-identical); dq from
-    the stored bf16 score gradients matches dq that recomputes them up to dS
-    rounding."""
+    """The two workspaces of the causal, window and gather gradients: the
+    key-block pass is the same arithmetic in both (dkv and dsink
+    bit-identical); dq from the stored bf16 score gradients matches dq that
+    recomputes them up to dS rounding."""
     p = _mla("paths_S700", 700, 44, 2, 64)
     say(f"[gpu] stored vs recomputed score gradients, S={p.Sq}")
     d = Dev(p)
     dout = inputs.make_dout(p, seed=45).cuda()
-    out, lse, _ = hs.block_score(d.prob, d.q, d.kv, d.sink)
+    out, lse, bl = hs.block_score(d.prob, d.q, d.kv, d.sink)
     ow, lw = hs.swa(d.prob, d.q, d.kv, d.sink, p.window)
+    idx = hs.topk_blocks(d.prob, bl, p.top_k)
+    og, lg = hs.sparse_gather(d.prob, d.q, d.kv, d.sink, idx, p.top_k)
     for name, call in (
             ("causal", lambda st: hs.block_score_bwd(d.prob, d.q, d.kv, d.sink, out, lse, dout,
                                                      store_ds=st)),
             ("window", lambda st: hs.swa_bwd(d.prob, d.q, d.kv, d.sink, p.window, ow, lw, dout,
-                                             store_ds=st))):
+                                             store_ds=st)),
+            ("gather", lambda st: hs.sparse_gather_bwd(d.prob, d.q, d.kv, d.sink, idx, p.top_k, og,
+                                                       lg, dout, store_ds=st))):
         a = call(True)
         b = call(False)
         torch.cuda.synchronize()
