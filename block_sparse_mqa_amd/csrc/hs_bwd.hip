@@ -900,8 +900,8 @@ void bwd_dkv_bf16_kernel(BwdArgs a) {
 // the 64 rows are exactly one block (key k of block c is row 64 c + k), so a
 // thread keeps its 36 elements in registers and walks the block's items once:
 // per item 36 independent loads, and the workgroup reads each item's partial
-// as one contiguous 147 KB run. With documents a row's block is looked up per
-// element. Both add the partials in the same order.
+// as one contiguous 147 KB run. With documents each row looks up its own
+// block, four threads per row. Both add the partials in the same order.
 __global__ __launch_bounds__(256) void bwd_reduce_bf16_kernel(BwdArgs a) {
   using namespace bw;
   const Geom& g = a.g;
@@ -940,22 +940,34 @@ __global__ __launch_bounds__(256) void bwd_reduce_bf16_kernel(BwdArgs a) {
     }
     return;
   }
-  for (int e = threadIdx.x; e < 64 * V4; e += 256) {
-    const int i = 64 * c + e / V4, c4 = e % V4;
-    if (i >= g.Skv) break;
-    f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (i < L) {
-      const Doc d = doc_of_pos(g, b, i);
-      const int j = block_of_pos(g, d, i);
-      const int k = i - (d.start + (j - d.blk0) * g.BS);
-      for (int cc = 0; cc < a.n_chunks; ++cc) {
-        const int f = (b * a.n_chunks + cc) * g.NB + j;
-        for (int it = a.plan_pre[f]; it < a.plan_pre[f + 1]; ++it)
-          v += *(const f32x4*)(a.part + ((size_t)it * BS + k) * DK + 4 * c4);
+  // With documents: four threads per row (row 64 c + t / 4), thread q of a
+  // row taking float4 columns q, q + 4, ..; each row finds its own block.
+  const int i = 64 * c + (threadIdx.x >> 2), q = threadIdx.x & 3;
+  if (i >= g.Skv) return;
+  f32x4 v[PT];
+#pragma unroll
+  for (int n = 0; n < PT; ++n) v[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (i < L) {
+    const Doc d = doc_of_pos(g, b, i);
+    const int j = block_of_pos(g, d, i);
+    const int k = i - (d.start + (j - d.blk0) * g.BS);
+    for (int cc = 0; cc < a.n_chunks; ++cc) {
+      const int f = (b * a.n_chunks + cc) * g.NB + j;
+      const int it1 = a.plan_pre[f + 1];
+      for (int it = a.plan_pre[f]; it < it1; ++it) {
+        const f32x4* src = (const f32x4*)(a.part + ((size_t)it * BS + k) * DK) + q;
+        f32x4 t[PT];
+#pragma unroll
+        for (int n = 0; n < PT; ++n) t[n] = __builtin_nontemporal_load(src + 4 * n);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int n = 0; n < PT; ++n) v[n] += t[n];
       }
     }
-    *(f32x4*)(a.dkv + ((size_t)b * g.Skv + i) * DK + 4 * c4) = v;
   }
+  f32x4* dst = (f32x4*)(a.dkv + ((size_t)b * g.Skv + i) * DK) + q;
+#pragma unroll
+  for (int n = 0; n < PT; ++n) dst[4 * n] = v[n];
 }
 
 // ---------------------------------------------------------------------------
