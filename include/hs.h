@@ -153,10 +153,11 @@ int32_t hs_num_blocks(const hs_problem* p);
 /* Workspace bytes the given operation needs for this problem (0 when it
  * needs none; single-token decode splits the key range across workgroups and
  * merges partial results through the workspace; the gradient operations
- * always need one; HS_OP_BLOCK_SCORE_BWD_STORE_DS and HS_OP_SWA_BWD_STORE_DS
- * give the larger causal and window gradient workspaces that also hold the
- * score gradients). top_k and window are the values the operation will be
- * called with (ignored where irrelevant). */
+ * always need one; HS_OP_BLOCK_SCORE_BWD_STORE_DS, HS_OP_SWA_BWD_STORE_DS and
+ * HS_OP_SPARSE_GATHER_BWD_STORE_DS give the larger causal, window and gather
+ * gradient workspaces that also hold the score gradients). top_k and window
+ * are the values the operation will be called with (ignored where
+ * irrelevant). */
 hs_status hs_workspace_size(const hs_problem* p, int32_t op, int32_t top_k, int32_t window,
                             size_t* bytes);
 
