@@ -15,6 +15,11 @@ gradient to the kernels, which add it exactly (dlse in include/hs.h).
 The library computes gradients in fp32. Autograd needs each gradient in its
 input's dtype, so bf16 inputs receive the fp32 gradients rounded to bf16.
 Nothing else runs outside the kernels.
+
+store_ds (default False) picks the larger gradient workspaces, in which the
+key-block pass stores the bf16 score gradients and dq reads them instead of
+recomputing the scores (faster, 8 KB per (row, key block) pair; the same
+gradients up to the rounding of dS).
 """
 from __future__ import annotations
 
@@ -22,9 +27,9 @@ from typing import Optional
 
 import torch
 
-from . import (HS_OP_SPARSE_GATHER_BWD, Problem, _workspace, block_score_topk,
-               hs_block_score_bwd, hs_sparse_gather_bwd, hs_swa_bwd, score_bwd_workspace,
-               sparse_gather, swa, swa_bwd_workspace, swa_sparse)
+from . import (Problem, block_score_topk, hs_block_score_bwd, hs_sparse_gather_bwd, hs_swa_bwd,
+               score_bwd_workspace, sparse_gather, sparse_gather_bwd_workspace, swa,
+               swa_bwd_workspace, swa_sparse)
 
 
 def _grads(prob, q, sink, need_sink):
@@ -47,10 +52,10 @@ class BlockScoreTopk(torch.autograd.Function):
     scores and the per-token top-k; gradients reach q, kv and the sink."""
 
     @staticmethod
-    def forward(ctx, q, kv, sink, prob: Problem, top_k: int):
+    def forward(ctx, q, kv, sink, prob: Problem, top_k: int, store_ds: bool = False):
         out, lse, bl, idx = block_score_topk(prob, q, kv, sink, top_k)
         ctx.save_for_backward(q, kv, sink, out, lse)
-        ctx.prob = prob
+        ctx.prob, ctx.store_ds = prob, store_ds
         ctx.mark_non_differentiable(bl, idx)
         return out, lse, bl, idx
 
@@ -60,8 +65,8 @@ class BlockScoreTopk(torch.autograd.Function):
         prob = ctx.prob
         dq, dkv, dsink = _grads(prob, q, sink, ctx.needs_input_grad[2])
         hs_block_score_bwd(prob, q, kv, sink, out, lse, dout.contiguous(), dq, dkv, dsink,
-                           score_bwd_workspace(prob), dlse=dlse.contiguous())
-        return (*_finish(ctx, q, kv, sink, dq, dkv, dsink), None, None)
+                           score_bwd_workspace(prob, ctx.store_ds), dlse=dlse.contiguous())
+        return (*_finish(ctx, q, kv, sink, dq, dkv, dsink), None, None, None)
 
 
 class SparseGather(torch.autograd.Function):
@@ -69,10 +74,10 @@ class SparseGather(torch.autograd.Function):
     selection itself takes no gradient."""
 
     @staticmethod
-    def forward(ctx, q, kv, sink, block_idx, prob: Problem, top_k: int):
+    def forward(ctx, q, kv, sink, block_idx, prob: Problem, top_k: int, store_ds: bool = False):
         out, lse = sparse_gather(prob, q, kv, sink, block_idx, top_k)
         ctx.save_for_backward(q, kv, sink, block_idx, out, lse)
-        ctx.prob, ctx.top_k = prob, top_k
+        ctx.prob, ctx.top_k, ctx.store_ds = prob, top_k, store_ds
         return out, lse
 
     @staticmethod
@@ -82,19 +87,19 @@ class SparseGather(torch.autograd.Function):
         dq, dkv, dsink = _grads(prob, q, sink, ctx.needs_input_grad[2])
         hs_sparse_gather_bwd(prob, q, kv, sink, block_idx, ctx.top_k, out, lse,
                              dout.contiguous(), dq, dkv, dsink,
-                             _workspace(prob, HS_OP_SPARSE_GATHER_BWD, top_k=ctx.top_k),
+                             sparse_gather_bwd_workspace(prob, ctx.top_k, ctx.store_ds),
                              dlse=dlse.contiguous())
-        return (*_finish(ctx, q, kv, sink, dq, dkv, dsink), None, None, None)
+        return (*_finish(ctx, q, kv, sink, dq, dkv, dsink), None, None, None, None)
 
 
 class SlidingWindow(torch.autograd.Function):
     """(out, lse) of sliding-window MQA attention."""
 
     @staticmethod
-    def forward(ctx, q, kv, sink, prob: Problem, window: int):
+    def forward(ctx, q, kv, sink, prob: Problem, window: int, store_ds: bool = False):
         out, lse = swa(prob, q, kv, sink, window)
         ctx.save_for_backward(q, kv, sink, out, lse)
-        ctx.prob, ctx.window = prob, window
+        ctx.prob, ctx.window, ctx.store_ds = prob, window, store_ds
         return out, lse
 
     @staticmethod
@@ -103,8 +108,8 @@ class SlidingWindow(torch.autograd.Function):
         prob = ctx.prob
         dq, dkv, dsink = _grads(prob, q, sink, ctx.needs_input_grad[2])
         hs_swa_bwd(prob, q, kv, sink, ctx.window, out, lse, dout.contiguous(), dq, dkv, dsink,
-                   swa_bwd_workspace(prob, ctx.window), dlse=dlse.contiguous())
-        return (*_finish(ctx, q, kv, sink, dq, dkv, dsink), None, None)
+                   swa_bwd_workspace(prob, ctx.window, ctx.store_ds), dlse=dlse.contiguous())
+        return (*_finish(ctx, q, kv, sink, dq, dkv, dsink), None, None, None)
 
 
 class SlidingWindowLayer(torch.autograd.Function):
@@ -115,10 +120,11 @@ class SlidingWindowLayer(torch.autograd.Function):
     lse receive; a branch whose outputs receive none is skipped."""
 
     @staticmethod
-    def forward(ctx, q, kv, sink, block_idx, prob: Problem, window: int, top_k: int):
+    def forward(ctx, q, kv, sink, block_idx, prob: Problem, window: int, top_k: int,
+                store_ds: bool = False):
         ow, lw, og, lg = swa_sparse(prob, q, kv, sink, window, block_idx, top_k)
         ctx.save_for_backward(q, kv, sink, block_idx, ow, lw, og, lg)
-        ctx.prob, ctx.window, ctx.top_k = prob, window, top_k
+        ctx.prob, ctx.window, ctx.top_k, ctx.store_ds = prob, window, top_k, store_ds
         ctx.set_materialize_grads(False)
         return ow, lw, og, lg
 
@@ -130,10 +136,10 @@ class SlidingWindowLayer(torch.autograd.Function):
         for dout, dl, run in (
                 (dout_swa, dlw, lambda g, d, l_: hs_swa_bwd(
                     prob, q, kv, sink, ctx.window, ow, lw, d, *g,
-                    swa_bwd_workspace(prob, ctx.window), dlse=l_)),
+                    swa_bwd_workspace(prob, ctx.window, ctx.store_ds), dlse=l_)),
                 (dout_sparse, dlg, lambda g, d, l_: hs_sparse_gather_bwd(
                     prob, q, kv, sink, block_idx, ctx.top_k, og, lg, d, *g,
-                    _workspace(prob, HS_OP_SPARSE_GATHER_BWD, top_k=ctx.top_k), dlse=l_))):
+                    sparse_gather_bwd_workspace(prob, ctx.top_k, ctx.store_ds), dlse=l_))):
             if dout is None and dl is None:
                 continue
             g = _grads(prob, q, sink, ctx.needs_input_grad[2])
@@ -142,29 +148,31 @@ class SlidingWindowLayer(torch.autograd.Function):
             total = g if total is None else tuple(
                 None if a is None else a + b for a, b in zip(total, g))
         if total is None:
-            return None, None, None, None, None, None, None
-        return (*_finish(ctx, q, kv, sink, *total), None, None, None, None)
+            return None, None, None, None, None, None, None, None
+        return (*_finish(ctx, q, kv, sink, *total), None, None, None, None, None)
 
 
 def sliding_window_layer(q, kv, sink: Optional[torch.Tensor], block_idx, prob: Problem,
-                         window: int, top_k: int):
+                         window: int, top_k: int, store_ds: bool = False):
     """Both branches of a sliding-window layer: returns (out_swa, lse_swa,
     out_sparse, lse_sparse); differentiable in q, kv and sink."""
-    return SlidingWindowLayer.apply(q, kv, sink, block_idx, prob, window, top_k)
+    return SlidingWindowLayer.apply(q, kv, sink, block_idx, prob, window, top_k, store_ds)
 
 
-def block_score_attention(q, kv, sink: Optional[torch.Tensor], prob: Problem, top_k: int):
+def block_score_attention(q, kv, sink: Optional[torch.Tensor], prob: Problem, top_k: int,
+                          store_ds: bool = False):
     """Causal attention with sink, its block scores and the top-k selection:
     returns (out, lse, block_logit, block_idx); differentiable in q, kv, sink."""
-    return BlockScoreTopk.apply(q, kv, sink, prob, top_k)
+    return BlockScoreTopk.apply(q, kv, sink, prob, top_k, store_ds)
 
 
 def sparse_gather_attention(q, kv, sink: Optional[torch.Tensor], block_idx, prob: Problem,
-                            top_k: int):
+                            top_k: int, store_ds: bool = False):
     """Block-sparse gather attention: returns (out, lse)."""
-    return SparseGather.apply(q, kv, sink, block_idx, prob, top_k)
+    return SparseGather.apply(q, kv, sink, block_idx, prob, top_k, store_ds)
 
 
-def sliding_window_attention(q, kv, sink: Optional[torch.Tensor], prob: Problem, window: int):
+def sliding_window_attention(q, kv, sink: Optional[torch.Tensor], prob: Problem, window: int,
+                             store_ds: bool = False):
     """Sliding-window MQA attention: returns (out, lse)."""
-    return SlidingWindow.apply(q, kv, sink, prob, window)
+    return SlidingWindow.apply(q, kv, sink, prob, window, store_ds)

@@ -154,3 +154,46 @@ def test_loss_using_lse_gets_its_gradient():
         errs[name] = [_grad_close(np64(a), b, "bf16", f"{name} {n}")
                       for a, b, n in zip(lib, want, ("dq", "dkv", "dsink"))]
     say(f"[gpu] gradients with dlse vs oracle: {errs}")
+
+
+def test_stored_score_gradients_through_autograd():
+    """store_ds=True routes each function's backward through the stored
+    score-gradient workspace: the gradients equal the library's stored-form
+    calls exactly, and dkv and dsink equal the recomputing form's bit for
+    bit while dq stays within the rounding of the stored bf16 dS."""
+    p = inputs.make(1, 260, 260, MLA["H"], MLA["Dk"], MLA["Dv"], seed=88, top_k=3, window=90,
+                    name="autograd_store")
+    prob = hs.Problem(1, 260, 260, p.H, p.Dk, p.Dv, scale=p.scale)
+    dout = inputs.make_dout(p, seed=89).cuda()
+    q, kv, sink = _leaves(p)
+    with torch.no_grad():
+        _, _, _, idx = hsa.block_score_attention(q, kv, sink, prob, p.top_k)
+
+    def run(store):
+        out, lse, _, _ = hsa.block_score_attention(q, kv, sink, prob, p.top_k, store_ds=store)
+        og, lg = hsa.sparse_gather_attention(q, kv, sink, idx, prob, p.top_k, store_ds=store)
+        ow, lw = hsa.sliding_window_attention(q, kv, sink, prob, p.window, store_ds=store)
+        lo_w, _, lo_g, _ = hsa.sliding_window_layer(q, kv, sink, idx, prob, p.window, p.top_k,
+                                                    store_ds=store)
+        res = [torch.autograd.grad(o, (q, kv, sink), dout) for o in (out, og, ow)]
+        res.append(torch.autograd.grad((lo_w, lo_g), (q, kv, sink), (dout, dout)))
+        lib = (lambda: hs.block_score_bwd(prob, q, kv, sink, out, lse, dout, store_ds=store),
+               lambda: hs.sparse_gather_bwd(prob, q, kv, sink, idx, p.top_k, og, lg, dout,
+                                            store_ds=store),
+               lambda: hs.swa_bwd(prob, q, kv, sink, p.window, ow, lw, dout, store_ds=store))
+        with torch.no_grad():
+            want = [f() for f in lib]
+        torch.cuda.synchronize()
+        for (gq, gkv, gs), (dq, dkv, dsink) in zip(res, want):
+            assert torch.equal(gq, dq.to(q.dtype)) and torch.equal(gkv, dkv.to(kv.dtype))
+            assert torch.equal(gs, dsink)
+        return res
+
+    stored, recomputed = run(True), run(False)
+    rel = []
+    for (aq, akv, asink), (bq, bkv, bsink) in zip(stored, recomputed):
+        assert torch.equal(akv, bkv) and torch.equal(asink, bsink)
+        r = float((aq.float() - bq.float()).abs().max() / bq.float().abs().max())
+        assert r < 1e-2, r
+        rel.append(r)
+    say(f"[gpu] stored dS through autograd: dq max rel diff {[f'{r:.1e}' for r in rel]}")
