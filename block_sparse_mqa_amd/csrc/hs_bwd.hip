@@ -470,8 +470,9 @@ void bwd_dq_ds_bf16_kernel(BwdArgs a) {
   const long long base = has_row ? ds_row_base(a, b, r) : 0;
   const bf16* dsp = a.ds_tiles + (base * 4 + hw) * 2 * 512 + lane * 8;  // row tile t: + 4096 t
   const bf16x8 zero8 = {};
-  // dS of tile t of the walk for this wave's row
-  auto ds_load = [&](int t, bf16x8* d) __attribute__((always_inline)) {
+  // dS of tile t of the walk for this wave's row; false: the row has no
+  // entry for the tile (its dS is zero)
+  auto ds_load = [&](int t, bf16x8* d) __attribute__((always_inline)) -> bool {
     int e = -1;
     if (OP == kGather) {
       e = has_row ? upos[wave][rsel][t] : -1;
@@ -487,9 +488,10 @@ void bwd_dq_ds_bf16_kernel(BwdArgs a) {
       d[0] = zero8;
       d[1] = zero8;
     }
+    return e >= 0;
   };
   bf16x8 dnext[2], dcur[2];
-  if (ntiles > 0) ds_load(0, dnext);
+  bool mine_next = ntiles > 0 && ds_load(0, dnext);
 
   f32x4 acc[DBK];
 #pragma unroll
@@ -502,7 +504,8 @@ void bwd_dq_ds_bf16_kernel(BwdArgs a) {
     __syncthreads();  // tile t and its dS resident; tile t-1 consumed by every wave
     dcur[0] = dnext[0];
     dcur[1] = dnext[1];
-    ds_load(tn, dnext);
+    const bool mine = mine_next;
+    mine_next = ds_load(tn, dnext);
     // The copy of the next tile (on the last tile the current one again, into
     // the idle buffer) is spread over the stream.
     const Blk nbk = block_rows(g, b, tile_block(tn));
@@ -527,6 +530,15 @@ void bwd_dq_ds_bf16_kernel(BwdArgs a) {
         dma16(cp_src + 128 * G, cp_dst + G * GR);
       }
     };
+    // A wave whose row has no entry for this tile (a block that only the
+    // other row of the pair selected or reaches, or a pair without a second
+    // row) has dS = 0 here: it skips the MFMAs and issues only its share of
+    // the copy, which leaves its SIMD to the other row's wave.
+    if (!__builtin_amdgcn_readfirstlane((int)mine)) {
+#pragma unroll
+      for (int G = 0; G < 9; ++G) dma16(cp_src + 128 * G, cp_dst + G * GR);
+      continue;
+    }
     operand_stream<NF, 8>(load, use, pre);
   }
   __builtin_amdgcn_s_waitcnt(0);
